@@ -1,0 +1,80 @@
+"""Planted mistakes in the oracle must be caught by the pins.
+
+Each mutant is a copy of oracle/kda_oracle.c with one plausible mistake (a
+dropped term, a wrong sign, a wrong index, a transposed operand, the read-out
+taken before the update).  It is compiled with gcc into a temporary
+directory and the pin suite runs against it in a child process, so a mutant
+that crashes counts as caught.  CPU only; the real oracle is not modified.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+_ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+_SRC = os.path.join(_ROOT, "oracle", "kda_oracle.c")
+
+# (name, exact text in the source, replacement)
+MUTANTS = [
+    ("decay_dropped", "S[(size_t)i * dv + j] *= a;", "S[(size_t)i * dv + j] *= 1.0;"),
+    ("decay_sign", "exp((double)lat[i])", "exp(-(double)lat[i])"),
+    ("decay_on_value_columns", "const double a = exp((double)lat[i]);\n"
+     "            for (int32_t j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a;",
+     "for (int32_t j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= "
+     "exp((double)lat[j < dk ? j : 0]);"),
+    ("error_sign", "u[j] = bt * ((double)vt[j] - u[j]);", "u[j] = bt * ((double)vt[j] + u[j]);"),
+    ("beta_dropped", "u[j] = bt * ((double)vt[j] - u[j]);", "u[j] = ((double)vt[j] - u[j]);"),
+    ("beta_wrong_head", "(double)J->beta[(size_t)t * H + h]", "(double)J->beta[(size_t)t * H]"),
+    ("prediction_uses_query", "u[j] += ki * S[(size_t)i * dv + j];",
+     "u[j] += (double)qt[i] * S[(size_t)i * dv + j];"),
+    ("readout_uses_key", "const double qi = (double)qt[i];", "const double qi = (double)kt[i];"),
+    ("state_transposed_in_prediction", "u[j] += ki * S[(size_t)i * dv + j];",
+     "u[j] += ki * S[((size_t)j * dk + i) % ((size_t)dk * dv)];"),
+    ("initial_state_ignored", "if (J->S0) {", "if (0) {"),
+    ("first_token_skipped", "for (int64_t t = J->cu[n]; t < J->cu[n + 1]; ++t)",
+     "for (int64_t t = J->cu[n] + (J->cu[n + 1] > J->cu[n]); t < J->cu[n + 1]; ++t)"),
+    ("rank1_update_dropped", "S[(size_t)i * dv + j] += ki * u[j];",
+     "S[(size_t)i * dv + j] += 0.0 * ki * u[j];"),
+]
+
+_CHILD = r"""
+import json, sys
+sys.path[:0] = [sys.argv[1], sys.argv[2]]
+import oracle, oracle_pins
+lib = oracle.bind(sys.argv[3])
+print(json.dumps(oracle_pins.run_all(lib)))
+"""
+
+
+def _readout_before_update(src):
+    """Move step 5 (read-out) in front of step 4 (rank-1 correction)."""
+    a = src.index("        /* 4. rank-1 correction")
+    b = src.index("        /* 5. read-out")
+    c = src.index("    }\n    memcpy(J->S_T + sbase")
+    return src[:a] + src[b:c] + src[a:b] + src[c:]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS + [("readout_before_update", None, None)],
+                         ids=[m[0] for m in MUTANTS] + ["readout_before_update"])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(_SRC).read()
+    if old is None:
+        mutated = _readout_before_update(src)
+    else:
+        assert src.count(old) >= 1, f"mutation anchor for {name} not found in the oracle"
+        mutated = src.replace(old, new, 1)
+    assert mutated != src
+    c_path = tmp_path / "kda_oracle.c"
+    c_path.write_text(mutated)
+    (tmp_path / "kda_oracle.h").write_text(open(_SRC[:-2] + ".h").read())
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", str(so),
+                    str(c_path), "-lm"], check=True)
+    r = subprocess.run([sys.executable, "-c", _CHILD, _ROOT, os.path.join(_ROOT, "tests"),
+                        str(so)], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        return  # the mutant crashed the pin run: caught
+    failed = json.loads(r.stdout.strip().splitlines()[-1])
+    assert failed, f"mutant {name} passed every pin"
