@@ -1,0 +1,212 @@
+"""ctypes binding of libkda.so (include/kda.h).
+
+The functions named ``kda_*`` mirror the C ABI one to one and take raw
+device pointers (ints) and a stream handle.  ``prefill`` and ``decode_step``
+are argument-marshalling conveniences over torch tensors: they check shapes
+and dtypes, allocate outputs with torch when none are given, and call the C
+ABI on torch's current stream.  Every arithmetic step runs in the library's
+HIP kernels; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARG = 1
+KDA_ERR_UNSUPPORTED = 2
+KDA_ERR_HIP = 3
+KDA_DTYPE_BF16 = 0
+KDA_DTYPE_F32 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+# (name, restype, argtypes) for every symbol declared in include/kda.h
+_vp, _fp, _ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+_i32, _i64, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "kda_prefill": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32, _i32,
+                                   ctypes.c_int, _vp, _fp, _vp, _sz, _vp]),
+    "kda_prefill_split": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32,
+                                         _i32, ctypes.c_int, _vp, _fp, _vp, _sz, _i32, _vp]),
+    "kda_prefill_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int]),
+    "kda_prefill_default_split": (_i32, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int]),
+    "kda_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _i32, _i32, _i32, _i32,
+                                       ctypes.c_int, _vp, _vp]),
+    "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kda_last_error": (ctypes.c_char_p, []),
+    "kda_version": (_i32, []),
+}
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{kda_status_string(status)}: {detail}")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libkda.so")
+
+
+def load() -> ctypes.CDLL:
+    """Open libkda.so; raise if it has not been built (no fallback exists)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m gated_delta_rule_60_amd.build` "
+                           "(the KDA forward pass has no other implementation)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# C ABI, one to one
+# ---------------------------------------------------------------------------
+def kda_prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
+                workspace, workspace_bytes, stream) -> int:
+    return load().kda_prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype,
+                              o, S_T, workspace, workspace_bytes, stream)
+
+
+def kda_prefill_split(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
+                      workspace, workspace_bytes, v_split, stream) -> int:
+    return load().kda_prefill_split(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
+                                    dtype, o, S_T, workspace, workspace_bytes, v_split, stream)
+
+
+def kda_prefill_workspace_size(N, T_tot, H, d_k, d_v, dtype) -> int:
+    return int(load().kda_prefill_workspace_size(N, T_tot, H, d_k, d_v, dtype))
+
+
+def kda_prefill_default_split(N, T_tot, H, d_k, d_v, dtype) -> int:
+    return int(load().kda_prefill_default_split(N, T_tot, H, d_k, d_v, dtype))
+
+
+def kda_decode_step(q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype, o, stream) -> int:
+    return load().kda_decode_step(q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype, o, stream)
+
+
+def kda_status_string(status: int) -> str:
+    return load().kda_status_string(status).decode()
+
+
+def kda_last_error() -> str:
+    return load().kda_last_error().decode()
+
+
+def kda_version() -> int:
+    return int(load().kda_version())
+
+
+def _check(status: int) -> None:
+    if status != KDA_OK:
+        raise KDAError(status, kda_last_error())
+
+
+# ---------------------------------------------------------------------------
+# torch conveniences (marshalling only)
+# ---------------------------------------------------------------------------
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return KDA_DTYPE_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t, name, shape, dtype, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(stream, device) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return int(s.cuda_stream)
+
+
+def prefill(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=None,
+            v_split: int = 0, stream=None):
+    """KDA chunked prefill on torch tensors; returns (o, S_T).
+
+    q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
+    log_alpha: [T, H, d_k] fp32; beta: [T, H] fp32; S0: [N, H, d_k, d_v] fp32
+    or None; cu_seqlens: int32 [N + 1] on the device (None = one sequence).
+    ``S_T`` may be ``S0`` itself (in-place update of the states).
+    """
+    import torch
+    if not q.is_cuda:
+        raise ValueError("kda prefill runs on a GPU device; q is on the CPU")
+    dev = q.device
+    T, H, dk = (int(x) for x in q.shape)
+    dv = int(v.shape[-1])
+    code = _dtype_code(q)
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    N = int(cu_seqlens.shape[0]) - 1
+    _need(q, "q", (T, H, dk), q.dtype, dev)
+    _need(k, "k", (T, H, dk), q.dtype, dev)
+    _need(v, "v", (T, H, dv), q.dtype, dev)
+    _need(log_alpha, "log_alpha", (T, H, dk), torch.float32, dev)
+    _need(beta, "beta", (T, H), torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if S0 is not None:
+        _need(S0, "S0", (N, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    if S_T is None:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _need(o, "o", (T, H, dv), q.dtype, dev)
+    _need(S_T, "S_T", (N, H, dk, dv), torch.float32, dev)
+    ws = kda_prefill_workspace_size(N, T, H, dk, dv, code)
+    wbuf = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+    with torch.cuda.device(dev):
+        _check(kda_prefill_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
+                                 beta.data_ptr(), S0.data_ptr() if S0 is not None else None,
+                                 cu_seqlens.data_ptr(), N, T, H, dk, dv, code, o.data_ptr(),
+                                 S_T.data_ptr(), wbuf.data_ptr() if wbuf is not None else None, ws,
+                                 int(v_split), _stream_handle(stream, dev)))
+    return o, S_T
+
+
+def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
+    """One KDA decode step; S [N, H, d_k, d_v] fp32 is updated in place.
+    Returns o [N, H, d_v] in q's dtype."""
+    import torch
+    if not q.is_cuda:
+        raise ValueError("kda decode runs on a GPU device; q is on the CPU")
+    dev = q.device
+    N, H, dk = (int(x) for x in q.shape)
+    dv = int(v.shape[-1])
+    code = _dtype_code(q)
+    _need(q, "q", (N, H, dk), q.dtype, dev)
+    _need(k, "k", (N, H, dk), q.dtype, dev)
+    _need(v, "v", (N, H, dv), q.dtype, dev)
+    _need(log_alpha, "log_alpha", (N, H, dk), torch.float32, dev)
+    _need(beta, "beta", (N, H), torch.float32, dev)
+    _need(S, "S", (N, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "o", (N, H, dv), q.dtype, dev)
+    with torch.cuda.device(dev):
+        _check(kda_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
+                               beta.data_ptr(), S.data_ptr(), N, H, dk, dv, code, o.data_ptr(),
+                               _stream_handle(stream, dev)))
+    return o

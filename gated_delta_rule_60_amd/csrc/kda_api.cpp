@@ -1,0 +1,139 @@
+// kda_api.cpp -- the C ABI declared in include/kda.h: host-side argument
+// validation (before any HIP call), launch-shape selection and error text.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "kda_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status fail(kda_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kda_status check_dims(int32_t d_k, int32_t d_v, kda_dtype dtype) {
+    if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32)
+        return fail(KDA_ERR_UNSUPPORTED, "dtype must be KDA_DTYPE_BF16 or KDA_DTYPE_F32");
+    if (!supported_dim(d_k) || !supported_dim(d_v))
+        return fail(KDA_ERR_UNSUPPORTED, "d_k and d_v must each be 32, 64 or 128 (got " +
+                                             std::to_string(d_k) + ", " + std::to_string(d_v) + ")");
+    return KDA_OK;
+}
+
+kda_status hip_fail(hipError_t e, const char* what) {
+    return fail(KDA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_version(void) { return KDA_VERSION; }
+
+const char* kda_status_string(kda_status status) {
+    switch (status) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported size or dtype";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error";
+        default: return "unknown kda_status";
+    }
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+size_t kda_prefill_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
+                                  kda_dtype dtype) {
+    (void)N;
+    (void)T_tot;
+    (void)H;
+    (void)d_k;
+    (void)d_v;
+    (void)dtype;
+    return 0;
+}
+
+int32_t kda_prefill_default_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
+                                  kda_dtype dtype) {
+    (void)T_tot;
+    if (N < 1 || H < 1 || !supported_dim(d_k) || !supported_dim(d_v) ||
+        (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32))
+        return 0;
+    return kda::default_v_split(N, H, d_k, d_v, dtype == KDA_DTYPE_BF16);
+}
+
+kda_status kda_prefill_split(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, const float* S0, const int32_t* cu_seqlens,
+                             int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
+                             kda_dtype dtype, void* o, float* S_T, void* workspace,
+                             size_t workspace_bytes, int32_t v_split, void* stream) {
+    g_last_error.clear();
+    if (N < 1 || H < 1 || T_tot < 0)
+        return fail(KDA_ERR_INVALID_ARG, "need N >= 1, H >= 1 and T_tot >= 0");
+    const kda_status ds = check_dims(d_k, d_v, dtype);
+    if (ds != KDA_OK) return ds;
+    if (!cu_seqlens || !S_T) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens and S_T must not be NULL");
+    if (T_tot > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
+        return fail(KDA_ERR_INVALID_ARG, "q, k, v, log_alpha, beta and o must not be NULL when T_tot > 0");
+    if (T_tot > INT32_MAX) return fail(KDA_ERR_INVALID_ARG, "T_tot must fit in int32 (cu_seqlens is int32)");
+    const void* ptrs[] = {q, k, v, log_alpha, o, S0, S_T};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (workspace_bytes < kda_prefill_workspace_size(N, T_tot, H, d_k, d_v, dtype))
+        return fail(KDA_ERR_INVALID_ARG, "workspace smaller than kda_prefill_workspace_size");
+    (void)workspace;
+    if (v_split == 0) v_split = kda::default_v_split(N, H, d_k, d_v, dtype == KDA_DTYPE_BF16);
+    if (!(v_split == 1 || v_split == 2 || v_split == 4 || v_split == 8) || d_v / v_split < 16)
+        return fail(KDA_ERR_INVALID_ARG, "v_split must be 1, 2, 4 or 8 with d_v / v_split >= 16");
+    const int64_t grid = static_cast<int64_t>(N) * H * v_split;
+    if (grid > INT32_MAX) return fail(KDA_ERR_INVALID_ARG, "N * H * v_split too large");
+
+    kda::PrefillArgs a{q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
+                       dtype == KDA_DTYPE_BF16, o, S_T, v_split, stream};
+    (void)hipGetLastError();  // report only this launch's status
+    const hipError_t e = kda::launch_prefill(a);
+    if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+    return KDA_OK;
+}
+
+kda_status kda_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
+                       const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
+                       int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
+                       float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
+    return kda_prefill_split(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype,
+                             o, S_T, workspace, workspace_bytes, 0, stream);
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* beta, float* S, int32_t N, int32_t H, int32_t d_k,
+                           int32_t d_v, kda_dtype dtype, void* o, void* stream) {
+    g_last_error.clear();
+    if (N < 1 || H < 1) return fail(KDA_ERR_INVALID_ARG, "need N >= 1 and H >= 1");
+    const kda_status ds = check_dims(d_k, d_v, dtype);
+    if (ds != KDA_OK) return ds;
+    if (!q || !k || !v || !log_alpha || !beta || !S || !o)
+        return fail(KDA_ERR_INVALID_ARG, "q, k, v, log_alpha, beta, S and o must not be NULL");
+    const void* ptrs[] = {q, k, v, log_alpha, S, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(KDA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (static_cast<int64_t>(N) * H > INT32_MAX) return fail(KDA_ERR_INVALID_ARG, "N * H too large");
+    kda::DecodeArgs a{q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype == KDA_DTYPE_BF16, o, stream};
+    (void)hipGetLastError();  // report only this launch's status
+    const hipError_t e = kda::launch_decode(a);
+    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    return KDA_OK;
+}
+
+}  // extern "C"

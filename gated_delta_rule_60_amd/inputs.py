@@ -40,16 +40,25 @@ __all__ = [
 ]
 
 
-def round_to_bf16(x: np.ndarray) -> np.ndarray:
+def round_to_bf16(x: np.ndarray, out: Optional[np.ndarray] = None) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even).
 
     Returns float32 values that are exactly representable in bfloat16, so a
-    later float32 -> bfloat16 cast is exact.  Inputs must be finite.
+    later float32 -> bfloat16 cast is exact.  Inputs must be finite (then the
+    32-bit integer sum below cannot overflow).  ``out`` may be ``x`` itself.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    if out is None:
+        out = np.empty_like(x)
+    src = x.reshape(-1).view(np.uint32)
+    dst = out.reshape(-1).view(np.uint32)
+    step = 1 << 22
+    for s in range(0, src.shape[0], step):
+        u = src[s:s + step].copy()
+        u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+        u &= np.uint32(0xFFFF0000)
+        dst[s:s + step] = u
+    return out
 
 
 @dataclasses.dataclass
@@ -94,26 +103,36 @@ class DecodeStepInputs:
     dtype: str
 
 
-def _unit_rows(x: np.ndarray) -> np.ndarray:
-    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
-    return (x / n.astype(np.float32)).astype(np.float32)
+def _unit_rows_(x: np.ndarray) -> np.ndarray:
+    """Divide each row (last axis) by its L2 norm, in place, block by block;
+    the norm is accumulated in float64."""
+    flat = x.reshape(-1, x.shape[-1])
+    step = 1 << 18
+    for s in range(0, flat.shape[0], step):
+        blk = flat[s:s + step]
+        n = np.sqrt(np.einsum("ij,ij->i", blk, blk, dtype=np.float64))
+        blk /= n.astype(np.float32)[:, None]
+    return x
 
 
 def _qkv_gates(rng: np.random.Generator, lead: tuple, d_k: int, d_v: int,
                log_alpha_range: tuple, dtype: str):
-    q = _unit_rows(rng.standard_normal(lead + (d_k,), dtype=np.float32))
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(f"unknown dtype {dtype!r}")
+    q = _unit_rows_(rng.standard_normal(lead + (d_k,), dtype=np.float32))
     q *= np.float32(1.0 / np.sqrt(d_k))
-    k = _unit_rows(rng.standard_normal(lead + (d_k,), dtype=np.float32))
+    k = _unit_rows_(rng.standard_normal(lead + (d_k,), dtype=np.float32))
     v = rng.standard_normal(lead + (d_v,), dtype=np.float32)
     lo, hi = log_alpha_range
-    log_alpha = -(np.float32(lo) + np.float32(hi - lo) * rng.random(lead + (d_k,), dtype=np.float32))
+    log_alpha = rng.random(lead + (d_k,), dtype=np.float32)
+    log_alpha *= np.float32(-(hi - lo))
+    log_alpha -= np.float32(lo)
     z = rng.standard_normal(lead, dtype=np.float32)
     beta = (1.0 / (1.0 + np.exp(-z.astype(np.float64)))).astype(np.float32)
     if dtype == "bf16":
-        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
-    elif dtype != "f32":
-        raise ValueError(f"unknown dtype {dtype!r}")
-    return q, k, v, log_alpha.astype(np.float32), beta
+        for a in (q, k, v):
+            round_to_bf16(a, out=a)
+    return q, k, v, log_alpha, beta
 
 
 def varlen_lengths(rng: np.random.Generator, n: int, lo: int, hi: int) -> list:

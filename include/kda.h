@@ -1,0 +1,148 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward pass.
+ *
+ * What is computed.  For every sequence n and head h, token by token, the
+ * KDA update rule of "Kimi Linear：让长上下文大模型真正实用的线性注意力架构"
+ * (juejin.cn), section 三.5:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                                   (read-out after the update)
+ *
+ * alpha_t = exp(log_alpha_t) holds one retention factor per key channel (the
+ * fine-grained gate of section 三.1); beta_t is one scalar step size per token
+ * and head (section 三.5 reads the update as one online gradient-descent step
+ * of size beta_t).  S is a d_k x d_v matrix per (sequence, head): row i is key
+ * channel i, column j is value channel j.  The pages apply no rotary position
+ * encoding (section 三.4, NoPE), and neither does this library: q and k are
+ * used as given (scaling and normalisation are the caller's).  The read-out
+ * rule is not printed on the pages; o_t = S_t^T q_t is the numerator of the
+ * kernelised linear-attention form Q (K^T V) on the xdnf.cn page, section 2.2.
+ *
+ * Conventions shared by every entry point.
+ *  - Pointers named "device" are HIP device pointers on the current device;
+ *    the caller owns every buffer.  The library allocates no device memory
+ *    and keeps no global mutable state apart from a thread-local error text.
+ *  - All tensors are dense, contiguous and row-major with the shapes given.
+ *    Floating-point pointers must be 16-byte aligned.
+ *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL is the default stream) and never synchronises.  Arguments are
+ *    validated on the host before any HIP call; a kernel fault surfaces at
+ *    the caller's next synchronisation.
+ *  - Results are deterministic: the same inputs give the same bits.
+ *  - Numerical contract: log_alpha finite and <= 0 with the sum of log_alpha
+ *    over any 64 consecutive tokens of a sequence >= -80 per channel (the
+ *    chunked prefill evaluates exp(+-that sum) in fp32); beta finite.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, small workspace */
+    KDA_ERR_UNSUPPORTED = 2, /* head dimension or dtype this build does not support */
+    KDA_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
+} kda_status;
+
+typedef enum {
+    KDA_DTYPE_BF16 = 0, /* q, k, v, o stored as bfloat16 */
+    KDA_DTYPE_F32 = 1   /* q, k, v, o stored as float32 */
+} kda_dtype;
+
+/*
+ * kda_prefill -- chunk-parallel forward pass over a packed batch of
+ * variable-length sequences (section 三.2 of the same page: the specialised
+ * diagonal-plus-low-rank transition admits chunk-parallel evaluation).
+ *
+ *   q          device [T_tot, H, d_k]  dtype      queries
+ *   k          device [T_tot, H, d_k]  dtype      keys
+ *   v          device [T_tot, H, d_v]  dtype      values
+ *   log_alpha  device [T_tot, H, d_k]  float32    log of the per-channel decay
+ *   beta       device [T_tot, H]       float32    step size
+ *   S0         device [N, H, d_k, d_v] float32    initial states; NULL = zero
+ *   cu_seqlens device [N + 1]          int32      sequence offsets: cu[0] = 0,
+ *              non-decreasing, cu[N] = T_tot.  Its contents are read on the
+ *              device only and are not checked (the caller's contract).
+ *   N, T_tot, H        >= 1, >= 0, >= 1
+ *   d_k, d_v           each one of 32, 64, 128
+ *   dtype              storage type of q, k, v and o
+ *   o          device [T_tot, H, d_v]  dtype      outputs (written)
+ *   S_T        device [N, H, d_k, d_v] float32    final states (written); may
+ *              be the same pointer as S0.  An empty sequence gives S_T = S0.
+ *   workspace, workspace_bytes   scratch of at least
+ *              kda_prefill_workspace_size(...) bytes (currently 0; NULL allowed)
+ *   stream     hipStream_t or NULL
+ * q, k, v, log_alpha, beta and o may be NULL when T_tot == 0.  No state
+ * crosses a sequence boundary.
+ */
+kda_status kda_prefill(const void* q, const void* k, const void* v,
+                       const float* log_alpha, const float* beta, const float* S0,
+                       const int32_t* cu_seqlens, int32_t N, int64_t T_tot, int32_t H,
+                       int32_t d_k, int32_t d_v, kda_dtype dtype, void* o, float* S_T,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_prefill_split -- kda_prefill with an explicit launch shape: the d_v
+ * value columns of every (sequence, head) are split over `v_split`
+ * workgroups that each run the whole chunk recurrence for d_v / v_split
+ * columns (the columns of S evolve independently).  v_split must be 1, 2, 4
+ * or 8 with d_v / v_split >= 16.  v_split = 0 selects the same shape as
+ * kda_prefill.  Results differ from kda_prefill only by rounding order of
+ * no operation: every v_split gives the same bits.
+ */
+kda_status kda_prefill_split(const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, const float* S0,
+                             const int32_t* cu_seqlens, int32_t N, int64_t T_tot, int32_t H,
+                             int32_t d_k, int32_t d_v, kda_dtype dtype, void* o, float* S_T,
+                             void* workspace, size_t workspace_bytes, int32_t v_split,
+                             void* stream);
+
+/* Bytes of workspace kda_prefill needs for these sizes (0 in this version). */
+size_t kda_prefill_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
+                                  int32_t d_v, kda_dtype dtype);
+
+/* The v_split kda_prefill would use for these sizes (1, 2, 4 or 8), or 0 if
+ * the sizes are not supported. */
+int32_t kda_prefill_default_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
+                                  int32_t d_v, kda_dtype dtype);
+
+/*
+ * kda_decode_step -- one token for each of N independent sequences (the same
+ * update rule, one step), with the state updated in place.  Each state is
+ * read from and written to HBM exactly once.
+ *
+ *   q, k       device [N, H, d_k]      dtype
+ *   v          device [N, H, d_v]      dtype
+ *   log_alpha  device [N, H, d_k]      float32
+ *   beta       device [N, H]           float32
+ *   S          device [N, H, d_k, d_v] float32   read and overwritten
+ *   N, H >= 1; d_k, d_v each one of 32, 64, 128
+ *   o          device [N, H, d_v]      dtype     written
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, float* S, int32_t N,
+                           int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
+                           void* stream);
+
+/* Static text for a status code. */
+const char* kda_status_string(kda_status status);
+
+/* Detail of the last failed call on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+/* KDA_VERSION of the library. */
+int32_t kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

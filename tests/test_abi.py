@@ -1,0 +1,115 @@
+"""The C ABI of libkda.so on the CPU: every symbol of include/kda.h is
+exported, and every invalid-argument path returns its status before any HIP
+call (no kernel is launched here)."""
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_60_amd as kda
+from gated_delta_rule_60_amd import _lib
+
+_ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+BF16, F32 = kda.KDA_DTYPE_BF16, kda.KDA_DTYPE_F32
+
+
+def _declared_functions():
+    text = open(os.path.join(_ROOT, "include", "kda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("kda_prefill", "kda_decode_step", "kda_prefill_workspace_size",
+                     "kda_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kda.load()
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} declared in kda.h but not exported"
+        assert name in _lib.SIGNATURES, f"{name} has no binding in _lib.py"
+
+
+def test_status_strings_and_version():
+    assert kda.kda_version() == 1
+    for s in (0, 1, 2, 3):
+        assert kda.kda_status_string(s).startswith("KDA_")
+    assert "unknown" in kda.kda_status_string(99)
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, log_alpha=FAKE, beta=FAKE, S0=None, cu_seqlens=FAKE, N=1,
+             T_tot=64, H=2, d_k=64, d_v=64, dtype=BF16, o=FAKE, S_T=FAKE, workspace=None,
+             workspace_bytes=0, v_split=0, stream=None)
+    a.update(kw)
+    return kda.kda_prefill_split(**a)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(N=0), kda.KDA_ERR_INVALID_ARG, "N >= 1"),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARG, "H >= 1"),
+    (dict(T_tot=-1), kda.KDA_ERR_INVALID_ARG, "T_tot"),
+    (dict(d_k=48), kda.KDA_ERR_UNSUPPORTED, "d_k and d_v"),
+    (dict(d_v=256), kda.KDA_ERR_UNSUPPORTED, "d_k and d_v"),
+    (dict(dtype=7), kda.KDA_ERR_UNSUPPORTED, "dtype"),
+    (dict(cu_seqlens=None), kda.KDA_ERR_INVALID_ARG, "cu_seqlens"),
+    (dict(S_T=None), kda.KDA_ERR_INVALID_ARG, "S_T"),
+    (dict(q=None), kda.KDA_ERR_INVALID_ARG, "must not be NULL"),
+    (dict(beta=None), kda.KDA_ERR_INVALID_ARG, "must not be NULL"),
+    (dict(o=None), kda.KDA_ERR_INVALID_ARG, "must not be NULL"),
+    (dict(k=FAKE + 4), kda.KDA_ERR_INVALID_ARG, "aligned"),
+    (dict(S0=FAKE + 8), kda.KDA_ERR_INVALID_ARG, "aligned"),
+    (dict(v_split=3), kda.KDA_ERR_INVALID_ARG, "v_split"),
+    (dict(v_split=8), kda.KDA_ERR_INVALID_ARG, "v_split"),  # 64 / 8 < 16
+    (dict(T_tot=2**31), kda.KDA_ERR_INVALID_ARG, "int32"),
+])
+def test_prefill_rejects_invalid_arguments(kw, status, needle):
+    assert _prefill(**kw) == status
+    assert needle in kda.kda_last_error()
+
+
+def test_prefill_entry_point_validates_too():
+    rc = kda.kda_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 10, 1, 32, 100, BF16, FAKE,
+                         FAKE, None, 0, None)
+    assert rc == kda.KDA_ERR_UNSUPPORTED
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, log_alpha=FAKE, beta=FAKE, S=FAKE, N=4, H=2, d_k=128, d_v=128,
+             dtype=F32, o=FAKE, stream=None)
+    a.update(kw)
+    return kda.kda_decode_step(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), kda.KDA_ERR_INVALID_ARG),
+    (dict(H=-1), kda.KDA_ERR_INVALID_ARG),
+    (dict(d_k=16), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=2), kda.KDA_ERR_UNSUPPORTED),
+    (dict(S=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(o=None), kda.KDA_ERR_INVALID_ARG),
+    (dict(v=FAKE + 2), kda.KDA_ERR_INVALID_ARG),
+])
+def test_decode_rejects_invalid_arguments(kw, status):
+    assert _decode(**kw) == status
+    assert kda.kda_last_error() != ""
+
+
+def test_workspace_and_default_split_queries():
+    assert kda.kda_prefill_workspace_size(8, 32677, 32, 128, 128, BF16) == 0
+    for (N, H) in ((1, 32), (8, 32), (256, 32), (1, 2)):
+        s = kda.kda_prefill_default_split(N, 4096, H, 128, 128, BF16)
+        assert s in (1, 2, 4, 8)
+    assert kda.kda_prefill_default_split(1, 10, 1, 48, 128, BF16) == 0
+    assert kda.kda_prefill_default_split(1, 10, 1, 32, 32, BF16) in (1, 2)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_LIB", None)
+    monkeypatch.setattr(_lib, "_HERE", str(tmp_path))
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()

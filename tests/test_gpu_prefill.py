@@ -1,0 +1,107 @@
+"""GPU prefill parity against the fp64 oracle (through the C ABI).
+
+Small cases span several chunks, ragged tails (lengths 1, 63, 64, 65, 127),
+empty sequences, d_k != d_v, both dtypes and every launch shape; the full
+workloads compare all outputs (T=256 fp32, T=4096) or oracle-sampled heads
+(the 32k varlen batch and the 128k sequence) in the launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+
+import gated_delta_rule_60_amd as kda
+import oracle
+from gated_delta_rule_60_amd import inputs
+from gpu_util import assert_close, host, log, upload, valid_splits
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # lengths, H, d_k, d_v, dtype, s0
+    ([1], 1, 32, 32, "f32", True),
+    ([63, 64, 65], 2, 32, 32, "f32", False),
+    ([127, 0, 200], 2, 64, 64, "f32", True),
+    ([130, 1, 64], 2, 128, 128, "f32", True),
+    ([64, 65], 1, 64, 128, "f32", True),
+    ([1, 63, 64, 65, 0, 127], 3, 128, 128, "bf16", True),
+    ([300], 2, 64, 32, "bf16", True),
+    ([77, 190], 2, 32, 128, "bf16", False),
+    ([129, 255], 2, 64, 64, "bf16", True),
+    ([513], 1, 128, 64, "bf16", True),
+]
+
+
+def _small_id(c):
+    return f"L{'-'.join(map(str, c[0]))}_H{c[1]}_dk{c[2]}_dv{c[3]}_{c[4]}_{'S0' if c[5] else 'zero'}"
+
+
+def _run_case(lengths, H, dk, dv, dtype, s0, seed):
+    x = inputs.make_prefill_inputs(lengths, H, dk, dv, dtype, seed=seed,
+                                   s0_std=1.0 if s0 else None)
+    ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens)
+    d = upload(x)
+    for split in valid_splits(dv):
+        log(f"  prefill {lengths} H={H} dk={dk} dv={dv} {dtype} v_split={split}")
+        o, ST = kda.prefill(**d, v_split=split)
+        assert_close(host(o), ref_o, dtype, "o")
+        assert_close(host(ST), ref_S, dtype, "S_T")
+
+
+@pytest.mark.parametrize("case", SMALL, ids=_small_id)
+def test_small_cases_every_split(case):
+    _run_case(*case, seed=sum(case[0]) + case[2])
+
+
+def test_workload_t256_fp32():
+    x = inputs.make_workload("prefill_t256_h2_d32_f32")
+    ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens)
+    o, ST = kda.prefill(**upload(x))
+    assert_close(host(o), ref_o, "f32", "o")
+    assert_close(host(ST), ref_S, "f32", "S_T")
+
+
+def test_workload_t4096():
+    x = inputs.make_workload("prefill_t4096_h32_d128_bf16")
+    log("  oracle, 32 heads x 4096 tokens")
+    ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens)
+    o, ST = kda.prefill(**upload(x))
+    assert_close(host(o), ref_o, "bf16", "o")
+    assert_close(host(ST), ref_S, "bf16", "S_T")
+
+
+def _sampled(x, heads):
+    mask = np.zeros((x.N, x.H), bool)
+    mask[:, heads] = True
+    return mask
+
+
+def test_workload_varlen_32k_sampled_heads():
+    x = inputs.make_workload("prefill_varlen8_32k_h32_d128_bf16")
+    heads = [0, 13, 31]
+    log(f"  oracle on heads {heads} of all 8 sequences")
+    ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens,
+                                  pair_mask=_sampled(x, heads))
+    o, ST = kda.prefill(**upload(x))
+    o, ST = host(o), host(ST)
+    assert_close(o[:, heads], ref_o[:, heads], "bf16", "o (sampled heads)")
+    assert_close(ST[:, heads], ref_S[:, heads], "bf16", "S_T (sampled heads)")
+    for n in range(x.N):
+        a, b = x.cu_seqlens[n], x.cu_seqlens[n + 1]
+        assert_close(o[a:b, heads], ref_o[a:b, heads], "bf16", f"o sequence {n} (len {b - a})")
+
+
+def test_workload_128k_sampled_heads_windows():
+    x = inputs.make_workload("prefill_t131072_h32_d128_bf16")
+    heads = [5, 26]
+    log(f"  oracle on heads {heads} over 131072 tokens")
+    ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens,
+                                  pair_mask=_sampled(x, heads))
+    d = upload(x)
+    del x
+    o, ST = kda.prefill(**d)
+    o = host(o[:, heads])
+    ST = host(ST[:, heads])
+    assert_close(ST, ref_S[:, heads], "bf16", "S_T")
+    assert_close(o[:4096], ref_o[:4096, heads], "bf16", "o first 4096")
+    assert_close(o[-4096:], ref_o[-4096:, heads], "bf16", "o last 4096")
+    assert_close(o, ref_o[:, heads], "bf16", "o all tokens")
