@@ -88,6 +88,8 @@ kda_status kda_prefill_split(const void* q, const void* k, const void* v, const 
     if (T_tot > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
         return fail(KDA_ERR_INVALID_ARG, "q, k, v, log_alpha, beta and o must not be NULL when T_tot > 0");
     if (T_tot > INT32_MAX) return fail(KDA_ERR_INVALID_ARG, "T_tot must fit in int32 (cu_seqlens is int32)");
+    if (T_tot * H * static_cast<int64_t>(d_k > d_v ? d_k : d_v) > INT32_MAX)
+        return fail(KDA_ERR_INVALID_ARG, "q, k, v, o and log_alpha must each hold fewer than 2^31 elements");
     const void* ptrs[] = {q, k, v, log_alpha, o, S0, S_T};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");

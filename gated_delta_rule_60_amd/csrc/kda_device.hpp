@@ -14,7 +14,7 @@
 // frag8 operand with no data movement.  A 16-deep block is a "frag4":
 // slot j <-> k = 4*g + j, which is exactly one C-layout tile.
 //
-//   bf16: frag8 -> v_mfma_f32_16x16x32_bf16, frag4 -> v_mfma_f32_16x16x16_bf16
+//   bf16: frag8 -> v_mfma_f32_16x16x32_bf16, frag4 -> the same with the upper k half zero
 //   f32 : frag8 -> 8 x v_mfma_f32_16x16x4_f32,  frag4 -> 4 x v_mfma_f32_16x16x4_f32
 #pragma once
 
@@ -58,6 +58,16 @@ struct Elem<true> {
     using E = __bf16;
     using F8 = bf16x8_t;
     using F4 = bf16x4_t;
+    using R4 = uint2;  // four consecutive global elements, raw
+    __device__ static __forceinline__ R4 raw4(const G* p) { return *reinterpret_cast<const uint2*>(p); }
+    __device__ static __forceinline__ void unpack4(const R4& r, float (&x)[4]) {
+        x[0] = __uint_as_float(r.x << 16);
+        x[1] = __uint_as_float(r.x & 0xFFFF0000u);
+        x[2] = __uint_as_float(r.y << 16);
+        x[3] = __uint_as_float(r.y & 0xFFFF0000u);
+    }
+    // raw global quad -> four LDS operand elements (bit copy)
+    __device__ static __forceinline__ void lds_put_raw4(E* p, const R4& r) { *reinterpret_cast<uint2*>(p) = r; }
     // four consecutive global elements -> floats
     __device__ static __forceinline__ void load4(const G* p, float (&x)[4]) {
         const uint2 r = *reinterpret_cast<const uint2*>(p);
@@ -83,6 +93,15 @@ struct Elem<false> {
     using E = float;
     using F8 = f32x8_t;
     using F4 = f32x4_t;
+    using R4 = float4;
+    __device__ static __forceinline__ R4 raw4(const G* p) { return *reinterpret_cast<const float4*>(p); }
+    __device__ static __forceinline__ void unpack4(const R4& r, float (&x)[4]) {
+        x[0] = r.x;
+        x[1] = r.y;
+        x[2] = r.z;
+        x[3] = r.w;
+    }
+    __device__ static __forceinline__ void lds_put_raw4(E* p, const R4& r) { *reinterpret_cast<float4*>(p) = r; }
     __device__ static __forceinline__ void load4(const G* p, float (&x)[4]) {
         const float4 r = *reinterpret_cast<const float4*>(p);
         x[0] = r.x;

@@ -17,20 +17,31 @@
 //     (I + L) U = beta (V - K~ S)                  (U: C x d_v)
 //     O      = Q~ S + A_qk U
 //     S_next = Diag(Gamma_C) S + Kbar^T U
-// (I + L) is unit lower triangular.  Its four 16x16 diagonal blocks are
-// inverted by forward substitution in fp32 (T_bb = (I + L_bb)^-1); U is then
-// obtained block by block, U_b = T_bb (R_b - sum_{c<b} L_bc U_c), with
-// MFMA products.  Padded tail rows (past the end of a sequence) carry
-// k = q = v = beta = log alpha = 0 and therefore contribute nothing.
+// (I + L) is unit lower triangular.  Its 16x16 diagonal blocks are inverted
+// by forward substitution in fp32 (T_bb = (I + L_bb)^-1); U is obtained block
+// by block, U_b = T_bb (R_b - sum_{c<b} L_bc U_c), with MFMA products.
+// Padded tail rows (past the end of a sequence) carry k = q = v = beta =
+// log alpha = 0 and therefore contribute nothing.
 //
-// Parallel decomposition.  One workgroup per (sequence, head, value slice);
-// it walks its sequence chunk by chunk.  Each wave owns 16 value columns of
-// the state for the whole sequence, in registers (fp32, MFMA C layout); the
-// columns of S evolve independently, so the per-column work (R, U, O and
-// the state update) never leaves the wave.  The S-independent terms of a
-// chunk (decayed operands, Gram products, the block-diagonal inverse) are
-// built cooperatively in LDS.  All MFMA operands are bf16 (or fp32 for f32
-// inputs); accumulation and the carried state are fp32.
+// Parallel decomposition.  One workgroup per (sequence, head, value slice)
+// walks its sequence chunk by chunk.  Each wave owns CT 16-column tiles of
+// the state for the whole sequence, in fp32 registers (MFMA C layout); the
+// columns of S evolve independently, so the per-column work never leaves the
+// wave, and one LDS read of a shared operand feeds CT MFMAs.
+//
+// Software pipeline.  The S-independent terms of a chunk ("prep") are built
+// one chunk ahead of the S-dependent recurrence ("chain"), in the same
+// barrier stages, from double-buffered LDS tiles, so that prep's VALU and
+// LDS work overlaps the chain's MFMA work.  For chunk i:
+//     stage X: block inverse of i (one wave)  | prep 1 of i+1: beta, V^T, sums
+//              of log alpha                    | chain of i: R'
+//     stage Y: prep 2 of i+1: cumulative decay, decayed tiles; loads of i+2
+//                                              | chain of i: U, O
+//     stage Z: prep 3 of i+1: Gram products    | chain of i: S update, O store
+// All MFMA operands are bf16 (or fp32 for f32 inputs); accumulation and the
+// carried state are fp32.
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -43,39 +54,63 @@ constexpr size_t align16(size_t x) { return (x + 15) & ~static_cast<size_t>(15);
 // Sequence-length ordering (longest first) is computed in-kernel for up to
 // this many sequences; larger batches run in natural order.
 constexpr int kSortMax = 64;
+constexpr size_t kLdsBudget = 160 * 1024;
 
-template <bool BF16, int DK, int NW>
-struct PrefillShape {
+template <bool BF16, int DK, int NW, int CT, int C_>
+struct Layout {
     using E = typename Elem<BF16>::E;
-    static constexpr int C = (!BF16 && DK == 128) ? 32 : 64;  // chunk length
-    static constexpr int NB = C / 16;                          // 16-row blocks per chunk
-    static constexpr int NT = 64 * NW;                         // threads
-    static constexpr int BV = 16 * NW;                         // value columns per workgroup
+    static constexpr int C = C_;
+    static constexpr int NB = C / 16;
+    static constexpr int NT = 64 * NW;
+    static constexpr int BV = 16 * CT * NW;
     static constexpr int PAD = 16 / static_cast<int>(sizeof(E));  // 16 bytes of row padding
     static constexpr int LDK = DK + PAD;
     static constexpr int LDC = C + PAD;
     static constexpr int LDV = BV + PAD;
     static constexpr int LDT = 16 + PAD;
-    static constexpr int RG = 4;            // rows per prefix-sum group (fixed for every NW)
-    static constexpr int NG = C / RG;       // prefix-sum groups per chunk
-    static constexpr int QPR = DK / 4;      // channel quads per row
-    static constexpr int NITEMS = NG * QPR;
+    static constexpr int LDD = 20;  // fp32 diagonal blocks: 16-byte aligned rows
     static constexpr size_t ES = sizeof(E);
-    static constexpr size_t OFF_KB = 0;                                   // beta K~   [C][LDK]
-    static constexpr size_t OFF_KH = align16(OFF_KB + C * LDK * ES);       // K^        [C][LDK]
-    static constexpr size_t OFF_Q = align16(OFF_KH + C * LDK * ES);        // Q~        [C][LDK]
-    static constexpr size_t OFF_KBT = align16(OFF_Q + C * LDK * ES);       // Kbar^T    [DK][LDC]
-    static constexpr size_t OFF_V = align16(OFF_KBT + DK * LDC * ES);      // V, then O [C][LDV]
-    static constexpr size_t OFF_L = align16(OFF_V + C * LDV * ES);         // L         [C][LDC]
-    static constexpr size_t OFF_A = align16(OFF_L + C * LDC * ES);         // A_qk      [C][LDC]
-    static constexpr size_t OFF_T = align16(OFF_A + C * LDC * ES);         // -T_bb     [NB][16][LDT]
-    static constexpr size_t OFF_LD = align16(OFF_T + NB * 16 * LDT * ES);  // L_bb fp32 [NB][16][17]
-    static constexpr size_t OFF_BETA = align16(OFF_LD + NB * 16 * 17 * 4);  // beta     [C]
-    static constexpr size_t OFF_GC = align16(OFF_BETA + C * 4);            // Gamma_C   [DK]
-    static constexpr size_t OFF_TOT = align16(OFF_GC + DK * 4);            // group sums [NG][DK]
-    static constexpr size_t OFF_SEQ = align16(OFF_TOT + NG * DK * 4);      // lengths [kSortMax] + pick
+    // double-buffered tiles
+    static constexpr size_t SZ_KB = align16(C * LDK * ES);      // beta K~, Q~  [C][LDK]
+    static constexpr size_t SZ_KBT = align16(DK * LDC * ES);    // Kbar^T       [DK][LDC]
+    static constexpr size_t SZ_L = align16(C * LDC * ES);       // L, A_qk      [C][LDC]
+    static constexpr size_t SZ_T = align16(NB * 16 * LDT * ES);  // -T_bb       [NB][16][LDT]
+    static constexpr size_t SZ_VT = align16(BV * LDC * ES);     // V^T          [BV][LDC]
+    static constexpr size_t SZ_GC = align16(DK * 4);            // Gamma_C      [DK]
+    static constexpr size_t SZ_BETA = align16(C * 4);           // beta         [C]
+    static constexpr size_t OFF_KB = 0;
+    static constexpr size_t OFF_Q = OFF_KB + 2 * SZ_KB;
+    static constexpr size_t OFF_KBT = OFF_Q + 2 * SZ_KB;
+    static constexpr size_t OFF_L = OFF_KBT + 2 * SZ_KBT;
+    static constexpr size_t OFF_A = OFF_L + 2 * SZ_L;
+    static constexpr size_t OFF_T = OFF_A + 2 * SZ_L;
+    static constexpr size_t OFF_VT = OFF_T + 2 * SZ_T;
+    static constexpr size_t OFF_GC = OFF_VT + 2 * SZ_VT;
+    static constexpr size_t OFF_BETA = OFF_GC + 2 * SZ_GC;
+    // single-buffered
+    static constexpr size_t OFF_KH = OFF_BETA + 2 * SZ_BETA;                 // K^ [C][LDK]
+    static constexpr size_t OFF_O = OFF_KH + align16(C * LDK * ES);          // O  [C][LDV]
+    static constexpr size_t OFF_LD = OFF_O + align16(C * LDV * ES);          // L_bb^T fp32 [NB][16][LDD]
+    static constexpr size_t OFF_TOT = OFF_LD + align16(NB * 16 * LDD * 4);   // group sums [C/4][DK]
+    static constexpr size_t OFF_SEQ = OFF_TOT + align16((C / 4) * DK * 4);
     static constexpr size_t BYTES = align16(OFF_SEQ + (kSortMax + 1) * 4);
-    static_assert(BYTES <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+};
+
+template <bool BF16, int DK, int NW, int CT>
+using ChosenLayout =
+    Layout<BF16, DK, NW, CT, (Layout<BF16, DK, NW, CT, 32>::BYTES <= kLdsBudget ? 32 : 16)>;
+
+template <bool BF16, int DK, int NW, int CT>
+struct PrefillShape : ChosenLayout<BF16, DK, NW, CT> {
+    using Base = ChosenLayout<BF16, DK, NW, CT>;
+    static_assert(Base::BYTES <= kLdsBudget, "LDS budget of one gfx950 workgroup");
+    static constexpr int RG = 4;                // rows per prefix-sum group (fixed)
+    static constexpr int NG = Base::C / RG;     // prefix-sum groups per chunk
+    static constexpr int QPR = DK / 4;          // channel quads per row
+    static constexpr int NITEMS = NG * QPR;     // (group, channel quad) items
+    static constexpr int IPT = (NITEMS + Base::NT - 1) / Base::NT;
+    static constexpr int VITEMS = (Base::C / 4) * (Base::BV / 4);  // 4x4 blocks of V
+    static constexpr int VPT = (VITEMS + Base::NT - 1) / Base::NT;
 };
 
 template <bool BF16>
@@ -92,35 +127,79 @@ __device__ __forceinline__ void lds_store4(typename Elem<BF16>::E* p, float a, f
     }
 }
 
+// 4 consecutive operand elements from LDS, widened to fp32
+template <bool BF16>
+__device__ __forceinline__ f32x4_t lds_load4(const typename Elem<BF16>::E* p) {
+    if constexpr (BF16) {
+        const bf16x4_t r = *reinterpret_cast<const bf16x4_t*>(p);
+        return f32x4_t{static_cast<float>(r[0]), static_cast<float>(r[1]), static_cast<float>(r[2]),
+                       static_cast<float>(r[3])};
+    } else {
+        return *reinterpret_cast<const f32x4_t*>(p);
+    }
+}
+
+// Transposes a 4x4 block given as four raw row quads into four column quads.
+template <bool BF16>
+__device__ __forceinline__ void transpose4(const typename Elem<BF16>::R4 (&rows)[4],
+                                           typename Elem<BF16>::R4 (&cols)[4]) {
+    if constexpr (BF16) {
+        // rows[r] = {x: c0 | c1 << 16, y: c2 | c3 << 16}
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int sh = (c & 1) ? 16 : 0;
+            uint32_t e[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e[r] = (((c < 2) ? rows[r].x : rows[r].y) >> sh) & 0xFFFFu;
+            cols[c].x = e[0] | (e[1] << 16);
+            cols[c].y = e[2] | (e[3] << 16);
+        }
+    } else {
+        cols[0] = make_float4(rows[0].x, rows[1].x, rows[2].x, rows[3].x);
+        cols[1] = make_float4(rows[0].y, rows[1].y, rows[2].y, rows[3].y);
+        cols[2] = make_float4(rows[0].z, rows[1].z, rows[2].z, rows[3].z);
+        cols[3] = make_float4(rows[0].w, rows[1].w, rows[2].w, rows[3].w);
+    }
+}
+
 }  // namespace
 
-template <bool BF16, int DK, int NW>
+template <bool BF16, int DK, int NW, int CT>
 __global__ __launch_bounds__(64 * NW) void prefill_kernel(
     const typename Elem<BF16>::G* __restrict__ q, const typename Elem<BF16>::G* __restrict__ k,
     const typename Elem<BF16>::G* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, const float* __restrict__ S0, const int32_t* __restrict__ cu,
     int N, int H, int dv, int v_split, typename Elem<BF16>::G* __restrict__ o,
     float* __restrict__ S_T) {
-    using Sh = PrefillShape<BF16, DK, NW>;
+    using Sh = PrefillShape<BF16, DK, NW, CT>;
     using T = Elem<BF16>;
     using E = typename T::E;
     using G = typename T::G;
+    using R4 = typename T::R4;
+    using F8 = typename T::F8;
+    using F4 = typename T::F4;
     constexpr int C = Sh::C, NB = Sh::NB, NT = Sh::NT, BV = Sh::BV;
-    constexpr int LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV, LDT = Sh::LDT;
+    constexpr int LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV, LDT = Sh::LDT, LDD = Sh::LDD;
     constexpr int KB = DK / 32;  // 32-deep k blocks over key channels
+    constexpr int RG = Sh::RG, NG = Sh::NG, QPR = Sh::QPR, IPT = Sh::IPT, NITEMS = Sh::NITEMS;
+    constexpr int VPT = Sh::VPT, VITEMS = Sh::VITEMS;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Sh::BYTES];
-    E* const tKb = reinterpret_cast<E*>(smem + Sh::OFF_KB);
+#define KDA_TILE(name, type, off, sz) \
+    auto name = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<type*>(smem + (off) + b * (sz)); }
+    KDA_TILE(tKb, E, Sh::OFF_KB, Sh::SZ_KB);
+    KDA_TILE(tQ, E, Sh::OFF_Q, Sh::SZ_KB);
+    KDA_TILE(tKbT, E, Sh::OFF_KBT, Sh::SZ_KBT);
+    KDA_TILE(tL, E, Sh::OFF_L, Sh::SZ_L);
+    KDA_TILE(tA, E, Sh::OFF_A, Sh::SZ_L);
+    KDA_TILE(tT, E, Sh::OFF_T, Sh::SZ_T);
+    KDA_TILE(tVt, E, Sh::OFF_VT, Sh::SZ_VT);
+    KDA_TILE(sGC, float, Sh::OFF_GC, Sh::SZ_GC);
+    KDA_TILE(sBeta, float, Sh::OFF_BETA, Sh::SZ_BETA);
+#undef KDA_TILE
     E* const tKh = reinterpret_cast<E*>(smem + Sh::OFF_KH);
-    E* const tQ = reinterpret_cast<E*>(smem + Sh::OFF_Q);
-    E* const tKbT = reinterpret_cast<E*>(smem + Sh::OFF_KBT);
-    E* const tV = reinterpret_cast<E*>(smem + Sh::OFF_V);
-    E* const tL = reinterpret_cast<E*>(smem + Sh::OFF_L);
-    E* const tA = reinterpret_cast<E*>(smem + Sh::OFF_A);
-    E* const tT = reinterpret_cast<E*>(smem + Sh::OFF_T);
+    E* const tO = reinterpret_cast<E*>(smem + Sh::OFF_O);
     float* const fLd = reinterpret_cast<float*>(smem + Sh::OFF_LD);
-    float* const sBeta = reinterpret_cast<float*>(smem + Sh::OFF_BETA);
-    float* const sGC = reinterpret_cast<float*>(smem + Sh::OFF_GC);
     float* const sTot = reinterpret_cast<float*>(smem + Sh::OFF_TOT);
     int* const sSeq = reinterpret_cast<int*>(smem + Sh::OFF_SEQ);
 
@@ -168,283 +247,464 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(
     }
     const int t_beg = cu[n];
     const int t_end = cu[n + 1];
+    const int nchunks = (t_end - t_beg + C - 1) / C;
     const int j0 = slice * BV;  // first value column of this workgroup
-    const int jw = 16 * wave;   // this wave's first column inside the slice
     const size_t pair = static_cast<size_t>(n) * H + h;
+
+    // Per-head base pointers; per-token offsets below fit in 32 bits (the
+    // host rejects tensors of 2^31 elements or more).
+    const int strideK = H * DK;
+    const int strideV = H * dv;
+    const G* const qh = q + static_cast<size_t>(h) * DK;
+    const G* const kh = k + static_cast<size_t>(h) * DK;
+    const float* const lah = log_alpha + static_cast<size_t>(h) * DK;
+    const float* const bh = beta + h;
+    const G* const vh = v + static_cast<size_t>(h) * dv + j0;
+    G* const oh = o + static_cast<size_t>(h) * dv + j0;
 
     // Upper block-triangles of L and A_qk stay zero for the whole kernel.
     for (int idx = tid; idx < C * LDC; idx += NT) {
-        tL[idx] = T::to_e(0.f);
-        tA[idx] = T::to_e(0.f);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            tL(b)[idx] = T::to_e(0.f);
+            tA(b)[idx] = T::to_e(0.f);
+        }
     }
 
-    // ---- state slice in registers: Sr[it][j] = S[16 it + 4 lg + j][j0 + jw + ln]
-    f32x4_t Sr[DK / 16];
-    {
-        const size_t col = static_cast<size_t>(j0 + jw + ln);
+    // ---- state slice in registers: Sr[ct][it][j] = S[16 it + 4 lg + j][col]
+    auto col0 = [&](int ct) __attribute__((always_inline)) { return 16 * (CT * wave + ct); };
+    f32x4_t Sr[CT][DK / 16];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        const size_t col = static_cast<size_t>(j0 + col0(ct) + ln);
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const size_t row = static_cast<size_t>(16 * it + 4 * lg + j);
-                Sr[it][j] = S0 ? S0[(pair * DK + row) * dv + col] : 0.f;
-            }
+            for (int j = 0; j < 4; ++j)
+                Sr[ct][it][j] = S0 ? S0[(pair * DK + 16 * it + 4 * lg + j) * dv + col] : 0.f;
         }
     }
-    __syncthreads();
 
-    for (int c0 = t_beg; c0 < t_end; c0 += C) {
-        const int len = min(C, t_end - c0);
-
-        // ---- phase 1a: beta, V slice, per-group sums of log alpha --------
-        for (int r = tid; r < C; r += NT)
-            sBeta[r] = (r < len) ? beta[static_cast<size_t>(c0 + r) * H + h] : 0.f;
-        for (int idx = tid; idx < C * (BV / 4); idx += NT) {
-            const int r = idx / (BV / 4);
-            const int cq = idx % (BV / 4);
-            float x[4] = {0.f, 0.f, 0.f, 0.f};
-            if (r < len) T::load4(v + (static_cast<size_t>(c0 + r) * H + h) * dv + j0 + 4 * cq, x);
-            lds_store4<BF16>(tV + r * LDV + 4 * cq, x[0], x[1], x[2], x[3]);
-        }
-        for (int it = tid; it < Sh::NITEMS; it += NT) {
-            const int grp = it / Sh::QPR;
-            const int i0 = 4 * (it % Sh::QPR);
-            float4 tot = make_float4(0.f, 0.f, 0.f, 0.f);
+    // ---- raw inputs of one chunk, in registers -----------------------------
+    // Every load is unconditional: rows past the end of the sequence read the
+    // last valid row (always in bounds) and are zeroed where they are used.
+    float4 rla[IPT][RG];
+    R4 rk[IPT][RG], rq[IPT][RG], rv[VPT][4];
+    float rb = 0.f;
+    auto load_chunk = [&](int c0, int len) __attribute__((always_inline)) {
+        const int last = len - 1;
 #pragma unroll
-            for (int rr = 0; rr < Sh::RG; ++rr) {
-                const int r = grp * Sh::RG + rr;
-                if (r < len) {
-                    const float4 a = *reinterpret_cast<const float4*>(
-                        log_alpha + (static_cast<size_t>(c0 + r) * H + h) * DK + i0);
-                    tot.x += a.x;
-                    tot.y += a.y;
-                    tot.z += a.z;
-                    tot.w += a.w;
+        for (int ii = 0; ii < IPT; ++ii) {
+            const int it = tid + NT * ii;
+            if (NITEMS % NT == 0 || it < NITEMS) {
+                const int grp = it / QPR;
+                const int i0 = 4 * (it % QPR);
+#pragma unroll
+                for (int rr = 0; rr < RG; ++rr) {
+                    const int off = (c0 + min(grp * RG + rr, last)) * strideK + i0;
+                    rla[ii][rr] = *reinterpret_cast<const float4*>(lah + off);
+                    rk[ii][rr] = T::raw4(kh + off);
+                    rq[ii][rr] = T::raw4(qh + off);
                 }
             }
-            *reinterpret_cast<float4*>(sTot + grp * DK + i0) = tot;
         }
-        __syncthreads();
-
-        // ---- phase 1b: cumulative decay and decayed operands -------------
-        for (int it = tid; it < Sh::NITEMS; it += NT) {
-            const int grp = it / Sh::QPR;
-            const int i0 = 4 * (it % Sh::QPR);
-            float g[4] = {0.f, 0.f, 0.f, 0.f};
-            float gc[4];
-            for (int p = 0; p < Sh::NG; ++p) {
-                if (p == grp) {
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) gc[c] = g[c];  // prefix before this group
-                }
-                const float4 s = *reinterpret_cast<const float4*>(sTot + p * DK + i0);
-                g[0] += s.x;
-                g[1] += s.y;
-                g[2] += s.z;
-                g[3] += s.w;
+        for (int vv = 0; vv < VPT; ++vv) {
+            const int idx = tid + NT * vv;
+            if (VITEMS % NT == 0 || idx < VITEMS) {
+                const int r0 = 4 * (idx / (BV / 4));
+                const int c4 = 4 * (idx % (BV / 4));
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    rv[vv][rr] = T::raw4(vh + (c0 + min(r0 + rr, last)) * strideV + c4);
             }
-            // now g = g_C (whole chunk), gc = prefix before the group: swap names
-            float Gc[4];
+        }
+        if (tid < C) rb = bh[(c0 + min(tid, last)) * H];
+    };
+
+    // ---- prep 1: beta, V^T, group sums of log alpha ------------------------
+    auto prep1 = [&](int B, int len) __attribute__((always_inline)) {
+        if (tid < C) sBeta(B)[tid] = (tid < len) ? rb : 0.f;
+#pragma unroll
+        for (int vv = 0; vv < VPT; ++vv) {
+            const int idx = tid + NT * vv;
+            if (VITEMS % NT == 0 || idx < VITEMS) {
+                const int r0 = 4 * (idx / (BV / 4));
+                const int c4 = 4 * (idx % (BV / 4));
+                R4 rows[4], cols[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) rows[rr] = (r0 + rr < len) ? rv[vv][rr] : R4{};
+                transpose4<BF16>(rows, cols);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) T::lds_put_raw4(tVt(B) + (c4 + c) * LDC + r0, cols[c]);
+            }
+        }
+#pragma unroll
+        for (int ii = 0; ii < IPT; ++ii) {
+            const int it = tid + NT * ii;
+            if (NITEMS % NT == 0 || it < NITEMS) {
+                const int grp = it / QPR;
+                const int i0 = 4 * (it % QPR);
+                float4 tot = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int rr = 0; rr < RG; ++rr) {
+                    const bool ok = grp * RG + rr < len;
+                    tot.x += ok ? rla[ii][rr].x : 0.f;
+                    tot.y += ok ? rla[ii][rr].y : 0.f;
+                    tot.z += ok ? rla[ii][rr].z : 0.f;
+                    tot.w += ok ? rla[ii][rr].w : 0.f;
+                }
+                *reinterpret_cast<float4*>(sTot + grp * DK + i0) = tot;
+            }
+        }
+    };
+
+    // ---- prep 2: cumulative decay and decayed operand tiles ----------------
+    auto prep2_item = [&](auto full, int ii, int B, int len) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full)::value;
+        const int it = tid + NT * ii;
+        const int grp = it / QPR;
+        const int i0 = 4 * (it % QPR);
+        // g = sum of the group sums before this group; g_C = sum of all of
+        // them; both in the same fixed order for every launch shape.
+        float g[4] = {0.f, 0.f, 0.f, 0.f}, gcs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < NG; ++p) {
+            const float4 sm = *reinterpret_cast<const float4*>(sTot + p * DK + i0);
+            const bool before = p < grp;
+            g[0] += before ? sm.x : 0.f;
+            g[1] += before ? sm.y : 0.f;
+            g[2] += before ? sm.z : 0.f;
+            g[3] += before ? sm.w : 0.f;
+            gcs[0] += sm.x;
+            gcs[1] += sm.y;
+            gcs[2] += sm.z;
+            gcs[3] += sm.w;
+        }
+        float Gc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) Gc[c] = __builtin_amdgcn_exp2f(gcs[c] * kLog2e);
+        if (grp == 0) *reinterpret_cast<float4*>(sGC(B) + i0) = make_float4(Gc[0], Gc[1], Gc[2], Gc[3]);
+        float kbar[RG][4];
+#pragma unroll
+        for (int rr = 0; rr < RG; ++rr) {
+            const int r = grp * RG + rr;
+            const bool ok = FULL || r < len;
+            float kk[4], qq[4];
+            T::unpack4(rk[ii][rr], kk);
+            T::unpack4(rq[ii][rr], qq);
+            const float4 a = rla[ii][rr];
+            g[0] += ok ? a.x : 0.f;
+            g[1] += ok ? a.y : 0.f;
+            g[2] += ok ? a.z : 0.f;
+            g[3] += ok ? a.w : 0.f;
+            const float b = sBeta(B)[r];
+            float gam[4], inv[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                Gc[c] = exp_e(g[c]);
-                g[c] = gc[c];
-            }
-            if (grp == 0) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) sGC[i0 + c] = Gc[c];
-            }
-            float kbar[Sh::RG][4];
-#pragma unroll
-            for (int rr = 0; rr < Sh::RG; ++rr) {
-                const int r = grp * Sh::RG + rr;
-                float kk[4] = {0.f, 0.f, 0.f, 0.f}, qq[4] = {0.f, 0.f, 0.f, 0.f};
-                if (r < len) {
-                    const size_t base = (static_cast<size_t>(c0 + r) * H + h) * DK + i0;
-                    const float4 a = *reinterpret_cast<const float4*>(log_alpha + base);
-                    g[0] += a.x;
-                    g[1] += a.y;
-                    g[2] += a.z;
-                    g[3] += a.w;
-                    T::load4(k + base, kk);
-                    T::load4(q + base, qq);
+                if (!FULL && !ok) {
+                    kk[c] = 0.f;
+                    qq[c] = 0.f;
                 }
-                const float b = sBeta[r];
-                float gam[4], inv[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    gam[c] = exp_e(g[c]);
-                    inv[c] = exp_e(-g[c]);
-                    kbar[rr][c] = kk[c] * (Gc[c] * inv[c]);
-                }
-                lds_store4<BF16>(tKb + r * LDK + i0, b * kk[0] * gam[0], b * kk[1] * gam[1],
-                                 b * kk[2] * gam[2], b * kk[3] * gam[3]);
-                lds_store4<BF16>(tKh + r * LDK + i0, kk[0] * inv[0], kk[1] * inv[1], kk[2] * inv[2],
-                                 kk[3] * inv[3]);
-                lds_store4<BF16>(tQ + r * LDK + i0, qq[0] * gam[0], qq[1] * gam[1], qq[2] * gam[2],
-                                 qq[3] * gam[3]);
+                // exp(+-g) as 2^(+-g log2 e): one v_exp_f32 each; |g| stays
+                // within the numerical contract, where results are normal.
+                const float gl = g[c] * kLog2e;
+                gam[c] = __builtin_amdgcn_exp2f(gl);
+                inv[c] = __builtin_amdgcn_exp2f(-gl);
+                kbar[rr][c] = kk[c] * (Gc[c] * inv[c]);
             }
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                lds_store4<BF16>(tKbT + (i0 + c) * LDC + grp * Sh::RG, kbar[0][c], kbar[1][c],
-                                 kbar[2][c], kbar[3][c]);
+            const float bk0 = b * kk[0], bk1 = b * kk[1], bk2 = b * kk[2], bk3 = b * kk[3];
+            lds_store4<BF16>(tKb(B) + r * LDK + i0, bk0 * gam[0], bk1 * gam[1], bk2 * gam[2], bk3 * gam[3]);
+            lds_store4<BF16>(tKh + r * LDK + i0, kk[0] * inv[0], kk[1] * inv[1], kk[2] * inv[2],
+                             kk[3] * inv[3]);
+            lds_store4<BF16>(tQ(B) + r * LDK + i0, qq[0] * gam[0], qq[1] * gam[1], qq[2] * gam[2],
+                             qq[3] * gam[3]);
         }
-        __syncthreads();
-
-        // ---- phase 2: Gram products L = strictly_lower(beta K~ K^T), A_qk ----
-        // Computed transposed, P[s][r] = K^_s . X_r, so that each lane's four
-        // C-layout values are four consecutive columns of row r.
-        {
-            constexpr int NTILE = NB * (NB + 1) / 2;
-            for (int job = wave; job < 2 * NTILE; job += NW) {
-                const bool isq = job >= NTILE;
-                const int tix = isq ? job - NTILE : job;
-                int rt = 0;
-                while ((rt + 1) * (rt + 2) / 2 <= tix) ++rt;
-                const int st = tix - rt * (rt + 1) / 2;
-                const E* Ab = tKh + 16 * st * LDK;
-                const E* Bb = (isq ? tQ : tKb) + 16 * rt * LDK;
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    acc = mma8<BF16>(acc, lds_frag8<BF16>(Ab + 32 * kb, LDK, lane),
-                                     lds_frag8<BF16>(Bb + 32 * kb, LDK, lane));
-                const int r = 16 * rt + ln;
-                float val[4];
+        for (int c = 0; c < 4; ++c)
+            lds_store4<BF16>(tKbT(B) + (i0 + c) * LDC + grp * RG, kbar[0][c], kbar[1][c], kbar[2][c],
+                             kbar[3][c]);
+    };
+    auto prep2 = [&](int B, int len) __attribute__((always_inline)) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int s = 16 * st + 4 * lg + j;
-                    val[j] = (isq ? (s <= r) : (s < r)) ? acc[j] : 0.f;
-                }
-                lds_store4<BF16>((isq ? tA : tL) + r * LDC + 16 * st + 4 * lg, val[0], val[1], val[2],
-                                 val[3]);
-                if (!isq && st == rt) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) fLd[(rt * 16 + ln) * 17 + 4 * lg + j] = val[j];
+        for (int ii = 0; ii < IPT; ++ii) {
+            if (NITEMS % NT == 0 || tid + NT * ii < NITEMS) {
+                if (len == C) {
+                    prep2_item(std::true_type{}, ii, B, len);
+                } else {
+                    prep2_item(std::false_type{}, ii, B, len);
                 }
             }
         }
-        __syncthreads();
+    };
 
-        // ---- phase 3: -T_bb = -(I + L_bb)^-1 by forward substitution ------
-        // Lane (block lg, column ln) solves (I + L_bb) x = e_ln in fp32.
-        if (wave == 0 && lg < NB) {
-            const float* Lb = fLd + lg * 16 * 17;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == ln) ? 1.f : 0.f;
-#pragma unroll
-                for (int s = 0; s < r; ++s) acc -= Lb[r * 17 + s] * x[s];
-                x[r] = acc;
+    // ---- prep 3: Gram products ---------------------------------------------
+    // Job (st, rt), st <= rt, computes the tiles at block (rt, st) of
+    // L = strictly_lower(beta K~ K^T) and A_qk = lower_incl(Q~ K^T), sharing
+    // the K^ operand.  They are computed transposed, P[s][r] = K^_s . X_r, so
+    // that each lane's four C-layout values are four consecutive columns of
+    // row r.  Diagonal L blocks are also kept in fp32 for the inverse.
+    auto prep3 = [&](int B) __attribute__((always_inline)) {
+        constexpr int NJOB = NB * (NB + 1) / 2;
+        for (int job = wave; job < NJOB; job += NW) {
+            int st, rt;
+            if (job < NB) {
+                st = rt = job;
+            } else {
+                int tix = job - NB;  // enumerate st < rt
+                rt = 1;
+                while (tix >= rt) {
+                    tix -= rt;
+                    ++rt;
+                }
+                st = tix;
             }
+            const E* Ab = tKh + 16 * st * LDK;
+            const E* Bk = tKb(B) + 16 * rt * LDK;
+            const E* Bq = tQ(B) + 16 * rt * LDK;
+            f32x4_t accL = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) tT[(lg * 16 + r) * LDT + ln] = T::to_e(-x[r]);
-        }
-        __syncthreads();
-
-        // ---- phase 4: per-wave column recurrence -------------------------
-        typename T::F8 sf[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) sf[kb] = acc_frag8<BF16>(Sr[2 * kb], Sr[2 * kb + 1]);
-
-        // R' = beta K~ S - beta V  (= -R)
-        f32x4_t Rp[NB];
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
+            for (int kb = 0; kb < KB; ++kb) {
+                const F8 a = lds_frag8<BF16>(Ab + 32 * kb, LDK, lane);
+                accL = mma8<BF16>(accL, a, lds_frag8<BF16>(Bk + 32 * kb, LDK, lane));
+                accA = mma8<BF16>(accA, a, lds_frag8<BF16>(Bq + 32 * kb, LDK, lane));
+            }
+            const int r = 16 * rt + ln;
+            float vl[4], va[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 16 * rt + 4 * lg + j;
-                Rp[rt][j] = -sBeta[r] * T::e_to_f32(tV[r * LDV + jw + ln]);
+                const int s = 16 * st + 4 * lg + j;
+                vl[j] = (s < r) ? accL[j] : 0.f;
+                va[j] = (s <= r) ? accA[j] : 0.f;
             }
+            lds_store4<BF16>(tL(B) + r * LDC + 16 * st + 4 * lg, vl[0], vl[1], vl[2], vl[3]);
+            lds_store4<BF16>(tA(B) + r * LDC + 16 * st + 4 * lg, va[0], va[1], va[2], va[3]);
+            if (st == rt) {
+                // fLd[b][s][r] = L_bb[r][s]
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                Rp[rt] = mma8<BF16>(Rp[rt], lds_frag8<BF16>(tKb + 16 * rt * LDK + 32 * kb, LDK, lane),
-                                    sf[kb]);
+                for (int j = 0; j < 4; ++j) fLd[(rt * 16 + 4 * lg + j) * LDD + ln] = vl[j];
+            }
         }
-        // U_b = (-T_bb) (R'_b + sum_{c<b} L_bc U_c)
-        f32x4_t U[NB];
+    };
+
+    // ---- prep 4: -T_bb = -(I + L_bb)^-1 by forward substitution -------------
+    // One wave; lane (block lg, column ln) solves (I + L_bb) x = e_ln in fp32,
+    // right-looking: once x_s is final, every later row r subtracts
+    // L[r][s] x_s (the operations and order of row-by-row solving).
+    constexpr int INV_WAVE = NW - 1;
+    auto prep4 = [&](int B) __attribute__((always_inline)) {
+        if (wave == INV_WAVE) {
+            const int bb = lg < NB ? lg : 0;  // spare lane groups repeat block 0
+            const float* Lb = fLd + bb * 16 * LDD;
+            float x[16];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            f32x4_t Y = Rp[b];
+            for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
 #pragma unroll
-            for (int kp = 0; kp + 1 < b; kp += 2)
-                Y = mma8<BF16>(Y, lds_frag8<BF16>(tL + 16 * b * LDC + 16 * kp, LDC, lane),
-                               acc_frag8<BF16>(U[kp], U[kp + 1]));
-            if (b & 1)
-                Y = mma4<BF16>(Y, lds_frag4<BF16>(tL + 16 * b * LDC + 16 * (b - 1), LDC, lane),
-                               acc_frag4<BF16>(U[b - 1]));
-            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            U[b] = mma4<BF16>(z, lds_frag4<BF16>(tT + 16 * b * LDT, LDT, lane), acc_frag4<BF16>(Y));
+            for (int s = 0; s < 15; ++s) {
+                float col[16];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 c4 = *reinterpret_cast<const float4*>(Lb + s * LDD + 4 * q4);
+                    col[4 * q4] = c4.x;
+                    col[4 * q4 + 1] = c4.y;
+                    col[4 * q4 + 2] = c4.z;
+                    col[4 * q4 + 3] = c4.w;
+                }
+#pragma unroll
+                for (int r = s + 1; r < 16; ++r) x[r] -= col[r] * x[s];
+            }
+            if (lg < NB) {
+                E* dst = tT(B) + lg * 16 * LDT + ln;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dst[r * LDT] = T::to_e(-x[r]);
+            }
         }
-        // O^T = S^T Q~^T + U^T A_qk^T, tile by tile over token blocks; the
-        // wave overwrites its own V columns with O (V is no longer needed).
+    };
+
+    // ---- chain: per-wave column recurrence of the chunk in buffer B ---------
+    F8 sf[CT][KB];
+    f32x4_t Rp[CT][NB], U[CT][NB];
+    F4 uf[CT][NB];
+
+    // R' = beta K~ S - beta V  (= -R)
+    auto chain_R = [&](int B) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sf[ct][kb] = acc_frag8<BF16>(Sr[ct][2 * kb], Sr[ct][2 * kb + 1]);
+        }
 #pragma unroll
         for (int rt = 0; rt < NB; ++rt) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            const float4 b4 = *reinterpret_cast<const float4*>(sBeta(B) + 16 * rt + 4 * lg);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                acc = mma8<BF16>(acc, sf[kb], lds_frag8<BF16>(tQ + 16 * rt * LDK + 32 * kb, LDK, lane));
+            for (int ct = 0; ct < CT; ++ct) {
+                const f32x4_t v4 = lds_load4<BF16>(tVt(B) + (col0(ct) + ln) * LDC + 16 * rt + 4 * lg);
+                Rp[ct][rt] = f32x4_t{-b4.x * v4[0], -b4.y * v4[1], -b4.z * v4[2], -b4.w * v4[3]};
+            }
 #pragma unroll
-            for (int sp = 0; sp + 1 <= rt; sp += 2)
-                acc = mma8<BF16>(acc, acc_frag8<BF16>(U[sp], U[sp + 1]),
-                                 lds_frag8<BF16>(tA + 16 * rt * LDC + 16 * sp, LDC, lane));
-            if (!(rt & 1))
-                acc = mma4<BF16>(acc, acc_frag4<BF16>(U[rt]),
-                                 lds_frag4<BF16>(tA + 16 * rt * LDC + 16 * rt, LDC, lane));
-            lds_store4<BF16>(tV + (16 * rt + ln) * LDV + jw + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
+            for (int kb = 0; kb < KB; ++kb) {
+                const F8 a = lds_frag8<BF16>(tKb(B) + 16 * rt * LDK + 32 * kb, LDK, lane);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) Rp[ct][rt] = mma8<BF16>(Rp[ct][rt], a, sf[ct][kb]);
+            }
         }
-        // S <- Diag(Gamma_C) S + Kbar^T U
+    };
+    auto u_frag8 = [&](int ct, int b) __attribute__((always_inline)) {
+        return F8(__builtin_shufflevector(uf[ct][b], uf[ct][b + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // U_b = (-T_bb) (R'_b + sum_{c<b} L_bc U_c);  then O^T = S^T Q~^T + U^T A_qk^T
+    auto chain_UO = [&](int B) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            f32x4_t Y[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) Y[ct] = Rp[ct][b];
+#pragma unroll
+            for (int kp = 0; kp + 1 < b; kp += 2) {
+                const F8 a = lds_frag8<BF16>(tL(B) + 16 * b * LDC + 16 * kp, LDC, lane);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) Y[ct] = mma8<BF16>(Y[ct], a, u_frag8(ct, kp));
+            }
+            if (b & 1) {
+                const F4 a = lds_frag4<BF16>(tL(B) + 16 * b * LDC + 16 * (b - 1), LDC, lane);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) Y[ct] = mma4<BF16>(Y[ct], a, uf[ct][b - 1]);
+            }
+            const F4 tb = lds_frag4<BF16>(tT(B) + 16 * b * LDT, LDT, lane);
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                U[ct][b] = mma4<BF16>(z, tb, acc_frag4<BF16>(Y[ct]));
+                uf[ct][b] = acc_frag4<BF16>(U[ct][b]);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+            f32x4_t acc[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const F8 bq = lds_frag8<BF16>(tQ(B) + 16 * rt * LDK + 32 * kb, LDK, lane);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], sf[ct][kb], bq);
+            }
+#pragma unroll
+            for (int sp = 0; sp + 1 <= rt; sp += 2) {
+                const F8 ba = lds_frag8<BF16>(tA(B) + 16 * rt * LDC + 16 * sp, LDC, lane);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], u_frag8(ct, sp), ba);
+            }
+            if (!(rt & 1)) {
+                const F4 ba = lds_frag4<BF16>(tA(B) + 16 * rt * LDC + 16 * rt, LDC, lane);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) acc[ct] = mma4<BF16>(acc[ct], uf[ct][rt], ba);
+            }
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                lds_store4<BF16>(tO + (16 * rt + ln) * LDV + col0(ct) + 4 * lg, acc[ct][0], acc[ct][1],
+                                 acc[ct][2], acc[ct][3]);
+        }
+    };
+    // S <- Diag(Gamma_C) S + Kbar^T U
+    auto chain_S = [&](int B) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it) {
-            f32x4_t acc;
+            const float4 g4 = *reinterpret_cast<const float4*>(sGC(B) + 16 * it + 4 * lg);
+            f32x4_t acc[CT];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = Sr[it][j] * sGC[16 * it + 4 * lg + j];
+            for (int ct = 0; ct < CT; ++ct)
+                acc[ct] = f32x4_t{Sr[ct][it][0] * g4.x, Sr[ct][it][1] * g4.y, Sr[ct][it][2] * g4.z,
+                                  Sr[ct][it][3] * g4.w};
 #pragma unroll
-            for (int kb = 0; kb < C / 32; ++kb)
-                acc = mma8<BF16>(acc, lds_frag8<BF16>(tKbT + 16 * it * LDC + 32 * kb, LDC, lane),
-                                 acc_frag8<BF16>(U[2 * kb], U[2 * kb + 1]));
-            Sr[it] = acc;
+            for (int kb = 0; kb < NB / 2; ++kb) {
+                const F8 a = lds_frag8<BF16>(tKbT(B) + 16 * it * LDC + 32 * kb, LDC, lane);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], a, u_frag8(ct, 2 * kb));
+            }
+            if constexpr (NB & 1) {
+                const F4 a = lds_frag4<BF16>(tKbT(B) + 16 * it * LDC + 16 * (NB - 1), LDC, lane);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) acc[ct] = mma4<BF16>(acc[ct], a, uf[ct][NB - 1]);
+            }
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) Sr[ct][it] = acc[ct];
         }
-        __syncthreads();
-
-        // ---- phase 5: coalesced store of the chunk's outputs --------------
+    };
+    // coalesced store of the chunk's outputs
+    auto store_O = [&](int c0, int len) __attribute__((always_inline)) {
         for (int idx = tid; idx < len * (BV / 4); idx += NT) {
             const int r = idx / (BV / 4);
             const int cq = idx % (BV / 4);
-            G* dst = o + (static_cast<size_t>(c0 + r) * H + h) * dv + j0 + 4 * cq;
+            G* dst = oh + (c0 + r) * strideV + 4 * cq;
             if constexpr (BF16) {
-                *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(tV + r * LDV + 4 * cq);
+                *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(tO + r * LDV + 4 * cq);
             } else {
-                *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(tV + r * LDV + 4 * cq);
+                *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(tO + r * LDV + 4 * cq);
             }
         }
+    };
+    auto chunk_len = [&](int i) __attribute__((always_inline)) { return min(C, t_end - (t_beg + i * C)); };
+
+    // ---- prologue: prep 1-3 of chunk 0 ---------------------------------------
+    __syncthreads();  // zeroed L / A_qk tiles
+    if (nchunks > 0) {
+        load_chunk(t_beg, chunk_len(0));
+        prep1(0, chunk_len(0));
+        __syncthreads();
+        prep2(0, chunk_len(0));
+        if (nchunks > 1) load_chunk(t_beg + C, chunk_len(1));
+        __syncthreads();
+        prep3(0);
+        __syncthreads();
+    }
+
+    // ---- steady state: chunk i in buffer i & 1, prep of chunk i+1 in the other
+    for (int i = 0; i < nchunks; ++i) {
+        const int B = i & 1;
+        const bool has_next = i + 1 < nchunks;
+        const int len1 = has_next ? chunk_len(i + 1) : 0;
+        // stage X
+        prep4(B);
+        if (has_next) prep1(1 - B, len1);
+        chain_R(B);
+        __syncthreads();
+        // stage Y
+        if (has_next) {
+            prep2(1 - B, len1);
+            if (i + 2 < nchunks) load_chunk(t_beg + (i + 2) * C, chunk_len(i + 2));
+        }
+        chain_UO(B);
+        __syncthreads();
+        // stage Z
+        if (has_next) prep3(1 - B);
+        chain_S(B);
+        store_O(t_beg + i * C, chunk_len(i));
         __syncthreads();
     }
 
     // ---- final state --------------------------------------------------------
-    {
-        const size_t col = static_cast<size_t>(j0 + jw + ln);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        const size_t col = static_cast<size_t>(j0 + col0(ct) + ln);
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const size_t row = static_cast<size_t>(16 * it + 4 * lg + j);
-                S_T[(pair * DK + row) * dv + col] = Sr[it][j];
-            }
+            for (int j = 0; j < 4; ++j) S_T[(pair * DK + 16 * it + 4 * lg + j) * dv + col] = Sr[ct][it][j];
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Host launchers
+// Host launchers.  The workgroup shape follows the value slice width
+// BV = d_v / v_split: 4 waves x 2 tiles (128), 4 x 1 (64), 2 x 1 (32), 1 x 1 (16).
 // ---------------------------------------------------------------------------
-template <bool BF16, int DK, int NW>
+template <bool BF16, int DK, int NW, int CT>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
     using G = typename Elem<BF16>::G;
     const unsigned grid = static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H) *
                           static_cast<unsigned>(a.v_split);
-    hipLaunchKernelGGL((prefill_kernel<BF16, DK, NW>), dim3(grid), dim3(64 * NW), 0,
+    hipLaunchKernelGGL((prefill_kernel<BF16, DK, NW, CT>), dim3(grid), dim3(64 * NW), 0,
                        static_cast<hipStream_t>(a.stream), static_cast<const G*>(a.q),
                        static_cast<const G*>(a.k), static_cast<const G*>(a.v), a.log_alpha, a.beta,
                        a.S0, a.cu_seqlens, a.N, a.H, a.d_v, a.v_split, static_cast<G*>(a.o), a.S_T);
@@ -453,11 +713,11 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
 
 template <bool BF16, int DK>
 static hipError_t launch_prefill_dk(const PrefillArgs& a) {
-    switch (a.d_v / (16 * a.v_split)) {
-        case 1: return launch_prefill_t<BF16, DK, 1>(a);
-        case 2: return launch_prefill_t<BF16, DK, 2>(a);
-        case 4: return launch_prefill_t<BF16, DK, 4>(a);
-        case 8: return launch_prefill_t<BF16, DK, 8>(a);
+    switch (a.d_v / a.v_split) {
+        case 128: return launch_prefill_t<BF16, DK, 4, 2>(a);
+        case 64: return launch_prefill_t<BF16, DK, 4, 1>(a);
+        case 32: return launch_prefill_t<BF16, DK, 2, 1>(a);
+        case 16: return launch_prefill_t<BF16, DK, 1, 1>(a);
         default: return hipErrorInvalidValue;
     }
 }
@@ -483,7 +743,7 @@ int32_t default_v_split(int32_t N, int32_t H, int32_t d_k, int32_t d_v, bool bf1
     int32_t split = 1;
     // Aim for at least ~192 workgroups on the 256 CUs; every split shares the
     // same per-column arithmetic, so this only changes the launch shape.
-    while (units * split < 192 && split < 8 && d_v / (16 * split * 2) >= 1) split *= 2;
+    while (units * split < 192 && split < 8 && d_v / (split * 2) >= 16) split *= 2;
     return split;
 }
 
