@@ -51,6 +51,32 @@ def decode_bytes(N: int, H: int, dk: int, dv: int, esize: int) -> int:
     return (8 * dk * dv + esize * (2 * dk + dv) + 4 * dk + 4 + esize * dv) * N * H
 
 
+_CSRC = os.path.join(_ROOT, "gated_delta_rule_60_amd", "csrc")
+_PROFILES = os.path.join(_ROOT, "profiles")
+
+
+def measured_traffic(kernel: str, workload: str, sources):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary of this kernel and workload, or None when the kernel sources have
+    changed since those counters were taken (or no summary exists)."""
+    import hashlib
+    import re
+
+    path = os.path.join(_PROFILES, f"{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_bytes = re.search(r"traffic bytes per launch: (\d+)", text)
+    m_hash = re.search(r"kernel source sha256 \([^)]*\): ([0-9a-f]{64})", text)
+    if not (m_bytes and m_hash):
+        return None
+    h = hashlib.sha256()
+    for s in sources:
+        with open(os.path.join(_CSRC, s), "rb") as f:
+            h.update(f.read())
+    return int(m_bytes.group(1)) if h.hexdigest() == m_hash.group(1) else None
+
+
 def cpu_baseline(x, seconds: float):
     """Time the fp64 oracle on the benchmark workload, a batch of heads at a
     time (all sequences of each head), until ``seconds`` of wall time have
@@ -231,7 +257,9 @@ def main():
                    "d_k": x.d_k, "d_v": x.d_v, "chunk": CHUNK, "v_split": split,
                    "lengths": [int(b - a) for a, b in zip(x.cu_seqlens[:-1], x.cu_seqlens[1:])]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("prefill_kernel", args.workload,
+                                                 ["kda_prefill.hip", "kda_device.hpp"]),
                      "kernel": "kda::prefill_kernel", "kernel_ms_avg": k_avg_ms,
                      "kernel_ms_min": min(kms), "alg_bytes_per_launch": nbytes},
         "mfma": {"alg_flops_per_launch": nflops,
@@ -251,6 +279,8 @@ def main():
             "roofline": {"bound": "hbm", "achieved": db / (mean_us * 1e-6) / 1e9,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": db / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("decode_step_kernel", "decode_n256_h32_d128_bf16",
+                                                     ["kda_decode.hip", "kda_device.hpp"]),
                          "kernel": "kda::decode_step_kernel", "alg_bytes_per_launch": db},
         }
     if not args.no_cpu_baseline:
