@@ -18,8 +18,9 @@
 //     O      = Q~ S + A_qk U
 //     S_next = Diag(Gamma_C) S + Kbar^T U
 // (I + L) is unit lower triangular.  Its 16x16 diagonal blocks are inverted
-// by forward substitution in fp32 (T_bb = (I + L_bb)^-1); U is obtained block
-// by block, U_b = T_bb (R_b - sum_{c<b} L_bc U_c), with MFMA products.
+// with MFMA products, T_bb = (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8)
+// for the nilpotent N = L_bb; U is obtained block by block,
+// U_b = T_bb (R_b - sum_{c<b} L_bc U_c), with MFMA products.
 // Padded tail rows (past the end of a sequence) carry k = q = v = beta =
 // log alpha = 0 and therefore contribute nothing.
 //
@@ -33,11 +34,11 @@
 // one chunk ahead of the S-dependent recurrence ("chain"), in the same
 // barrier stages, from double-buffered LDS tiles, so that prep's VALU and
 // LDS work overlaps the chain's MFMA work.  For chunk i:
-//     stage X: block inverse of i (one wave)  | prep 1 of i+1: beta, V^T, sums
-//              of log alpha                    | chain of i: R'
+//     stage X: prep 1 of i+1: beta, V^T, sums of log alpha | chain of i: R'
 //     stage Y: prep 2 of i+1: cumulative decay, decayed tiles; loads of i+2
-//                                              | chain of i: U, O
-//     stage Z: prep 3 of i+1: Gram products    | chain of i: S update, O store
+//                                                          | chain of i: U, O
+//     stage Z: prep 3 of i+1: Gram products, block inverse | chain of i: S update,
+//                                                            O store
 // All MFMA operands are bf16 (or fp32 for f32 inputs); accumulation and the
 // carried state are fp32.
 #include <type_traits>
@@ -68,7 +69,6 @@ struct Layout {
     static constexpr int LDC = C + PAD;
     static constexpr int LDV = BV + PAD;
     static constexpr int LDT = 16 + PAD;
-    static constexpr int LDD = 20;  // fp32 diagonal blocks: 16-byte aligned rows
     static constexpr size_t ES = sizeof(E);
     // double-buffered tiles
     static constexpr size_t SZ_KB = align16(C * LDK * ES);      // beta K~, Q~  [C][LDK]
@@ -90,8 +90,7 @@ struct Layout {
     // single-buffered
     static constexpr size_t OFF_KH = OFF_BETA + 2 * SZ_BETA;                 // K^ [C][LDK]
     static constexpr size_t OFF_O = OFF_KH + align16(C * LDK * ES);          // O  [C][LDV]
-    static constexpr size_t OFF_LD = OFF_O + align16(C * LDV * ES);          // L_bb^T fp32 [NB][16][LDD]
-    static constexpr size_t OFF_TOT = OFF_LD + align16(NB * 16 * LDD * 4);   // group sums [C/4][DK]
+    static constexpr size_t OFF_TOT = OFF_O + align16(C * LDV * ES);         // group sums [C/4][DK]
     static constexpr size_t OFF_SEQ = OFF_TOT + align16((C / 4) * DK * 4);
     static constexpr size_t BYTES = align16(OFF_SEQ + (kSortMax + 1) * 4);
 };
@@ -179,7 +178,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(
     using F8 = typename T::F8;
     using F4 = typename T::F4;
     constexpr int C = Sh::C, NB = Sh::NB, NT = Sh::NT, BV = Sh::BV;
-    constexpr int LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV, LDT = Sh::LDT, LDD = Sh::LDD;
+    constexpr int LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV, LDT = Sh::LDT;
     constexpr int KB = DK / 32;  // 32-deep k blocks over key channels
     constexpr int RG = Sh::RG, NG = Sh::NG, QPR = Sh::QPR, IPT = Sh::IPT, NITEMS = Sh::NITEMS;
     constexpr int VPT = Sh::VPT, VITEMS = Sh::VITEMS;
@@ -199,7 +198,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(
 #undef KDA_TILE
     E* const tKh = reinterpret_cast<E*>(smem + Sh::OFF_KH);
     E* const tO = reinterpret_cast<E*>(smem + Sh::OFF_O);
-    float* const fLd = reinterpret_cast<float*>(smem + Sh::OFF_LD);
     float* const sTot = reinterpret_cast<float*>(smem + Sh::OFF_TOT);
     int* const sSeq = reinterpret_cast<int*>(smem + Sh::OFF_SEQ);
 
@@ -438,15 +436,22 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(
         }
     };
 
-    // ---- prep 3: Gram products ---------------------------------------------
+    // ---- prep 3: Gram products and block inverse ---------------------------
     // Job (st, rt), st <= rt, computes the tiles at block (rt, st) of
     // L = strictly_lower(beta K~ K^T) and A_qk = lower_incl(Q~ K^T), sharing
     // the K^ operand.  They are computed transposed, P[s][r] = K^_s . X_r, so
     // that each lane's four C-layout values are four consecutive columns of
-    // row r.  Diagonal L blocks are also kept in fp32 for the inverse.
+    // row r.
+    //
+    // A diagonal job also forms -T_bb = -(I + N)^-1, N = L_bb (strictly lower,
+    // nilpotent: N^16 = 0), as the product (I - N)(I + N^2)(I + N^4)(I + N^8),
+    // with MFMA.  The factors are polynomials in N and commute, so every
+    // product can take its A operand from a C-layout tile already held:
+    // the A operand of X is the C layout of X^T, the B operand of X is the C
+    // layout of X.  Both layouts of N come from the Gram MFMAs (P and P^T).
     auto prep3 = [&](int B) __attribute__((always_inline)) {
         constexpr int NJOB = NB * (NB + 1) / 2;
-        for (int job = wave; job < NJOB; job += NW) {
+        for (int job = NW - 1 - wave; job < NJOB; job += NW) {
             int st, rt;
             if (job < NB) {
                 st = rt = job;
@@ -459,64 +464,55 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(
                 }
                 st = tix;
             }
+            const bool diag = st == rt;
             const E* Ab = tKh + 16 * st * LDK;
             const E* Bk = tKb(B) + 16 * rt * LDK;
             const E* Bq = tQ(B) + 16 * rt * LDK;
-            f32x4_t accL = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
+            f32x4_t accL = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f}, accN = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const F8 a = lds_frag8<BF16>(Ab + 32 * kb, LDK, lane);
-                accL = mma8<BF16>(accL, a, lds_frag8<BF16>(Bk + 32 * kb, LDK, lane));
+                const F8 bk = lds_frag8<BF16>(Bk + 32 * kb, LDK, lane);
+                accL = mma8<BF16>(accL, a, bk);
                 accA = mma8<BF16>(accA, a, lds_frag8<BF16>(Bq + 32 * kb, LDK, lane));
+                if (diag) accN = mma8<BF16>(accN, bk, a);  // P^T: C layout of N
             }
             const int r = 16 * rt + ln;
             float vl[4], va[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int s = 16 * st + 4 * lg + j;
-                vl[j] = (s < r) ? accL[j] : 0.f;
-                va[j] = (s <= r) ? accA[j] : 0.f;
+                const int s2 = 16 * st + 4 * lg + j;
+                vl[j] = (s2 < r) ? accL[j] : 0.f;
+                va[j] = (s2 <= r) ? accA[j] : 0.f;
             }
             lds_store4<BF16>(tL(B) + r * LDC + 16 * st + 4 * lg, vl[0], vl[1], vl[2], vl[3]);
             lds_store4<BF16>(tA(B) + r * LDC + 16 * st + 4 * lg, va[0], va[1], va[2], va[3]);
-            if (st == rt) {
-                // fLd[b][s][r] = L_bb[r][s]
+            if (diag) {
+                // C layout: lane (ln, lg), value j is element (row 4 lg + j, col ln).
+                f32x4_t Nt, Nc;  // C layouts of N^T and N (strictly lower N)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) fLd[(rt * 16 + 4 * lg + j) * LDD + ln] = vl[j];
-            }
-        }
-    };
-
-    // ---- prep 4: -T_bb = -(I + L_bb)^-1 by forward substitution -------------
-    // One wave; lane (block lg, column ln) solves (I + L_bb) x = e_ln in fp32,
-    // right-looking: once x_s is final, every later row r subtracts
-    // L[r][s] x_s (the operations and order of row-by-row solving).
-    constexpr int INV_WAVE = NW - 1;
-    auto prep4 = [&](int B) __attribute__((always_inline)) {
-        if (wave == INV_WAVE) {
-            const int bb = lg < NB ? lg : 0;  // spare lane groups repeat block 0
-            const float* Lb = fLd + bb * 16 * LDD;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
-#pragma unroll
-            for (int s = 0; s < 15; ++s) {
-                float col[16];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const float4 c4 = *reinterpret_cast<const float4*>(Lb + s * LDD + 4 * q4);
-                    col[4 * q4] = c4.x;
-                    col[4 * q4 + 1] = c4.y;
-                    col[4 * q4 + 2] = c4.z;
-                    col[4 * q4 + 3] = c4.w;
+                for (int j = 0; j < 4; ++j) {
+                    Nt[j] = vl[j];
+                    Nc[j] = (ln < 4 * lg + j) ? accN[j] : 0.f;
                 }
+                auto eye = [&](f32x4_t x, float sgn) __attribute__((always_inline)) {
+                    f32x4_t y;
 #pragma unroll
-                for (int r = s + 1; r < 16; ++r) x[r] -= col[r] * x[s];
-            }
-            if (lg < NB) {
-                E* dst = tT(B) + lg * 16 * LDT + ln;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) dst[r * LDT] = T::to_e(-x[r]);
+                    for (int j = 0; j < 4; ++j) y[j] = sgn * x[j] + ((4 * lg + j == ln) ? 1.f : 0.f);
+                    return y;
+                };
+                const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+                const f32x4_t N2 = mma4<BF16>(z, acc_frag4<BF16>(Nt), acc_frag4<BF16>(Nc));
+                const f32x4_t N2t = mma4<BF16>(z, acc_frag4<BF16>(Nc), acc_frag4<BF16>(Nt));
+                const f32x4_t N4 = mma4<BF16>(z, acc_frag4<BF16>(N2t), acc_frag4<BF16>(N2));
+                const f32x4_t N4t = mma4<BF16>(z, acc_frag4<BF16>(N2), acc_frag4<BF16>(N2t));
+                const f32x4_t N8 = mma4<BF16>(z, acc_frag4<BF16>(N4t), acc_frag4<BF16>(N4));
+                // Q1 = (I + N8^T)(I + N4^T), Q2 = (I + N2^T) Q1, Q3 = (I - N^T) Q2 = T^T
+                const f32x4_t Q1 = mma4<BF16>(z, acc_frag4<BF16>(eye(N8, 1.f)), acc_frag4<BF16>(eye(N4t, 1.f)));
+                const f32x4_t Q2 = mma4<BF16>(z, acc_frag4<BF16>(eye(N2, 1.f)), acc_frag4<BF16>(Q1));
+                const f32x4_t Q3 = mma4<BF16>(z, acc_frag4<BF16>(eye(Nc, -1.f)), acc_frag4<BF16>(Q2));
+                // lane (ln, lg) holds T[ln][4 lg + j]: store -T row-major
+                lds_store4<BF16>(tT(B) + (rt * 16 + ln) * LDT + 4 * lg, -Q3[0], -Q3[1], -Q3[2], -Q3[3]);
             }
         }
     };
@@ -665,7 +661,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(
         const bool has_next = i + 1 < nchunks;
         const int len1 = has_next ? chunk_len(i + 1) : 0;
         // stage X
-        prep4(B);
         if (has_next) prep1(1 - B, len1);
         chain_R(B);
         __syncthreads();
