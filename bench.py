@@ -188,15 +188,26 @@ def bench_decode(kda, torch, steps: int, warmup: int, n_inputs: int):
 
 
 def calib_copy(torch, gib: float, reps: int):
-    """A plain device-to-device copy of known size, for scaling HBM counters."""
+    """A plain device-to-device copy of known size, for scaling HBM counters;
+    also reports the copy's own read+write bandwidth (the practical ceiling of
+    a streaming kernel that reads and writes the same number of bytes)."""
     n = int(gib * (1 << 30)) // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda:0")
     b = torch.empty_like(a)
-    for _ in range(reps):
-        b.copy_(a)
+    b.copy_(a)
     torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    best = min(ms)
     print(json.dumps({"calib_copy_bytes_read": 4 * n, "calib_copy_bytes_written": 4 * n,
-                      "reps": reps}), flush=True)
+                      "reps": reps, "copy_ms_min": best,
+                      "copy_GBps_read_plus_write": 8 * n / (best * 1e-3) / 1e9}), flush=True)
 
 
 def main():

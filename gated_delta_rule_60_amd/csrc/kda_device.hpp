@@ -76,11 +76,14 @@ struct Elem<true> {
         x[2] = __uint_as_float(r.y << 16);
         x[3] = __uint_as_float(r.y & 0xFFFF0000u);
     }
+    // round to nearest even (v_cvt_pk_bf16_f32)
     __device__ static __forceinline__ void store4(G* p, const float (&x)[4]) {
-        uint2 r;
-        r.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
-        r.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
-        *reinterpret_cast<uint2*>(p) = r;
+        bf16x4_t r;
+        r[0] = static_cast<__bf16>(x[0]);
+        r[1] = static_cast<__bf16>(x[1]);
+        r[2] = static_cast<__bf16>(x[2]);
+        r[3] = static_cast<__bf16>(x[3]);
+        *reinterpret_cast<bf16x4_t*>(p) = r;
     }
     __device__ static __forceinline__ float to_f32(G x) { return bf16_to_f32(x); }
     __device__ static __forceinline__ E to_e(float x) { return static_cast<__bf16>(x); }

@@ -11,7 +11,7 @@
 // Chunk algebra.  Inside a chunk of C tokens (rows r), with S the state
 // entering the chunk, g_r = sum_{j<=r} log alpha_j (per key channel),
 // Gamma_r = exp(g_r):
-//     K~ = K * Gamma,  K^ = K / Gamma,  Q~ = Q * Gamma,  Kbar = K * Gamma_C / Gamma
+//     K~ = K * Gamma,  K^ = K / Gamma,  Q~ = Q * Gamma,  Kbar = K^ * Gamma_C
 //     L    = strictly_lower(beta K~ K^T)           (C x C)
 //     A_qk = lower_incl(Q~ K^T)                    (C x C)
 //     (I + L) U = beta (V - K~ S)                  (U: C x d_v)
@@ -25,26 +25,38 @@
 // log alpha = 0 and therefore contribute nothing.
 //
 // Parallel decomposition.  One workgroup per (sequence, head, value slice)
-// walks its sequence chunk by chunk.  Each wave owns CT 16-column tiles of
-// the state for the whole sequence, in fp32 registers (MFMA C layout); the
-// columns of S evolve independently, so the per-column work never leaves the
-// wave, and one LDS read of a shared operand feeds CT MFMAs.
+// walks its sequence chunk by chunk.  Its waves have two roles:
+//   * consumer waves (NC of them) carry the state.  Each owns CT 16-column
+//     tiles of S for the whole sequence, in fp32 registers (MFMA C layout);
+//     the columns of S evolve independently.  Per chunk the consumers first
+//     share the S-independent MFMA work (the Gram products L and A_qk and the
+//     diagonal-block inverses, one job per wave), meet at an LDS counter,
+//     then each forms R, U, O and the next S of its columns with MFMA and
+//     writes its O columns straight from registers.
+//   * producer waves (NP of them) do the vector-ALU part of the prep, one
+//     chunk ahead, into double-buffered LDS tiles: global loads (issued a
+//     chunk ahead), the per-channel cumulative decay (a wave-local prefix
+//     scan: each producer wave owns a strip of key channels for all rows),
+//     the decayed operand tiles and V^T.
+// The roles meet only at monotonic counters in LDS (tiles ready, jobs done,
+// buffer released), so the producers' prep of chunk i+1 runs at the same time
+// as the consumers' recurrence of chunk i on every SIMD.
 //
-// Software pipeline.  The S-independent terms of a chunk ("prep") are built
-// one chunk ahead of the S-dependent recurrence ("chain"), in the same
-// barrier stages, from double-buffered LDS tiles, so that prep's VALU and
-// LDS work overlaps the chain's MFMA work.  For chunk i:
-//     stage X: prep 1 of i+1: beta, V^T, sums of log alpha | chain of i: R'
-//     stage Y: prep 2 of i+1: cumulative decay, decayed tiles; loads of i+2
-//                                                          | chain of i: U, O
-//     stage Z: prep 3 of i+1: Gram products, block inverse | chain of i: S update,
-//                                                            O store
+// Only consumer waves issue MFMAs, one consumer per SIMD, and a CU holds one
+// workgroup: on gfx950 a VALU read of an MFMA result a few instructions after
+// the MFMA was observed to see stale accumulators when MFMAs of another wave
+// shared the SIMD's matrix pipe, even with the compiler's wait states.
 // All MFMA operands are bf16 (or fp32 for f32 inputs); accumulation and the
 // carried state are fp32.
 #include <type_traits>
 
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
+
+// No implicit a*b+c -> fma contraction in this file: every launch shape
+// (template instance) then performs the same roundings, which makes results
+// bit-identical across value-slice splits.  Fused operations are written out.
+#pragma clang fp contract(off)
 
 namespace kda {
 
@@ -57,59 +69,74 @@ constexpr size_t align16(size_t x) { return (x + 15) & ~static_cast<size_t>(15);
 constexpr int kSortMax = 64;
 constexpr size_t kLdsBudget = 160 * 1024;
 
-template <bool BF16, int DK, int NW, int CT, int C_>
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+// Two buffers of per-chunk tiles plus the workgroup's bookkeeping.  Buffer b
+// starts at b * BUF.
+template <bool BF16, int DK, int NC, int CT, int C_>
 struct Layout {
     using E = typename Elem<BF16>::E;
     static constexpr int C = C_;
     static constexpr int NB = C / 16;
-    static constexpr int NT = 64 * NW;
-    static constexpr int BV = 16 * CT * NW;
+    static constexpr int BV = 16 * CT * NC;
     static constexpr int PAD = 16 / static_cast<int>(sizeof(E));  // 16 bytes of row padding
     static constexpr int LDK = DK + PAD;
     static constexpr int LDC = C + PAD;
-    static constexpr int LDV = BV + PAD;
     static constexpr int LDT = 16 + PAD;
     static constexpr size_t ES = sizeof(E);
-    // double-buffered tiles
-    static constexpr size_t SZ_KB = align16(C * LDK * ES);      // beta K~, Q~  [C][LDK]
-    static constexpr size_t SZ_KBT = align16(DK * LDC * ES);    // Kbar^T       [DK][LDC]
-    static constexpr size_t SZ_L = align16(C * LDC * ES);       // L, A_qk      [C][LDC]
-    static constexpr size_t SZ_T = align16(NB * 16 * LDT * ES);  // -T_bb       [NB][16][LDT]
-    static constexpr size_t SZ_VT = align16(BV * LDC * ES);     // V^T          [BV][LDC]
-    static constexpr size_t SZ_GC = align16(DK * 4);            // Gamma_C      [DK]
-    static constexpr size_t SZ_BETA = align16(C * 4);           // beta         [C]
-    static constexpr size_t OFF_KB = 0;
-    static constexpr size_t OFF_Q = OFF_KB + 2 * SZ_KB;
-    static constexpr size_t OFF_KBT = OFF_Q + 2 * SZ_KB;
-    static constexpr size_t OFF_L = OFF_KBT + 2 * SZ_KBT;
-    static constexpr size_t OFF_A = OFF_L + 2 * SZ_L;
-    static constexpr size_t OFF_T = OFF_A + 2 * SZ_L;
-    static constexpr size_t OFF_VT = OFF_T + 2 * SZ_T;
-    static constexpr size_t OFF_GC = OFF_VT + 2 * SZ_VT;
-    static constexpr size_t OFF_BETA = OFF_GC + 2 * SZ_GC;
-    // single-buffered
-    static constexpr size_t OFF_KH = OFF_BETA + 2 * SZ_BETA;                 // K^ [C][LDK]
-    static constexpr size_t OFF_O = OFF_KH + align16(C * LDK * ES);          // O  [C][LDV]
-    static constexpr size_t OFF_TOT = OFF_O + align16(C * LDV * ES);         // group sums [C/4][DK]
-    static constexpr size_t OFF_SEQ = OFF_TOT + align16((C / 4) * DK * 4);
-    static constexpr size_t BYTES = align16(OFF_SEQ + (kSortMax + 1) * 4);
+    static constexpr size_t SZ_KB = align16(C * LDK * ES);      // beta K~, Q~, K^  [C][LDK]
+    static constexpr size_t SZ_KBT = align16(DK * LDC * ES);    // Kbar^T           [DK][LDC]
+    static constexpr size_t SZ_L = align16(C * LDC * ES);       // L, A_qk          [C][LDC]
+    static constexpr size_t SZ_T = align16(NB * 16 * LDT * ES);  // -T_bb           [NB][16][LDT]
+    static constexpr size_t SZ_VT = align16(BV * LDC * ES);     // V^T              [BV][LDC]
+    static constexpr size_t SZ_GC = align16(DK * 4);            // Gamma_C          [DK]
+    static constexpr size_t SZ_BETA = align16(C * 4);           // beta             [C]
+    static constexpr size_t O_KB = 0;
+    static constexpr size_t O_Q = O_KB + SZ_KB;
+    static constexpr size_t O_KH = O_Q + SZ_KB;
+    static constexpr size_t O_KBT = O_KH + SZ_KB;
+    static constexpr size_t O_L = O_KBT + SZ_KBT;
+    static constexpr size_t O_A = O_L + SZ_L;
+    static constexpr size_t O_T = O_A + SZ_L;
+    static constexpr size_t O_VT = O_T + SZ_T;
+    static constexpr size_t O_GC = O_VT + SZ_VT;
+    static constexpr size_t O_BETA = O_GC + SZ_GC;
+    static constexpr size_t BUF = O_BETA + SZ_BETA;
+    static constexpr size_t OFF_SEQ = 2 * BUF;
+    static constexpr size_t OFF_CTR = OFF_SEQ + align16((kSortMax + 1) * 4);
+    static constexpr size_t BYTES = OFF_CTR + 32;
+    // Allocation: more than half of a CU's LDS, so that a CU never holds two
+    // workgroups (each SIMD then runs the MFMAs of one consumer wave only).
+    static constexpr size_t ALLOC = BYTES > kLdsBudget / 2 + 16 ? BYTES : kLdsBudget / 2 + 16;
 };
 
-template <bool BF16, int DK, int NW, int CT>
-using ChosenLayout =
-    Layout<BF16, DK, NW, CT, (Layout<BF16, DK, NW, CT, 32>::BYTES <= kLdsBudget ? 32 : 16)>;
+// The chunk length depends only on the storage type and d_k (sized for the
+// widest value slice, 128 columns), so that every value-slice split of a
+// problem runs the same chunk algebra and gives the same bits.
+template <bool BF16, int DK>
+constexpr int kChunk = Layout<BF16, DK, 4, 2, 32>::BYTES <= kLdsBudget ? 32 : 16;
 
-template <bool BF16, int DK, int NW, int CT>
-struct PrefillShape : ChosenLayout<BF16, DK, NW, CT> {
-    using Base = ChosenLayout<BF16, DK, NW, CT>;
+template <bool BF16, int DK, int NC, int CT>
+using ChosenLayout = Layout<BF16, DK, NC, CT, kChunk<BF16, DK>>;
+
+// Wave roles, in this order: NC consumers (all MFMA work), NP producers
+// (vector ALU and memory only).
+template <bool BF16, int DK, int NC, int CT>
+struct PrefillShape : ChosenLayout<BF16, DK, NC, CT> {
+    using Base = ChosenLayout<BF16, DK, NC, CT>;
     static_assert(Base::BYTES <= kLdsBudget, "LDS budget of one gfx950 workgroup");
-    static constexpr int RG = 4;                // rows per prefix-sum group (fixed)
-    static constexpr int NG = Base::C / RG;     // prefix-sum groups per chunk
-    static constexpr int QPR = DK / 4;          // channel quads per row
-    static constexpr int NITEMS = NG * QPR;     // (group, channel quad) items
-    static constexpr int IPT = (NITEMS + Base::NT - 1) / Base::NT;
+    static constexpr int NRG = Base::C / 4;  // row groups of 4 rows
+    static constexpr int QW = 64 / NRG;      // channel quads per producer wave
+    static constexpr int NQ = DK / 4;        // channel quads
+    static constexpr int NP = NQ > QW ? NQ / QW : 1;
+    static_assert(NQ <= QW || NQ % QW == 0, "channel strips tile d_k");
+    static constexpr int NJOB = Base::NB * (Base::NB + 1) / 2;  // Gram/inverse jobs per chunk
+    static constexpr int NW = NC + NP;
+    static constexpr int NT = 64 * NW;
+    static_assert(NW <= 16, "at most 16 waves per workgroup");
     static constexpr int VITEMS = (Base::C / 4) * (Base::BV / 4);  // 4x4 blocks of V
-    static constexpr int VPT = (VITEMS + Base::NT - 1) / Base::NT;
+    static constexpr int VPT = (VITEMS + 64 * NP - 1) / (64 * NP);
 };
 
 template <bool BF16>
@@ -161,16 +188,86 @@ __device__ __forceinline__ void transpose4(const typename Elem<BF16>::R4 (&rows)
     }
 }
 
+// Raw buffer resource over [base, base + bytes): a load at a byte offset at
+// or past `bytes` returns zero without touching memory.  Per-chunk resources
+// make every load one instruction (a per-lane offset fixed for the whole
+// sequence plus a scalar row offset) and zero the rows past a sequence end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
+                       __uint_as_float(x[3]));
+}
+
+__device__ __forceinline__ float buf_load_f1(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+// four consecutive storage elements, raw
+template <bool BF16>
+__device__ __forceinline__ typename Elem<BF16>::R4 buf_load_raw4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    if constexpr (BF16) {
+        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        return make_uint2(x[0], x[1]);
+    } else {
+        return buf_load_f4(r, voff, soff);
+    }
+}
+
+// x of lane (l - D) within the same 16-lane row, 0 where there is none.
+// A DPP read from a lane that is masked off also yields 0, so callers must
+// call this with every lane of the wave active (not inside a lane-dependent
+// branch, which includes either arm of a conditional expression).
+template <int D>
+__device__ __forceinline__ float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + D, 0xF, 0xF, true));
+}
+
+// Inter-wave hand-off through monotonic counters in LDS.  signal: once this
+// wave's earlier LDS reads and writes have completed, add one.  wait: spin
+// until the counter reaches target.  LDS accesses of one wave are performed
+// in order, so data written before a signal is visible after the wait.
+__device__ __forceinline__ void ctr_signal(int* ctr, int lane) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    asm volatile("" ::: "memory");
+}
+
+//
+// Every wait is bounded: a wait that has not been satisfied after kSpinMax
+// sleeps (far beyond any legitimate hand-off) marks the workgroup as failed
+// in *fault and returns, so the kernel always drains; the consumers then
+// write NaN final states, which no caller can mistake for a result.
+constexpr int kSpinMax = 1 << 24;
+
+__device__ __forceinline__ void ctr_wait(int* ctr, int target, int* fault) {
+    int spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+        if (++spins > kSpinMax) {
+            __hip_atomic_store(fault, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace
 
-template <bool BF16, int DK, int NW, int CT>
-__global__ __launch_bounds__(64 * NW) void prefill_kernel(
+template <bool BF16, int DK, int NC, int CT>
+__global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_kernel(
     const typename Elem<BF16>::G* __restrict__ q, const typename Elem<BF16>::G* __restrict__ k,
     const typename Elem<BF16>::G* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, const float* __restrict__ S0, const int32_t* __restrict__ cu,
     int N, int H, int dv, int v_split, typename Elem<BF16>::G* __restrict__ o,
     float* __restrict__ S_T) {
-    using Sh = PrefillShape<BF16, DK, NW, CT>;
+    using Sh = PrefillShape<BF16, DK, NC, CT>;
     using T = Elem<BF16>;
     using E = typename T::E;
     using G = typename T::G;
@@ -178,28 +275,32 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(
     using F8 = typename T::F8;
     using F4 = typename T::F4;
     constexpr int C = Sh::C, NB = Sh::NB, NT = Sh::NT, BV = Sh::BV;
-    constexpr int LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV, LDT = Sh::LDT;
+    constexpr int NP = Sh::NP;
+    constexpr int LDK = Sh::LDK, LDC = Sh::LDC, LDT = Sh::LDT;
     constexpr int KB = DK / 32;  // 32-deep k blocks over key channels
-    constexpr int RG = Sh::RG, NG = Sh::NG, QPR = Sh::QPR, IPT = Sh::IPT, NITEMS = Sh::NITEMS;
-    constexpr int VPT = Sh::VPT, VITEMS = Sh::VITEMS;
+    constexpr int NRG = Sh::NRG, QW = Sh::QW, NQ = Sh::NQ, VPT = Sh::VPT, VITEMS = Sh::VITEMS;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Sh::BYTES];
-#define KDA_TILE(name, type, off, sz) \
-    auto name = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<type*>(smem + (off) + b * (sz)); }
-    KDA_TILE(tKb, E, Sh::OFF_KB, Sh::SZ_KB);
-    KDA_TILE(tQ, E, Sh::OFF_Q, Sh::SZ_KB);
-    KDA_TILE(tKbT, E, Sh::OFF_KBT, Sh::SZ_KBT);
-    KDA_TILE(tL, E, Sh::OFF_L, Sh::SZ_L);
-    KDA_TILE(tA, E, Sh::OFF_A, Sh::SZ_L);
-    KDA_TILE(tT, E, Sh::OFF_T, Sh::SZ_T);
-    KDA_TILE(tVt, E, Sh::OFF_VT, Sh::SZ_VT);
-    KDA_TILE(sGC, float, Sh::OFF_GC, Sh::SZ_GC);
-    KDA_TILE(sBeta, float, Sh::OFF_BETA, Sh::SZ_BETA);
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Sh::ALLOC];
+#define KDA_TILE(name, type, off) \
+    auto name = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<type*>(smem + b * Sh::BUF + (off)); }
+    KDA_TILE(tKb, E, Sh::O_KB);
+    KDA_TILE(tQ, E, Sh::O_Q);
+    KDA_TILE(tKh, E, Sh::O_KH);
+    KDA_TILE(tKbT, E, Sh::O_KBT);
+    KDA_TILE(tL, E, Sh::O_L);
+    KDA_TILE(tA, E, Sh::O_A);
+    KDA_TILE(tT, E, Sh::O_T);
+    KDA_TILE(tVt, E, Sh::O_VT);
+    KDA_TILE(sGC, float, Sh::O_GC);
+    KDA_TILE(sBeta, float, Sh::O_BETA);
 #undef KDA_TILE
-    E* const tKh = reinterpret_cast<E*>(smem + Sh::OFF_KH);
-    E* const tO = reinterpret_cast<E*>(smem + Sh::OFF_O);
-    float* const sTot = reinterpret_cast<float*>(smem + Sh::OFF_TOT);
     int* const sSeq = reinterpret_cast<int*>(smem + Sh::OFF_SEQ);
+    // Monotonic counters, one signal per wave per chunk:
+    int* const ctr = reinterpret_cast<int*>(smem + Sh::OFF_CTR);
+    int* const nPrep = ctr + 0;    // producers: decayed tiles written
+    int* const nSolved = ctr + 1;  // consumers: their L, A_qk, -T_bb jobs written
+    int* const nFree = ctr + 2;    // consumers: buffer of the chunk released
+    int* const fault = ctr + 3;    // a bounded wait gave up
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -248,17 +349,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(
     const int nchunks = (t_end - t_beg + C - 1) / C;
     const int j0 = slice * BV;  // first value column of this workgroup
     const size_t pair = static_cast<size_t>(n) * H + h;
+    auto chunk_len = [&](int i) __attribute__((always_inline)) { return min(C, t_end - (t_beg + i * C)); };
 
-    // Per-head base pointers; per-token offsets below fit in 32 bits (the
-    // host rejects tensors of 2^31 elements or more).
+    // Per-token offsets below fit in 32 bits (the host rejects tensors of
+    // 2^31 elements or more).
     const int strideK = H * DK;
     const int strideV = H * dv;
-    const G* const qh = q + static_cast<size_t>(h) * DK;
-    const G* const kh = k + static_cast<size_t>(h) * DK;
-    const float* const lah = log_alpha + static_cast<size_t>(h) * DK;
-    const float* const bh = beta + h;
-    const G* const vh = v + static_cast<size_t>(h) * dv + j0;
-    G* const oh = o + static_cast<size_t>(h) * dv + j0;
 
     // Upper block-triangles of L and A_qk stay zero for the whole kernel.
     for (int idx = tid; idx < C * LDC; idx += NT) {
@@ -268,438 +364,425 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(
             tA(b)[idx] = T::to_e(0.f);
         }
     }
+    if (tid < 4) ctr[tid] = 0;
+    __syncthreads();
 
-    // ---- state slice in registers: Sr[ct][it][j] = S[16 it + 4 lg + j][col]
-    auto col0 = [&](int ct) __attribute__((always_inline)) { return 16 * (CT * wave + ct); };
-    f32x4_t Sr[CT][DK / 16];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-        const size_t col = static_cast<size_t>(j0 + col0(ct) + ln);
-#pragma unroll
-        for (int it = 0; it < DK / 16; ++it) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                Sr[ct][it][j] = S0 ? S0[(pair * DK + 16 * it + 4 * lg + j) * dv + col] : 0.f;
-        }
-    }
-
-    // ---- raw inputs of one chunk, in registers -----------------------------
-    // Every load is unconditional: rows past the end of the sequence read the
-    // last valid row (always in bounds) and are zeroed where they are used.
-    float4 rla[IPT][RG];
-    R4 rk[IPT][RG], rq[IPT][RG], rv[VPT][4];
-    float rb = 0.f;
-    auto load_chunk = [&](int c0, int len) __attribute__((always_inline)) {
-        const int last = len - 1;
-#pragma unroll
-        for (int ii = 0; ii < IPT; ++ii) {
-            const int it = tid + NT * ii;
-            if (NITEMS % NT == 0 || it < NITEMS) {
-                const int grp = it / QPR;
-                const int i0 = 4 * (it % QPR);
-#pragma unroll
-                for (int rr = 0; rr < RG; ++rr) {
-                    const int off = (c0 + min(grp * RG + rr, last)) * strideK + i0;
-                    rla[ii][rr] = *reinterpret_cast<const float4*>(lah + off);
-                    rk[ii][rr] = T::raw4(kh + off);
-                    rq[ii][rr] = T::raw4(qh + off);
-                }
-            }
-        }
-#pragma unroll
-        for (int vv = 0; vv < VPT; ++vv) {
-            const int idx = tid + NT * vv;
-            if (VITEMS % NT == 0 || idx < VITEMS) {
-                const int r0 = 4 * (idx / (BV / 4));
-                const int c4 = 4 * (idx % (BV / 4));
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    rv[vv][rr] = T::raw4(vh + (c0 + min(r0 + rr, last)) * strideV + c4);
-            }
-        }
-        if (tid < C) rb = bh[(c0 + min(tid, last)) * H];
-    };
-
-    // ---- prep 1: beta, V^T, group sums of log alpha ------------------------
-    auto prep1 = [&](int B, int len) __attribute__((always_inline)) {
-        if (tid < C) sBeta(B)[tid] = (tid < len) ? rb : 0.f;
-#pragma unroll
-        for (int vv = 0; vv < VPT; ++vv) {
-            const int idx = tid + NT * vv;
-            if (VITEMS % NT == 0 || idx < VITEMS) {
-                const int r0 = 4 * (idx / (BV / 4));
-                const int c4 = 4 * (idx % (BV / 4));
-                R4 rows[4], cols[4];
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) rows[rr] = (r0 + rr < len) ? rv[vv][rr] : R4{};
-                transpose4<BF16>(rows, cols);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) T::lds_put_raw4(tVt(B) + (c4 + c) * LDC + r0, cols[c]);
-            }
-        }
-#pragma unroll
-        for (int ii = 0; ii < IPT; ++ii) {
-            const int it = tid + NT * ii;
-            if (NITEMS % NT == 0 || it < NITEMS) {
-                const int grp = it / QPR;
-                const int i0 = 4 * (it % QPR);
-                float4 tot = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-                for (int rr = 0; rr < RG; ++rr) {
-                    const bool ok = grp * RG + rr < len;
-                    tot.x += ok ? rla[ii][rr].x : 0.f;
-                    tot.y += ok ? rla[ii][rr].y : 0.f;
-                    tot.z += ok ? rla[ii][rr].z : 0.f;
-                    tot.w += ok ? rla[ii][rr].w : 0.f;
-                }
-                *reinterpret_cast<float4*>(sTot + grp * DK + i0) = tot;
-            }
-        }
-    };
-
-    // ---- prep 2: cumulative decay and decayed operand tiles ----------------
-    auto prep2_item = [&](auto full, int ii, int B, int len) __attribute__((always_inline)) {
-        constexpr bool FULL = decltype(full)::value;
-        const int it = tid + NT * ii;
-        const int grp = it / QPR;
-        const int i0 = 4 * (it % QPR);
-        // g = sum of the group sums before this group; g_C = sum of all of
-        // them; both in the same fixed order for every launch shape.
-        float g[4] = {0.f, 0.f, 0.f, 0.f}, gcs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = 0; p < NG; ++p) {
-            const float4 sm = *reinterpret_cast<const float4*>(sTot + p * DK + i0);
-            const bool before = p < grp;
-            g[0] += before ? sm.x : 0.f;
-            g[1] += before ? sm.y : 0.f;
-            g[2] += before ? sm.z : 0.f;
-            g[3] += before ? sm.w : 0.f;
-            gcs[0] += sm.x;
-            gcs[1] += sm.y;
-            gcs[2] += sm.z;
-            gcs[3] += sm.w;
-        }
-        float Gc[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) Gc[c] = __builtin_amdgcn_exp2f(gcs[c] * kLog2e);
-        if (grp == 0) *reinterpret_cast<float4*>(sGC(B) + i0) = make_float4(Gc[0], Gc[1], Gc[2], Gc[3]);
-        float kbar[RG][4];
-#pragma unroll
-        for (int rr = 0; rr < RG; ++rr) {
-            const int r = grp * RG + rr;
-            const bool ok = FULL || r < len;
-            float kk[4], qq[4];
-            T::unpack4(rk[ii][rr], kk);
-            T::unpack4(rq[ii][rr], qq);
-            const float4 a = rla[ii][rr];
-            g[0] += ok ? a.x : 0.f;
-            g[1] += ok ? a.y : 0.f;
-            g[2] += ok ? a.z : 0.f;
-            g[3] += ok ? a.w : 0.f;
-            const float b = sBeta(B)[r];
-            float gam[4], inv[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (!FULL && !ok) {
-                    kk[c] = 0.f;
-                    qq[c] = 0.f;
-                }
-                // exp(+-g) as 2^(+-g log2 e): one v_exp_f32 each; |g| stays
-                // within the numerical contract, where results are normal.
-                const float gl = g[c] * kLog2e;
-                gam[c] = __builtin_amdgcn_exp2f(gl);
-                inv[c] = __builtin_amdgcn_exp2f(-gl);
-                kbar[rr][c] = kk[c] * (Gc[c] * inv[c]);
-            }
-            const float bk0 = b * kk[0], bk1 = b * kk[1], bk2 = b * kk[2], bk3 = b * kk[3];
-            lds_store4<BF16>(tKb(B) + r * LDK + i0, bk0 * gam[0], bk1 * gam[1], bk2 * gam[2], bk3 * gam[3]);
-            lds_store4<BF16>(tKh + r * LDK + i0, kk[0] * inv[0], kk[1] * inv[1], kk[2] * inv[2],
-                             kk[3] * inv[3]);
-            lds_store4<BF16>(tQ(B) + r * LDK + i0, qq[0] * gam[0], qq[1] * gam[1], qq[2] * gam[2],
-                             qq[3] * gam[3]);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            lds_store4<BF16>(tKbT(B) + (i0 + c) * LDC + grp * RG, kbar[0][c], kbar[1][c], kbar[2][c],
-                             kbar[3][c]);
-    };
-    auto prep2 = [&](int B, int len) __attribute__((always_inline)) {
-#pragma unroll
-        for (int ii = 0; ii < IPT; ++ii) {
-            if (NITEMS % NT == 0 || tid + NT * ii < NITEMS) {
-                if (len == C) {
-                    prep2_item(std::true_type{}, ii, B, len);
-                } else {
-                    prep2_item(std::false_type{}, ii, B, len);
-                }
-            }
-        }
-    };
-
-    // ---- prep 3: Gram products and block inverse ---------------------------
-    // Job (st, rt), st <= rt, computes the tiles at block (rt, st) of
-    // L = strictly_lower(beta K~ K^T) and A_qk = lower_incl(Q~ K^T), sharing
-    // the K^ operand.  They are computed transposed, P[s][r] = K^_s . X_r, so
-    // that each lane's four C-layout values are four consecutive columns of
-    // row r.
-    //
-    // A diagonal job also forms -T_bb = -(I + N)^-1, N = L_bb (strictly lower,
-    // nilpotent: N^16 = 0), as the product (I - N)(I + N^2)(I + N^4)(I + N^8),
-    // with MFMA.  The factors are polynomials in N and commute, so every
-    // product can take its A operand from a C-layout tile already held:
-    // the A operand of X is the C layout of X^T, the B operand of X is the C
-    // layout of X.  Both layouts of N come from the Gram MFMAs (P and P^T).
-    auto prep3 = [&](int B) __attribute__((always_inline)) {
-        constexpr int NJOB = NB * (NB + 1) / 2;
-        for (int job = NW - 1 - wave; job < NJOB; job += NW) {
-            int st, rt;
-            if (job < NB) {
-                st = rt = job;
-            } else {
-                int tix = job - NB;  // enumerate st < rt
-                rt = 1;
-                while (tix >= rt) {
-                    tix -= rt;
-                    ++rt;
-                }
-                st = tix;
-            }
-            const bool diag = st == rt;
-            const E* Ab = tKh + 16 * st * LDK;
-            const E* Bk = tKb(B) + 16 * rt * LDK;
-            const E* Bq = tQ(B) + 16 * rt * LDK;
-            f32x4_t accL = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f}, accN = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const F8 a = lds_frag8<BF16>(Ab + 32 * kb, LDK, lane);
-                const F8 bk = lds_frag8<BF16>(Bk + 32 * kb, LDK, lane);
-                accL = mma8<BF16>(accL, a, bk);
-                accA = mma8<BF16>(accA, a, lds_frag8<BF16>(Bq + 32 * kb, LDK, lane));
-                if (diag) accN = mma8<BF16>(accN, bk, a);  // P^T: C layout of N
-            }
-            const int r = 16 * rt + ln;
-            float vl[4], va[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int s2 = 16 * st + 4 * lg + j;
-                vl[j] = (s2 < r) ? accL[j] : 0.f;
-                va[j] = (s2 <= r) ? accA[j] : 0.f;
-            }
-            lds_store4<BF16>(tL(B) + r * LDC + 16 * st + 4 * lg, vl[0], vl[1], vl[2], vl[3]);
-            lds_store4<BF16>(tA(B) + r * LDC + 16 * st + 4 * lg, va[0], va[1], va[2], va[3]);
-            if (diag) {
-                // C layout: lane (ln, lg), value j is element (row 4 lg + j, col ln).
-                f32x4_t Nt, Nc;  // C layouts of N^T and N (strictly lower N)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    Nt[j] = vl[j];
-                    Nc[j] = (ln < 4 * lg + j) ? accN[j] : 0.f;
-                }
-                auto eye = [&](f32x4_t x, float sgn) __attribute__((always_inline)) {
-                    f32x4_t y;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) y[j] = sgn * x[j] + ((4 * lg + j == ln) ? 1.f : 0.f);
-                    return y;
-                };
-                const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-                const f32x4_t N2 = mma4<BF16>(z, acc_frag4<BF16>(Nt), acc_frag4<BF16>(Nc));
-                const f32x4_t N2t = mma4<BF16>(z, acc_frag4<BF16>(Nc), acc_frag4<BF16>(Nt));
-                const f32x4_t N4 = mma4<BF16>(z, acc_frag4<BF16>(N2t), acc_frag4<BF16>(N2));
-                const f32x4_t N4t = mma4<BF16>(z, acc_frag4<BF16>(N2), acc_frag4<BF16>(N2t));
-                const f32x4_t N8 = mma4<BF16>(z, acc_frag4<BF16>(N4t), acc_frag4<BF16>(N4));
-                // Q1 = (I + N8^T)(I + N4^T), Q2 = (I + N2^T) Q1, Q3 = (I - N^T) Q2 = T^T
-                const f32x4_t Q1 = mma4<BF16>(z, acc_frag4<BF16>(eye(N8, 1.f)), acc_frag4<BF16>(eye(N4t, 1.f)));
-                const f32x4_t Q2 = mma4<BF16>(z, acc_frag4<BF16>(eye(N2, 1.f)), acc_frag4<BF16>(Q1));
-                const f32x4_t Q3 = mma4<BF16>(z, acc_frag4<BF16>(eye(Nc, -1.f)), acc_frag4<BF16>(Q2));
-                // lane (ln, lg) holds T[ln][4 lg + j]: store -T row-major
-                lds_store4<BF16>(tT(B) + (rt * 16 + ln) * LDT + 4 * lg, -Q3[0], -Q3[1], -Q3[2], -Q3[3]);
-            }
-        }
-    };
-
-    // ---- chain: per-wave column recurrence of the chunk in buffer B ---------
-    F8 sf[CT][KB];
-    f32x4_t Rp[CT][NB], U[CT][NB];
-    F4 uf[CT][NB];
-
-    // R' = beta K~ S - beta V  (= -R)
-    auto chain_R = [&](int B) __attribute__((always_inline)) {
+    // Issue priority follows the critical path: the consumers' recurrence is
+    // the serial chain of the sequence; the producers work ahead with slack.
+    if (wave < NC) {
+        // =====================================================================
+        // consumer: the recurrence of value columns j0 + 16 (CT wave + ct) + ...
+        // =====================================================================
+        __builtin_amdgcn_s_setprio(3);
+        G* const oh = o + static_cast<size_t>(h) * dv + j0;
+        auto col0 = [&](int ct) __attribute__((always_inline)) { return 16 * (CT * wave + ct); };
+        // Sr[ct][it][j] = S[16 it + 4 lg + j][col]
+        f32x4_t Sr[CT][DK / 16];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
+            const size_t col = static_cast<size_t>(j0 + col0(ct) + ln);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) sf[ct][kb] = acc_frag8<BF16>(Sr[ct][2 * kb], Sr[ct][2 * kb + 1]);
+            for (int it = 0; it < DK / 16; ++it) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    Sr[ct][it][j] = S0 ? S0[(pair * DK + 16 * it + 4 * lg + j) * dv + col] : 0.f;
+            }
         }
+
+        // Job (st, rt), st <= rt, computes the tiles at block (rt, st) of
+        // L = strictly_lower(beta K~ K^T) and A_qk = lower_incl(Q~ K^T),
+        // sharing the K^ operand.  They are computed transposed,
+        // P[s][r] = K^_s . X_r, so that each lane's four C-layout values are
+        // four consecutive columns of row r.
+        //
+        // A diagonal job also forms -T_bb = -(I + N)^-1, N = L_bb (strictly
+        // lower, nilpotent: N^16 = 0), as (I + N^8)(I + N^4)(I - N)(I + N^2)
+        // with MFMA, four products deep.  The factors are polynomials in N
+        // and commute, so every product can take its A operand from a
+        // C-layout tile already held: the A operand of X is the C layout of
+        // X^T, the B operand of X is the C layout of X.  Both layouts of N
+        // come from the Gram MFMAs (P and P^T).
+        auto prep3 = [&](int S) __attribute__((always_inline)) {
+            for (int job = wave; job < Sh::NJOB; job += NC) {
+                int st, rt;
+                if (job < NB) {
+                    st = rt = job;
+                } else {
+                    int tix = job - NB;  // enumerate st < rt
+                    rt = 1;
+                    while (tix >= rt) {
+                        tix -= rt;
+                        ++rt;
+                    }
+                    st = tix;
+                }
+                const bool diag = st == rt;
+                const E* Ab = tKh(S) + 16 * st * LDK;
+                const E* Bk = tKb(S) + 16 * rt * LDK;
+                const E* Bq = tQ(S) + 16 * rt * LDK;
+                f32x4_t accL = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f}, accN = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-            const float4 b4 = *reinterpret_cast<const float4*>(sBeta(B) + 16 * rt + 4 * lg);
+                for (int kb = 0; kb < KB; ++kb) {
+                    const F8 a = lds_frag8<BF16>(Ab + 32 * kb, LDK, lane);
+                    const F8 bk = lds_frag8<BF16>(Bk + 32 * kb, LDK, lane);
+                    accL = mma8<BF16>(accL, a, bk);
+                    accA = mma8<BF16>(accA, a, lds_frag8<BF16>(Bq + 32 * kb, LDK, lane));
+                    if (diag) accN = mma8<BF16>(accN, bk, a);  // P^T: C layout of N
+                }
+                const int r = 16 * rt + ln;
+                float vl[4], va[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int s2 = 16 * st + 4 * lg + j;
+                    vl[j] = (s2 < r) ? accL[j] : 0.f;
+                    va[j] = (s2 <= r) ? accA[j] : 0.f;
+                }
+                lds_store4<BF16>(tL(S) + r * LDC + 16 * st + 4 * lg, vl[0], vl[1], vl[2], vl[3]);
+                lds_store4<BF16>(tA(S) + r * LDC + 16 * st + 4 * lg, va[0], va[1], va[2], va[3]);
+                if (diag) {
+                    // C layout: lane (ln, lg), value j is element (row 4 lg + j, col ln).
+                    f32x4_t Nt, Nc;  // C layouts of N^T and N (strictly lower N)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        Nt[j] = vl[j];
+                        Nc[j] = (ln < 4 * lg + j) ? accN[j] : 0.f;
+                    }
+                    auto eye = [&](f32x4_t x, float sgn) __attribute__((always_inline)) {
+                        f32x4_t y;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) y[j] = sgn * x[j] + ((4 * lg + j == ln) ? 1.f : 0.f);
+                        return y;
+                    };
+                    auto f4 = [&](const f32x4_t& x) __attribute__((always_inline)) { return acc_frag4<BF16>(x); };
+                    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+                    // depth 1
+                    const f32x4_t N2 = mma4<BF16>(z, f4(Nt), f4(Nc));
+                    const f32x4_t N2t = mma4<BF16>(z, f4(Nc), f4(Nt));
+                    // depth 2: P1 = (I - N)(I + N^2)
+                    const f32x4_t P1 = mma4<BF16>(z, f4(eye(Nt, -1.f)), f4(eye(N2, 1.f)));
+                    const f32x4_t N4 = mma4<BF16>(z, f4(N2t), f4(N2));
+                    const f32x4_t N4t = mma4<BF16>(z, f4(N2), f4(N2t));
+                    // depth 3: P2 = (I + N^4) P1, and (N^8)^T
+                    const f32x4_t P2 = mma4<BF16>(z, f4(eye(N4t, 1.f)), f4(P1));
+                    const f32x4_t N8t = mma4<BF16>(z, f4(N4), f4(N4t));
+                    // depth 4: T^T = P2^T (I + N^8)^T
+                    const f32x4_t Tt = mma4<BF16>(z, f4(P2), f4(eye(N8t, 1.f)));
+                    // lane (ln, lg) holds T[ln][4 lg + j]: store -T row-major
+                    lds_store4<BF16>(tT(S) + (rt * 16 + ln) * LDT + 4 * lg, -Tt[0], -Tt[1], -Tt[2], -Tt[3]);
+                }
+            }
+        };
+
+        F8 sf[CT][KB];
+        f32x4_t Rp[CT][NB], U[CT][NB];
+        F4 uf[CT][NB];
+
+        // R' = beta K~ S - beta V  (= -R)
+        auto chain_R = [&](int B) __attribute__((always_inline)) {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                const f32x4_t v4 = lds_load4<BF16>(tVt(B) + (col0(ct) + ln) * LDC + 16 * rt + 4 * lg);
-                Rp[ct][rt] = f32x4_t{-b4.x * v4[0], -b4.y * v4[1], -b4.z * v4[2], -b4.w * v4[3]};
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    sf[ct][kb] = acc_frag8<BF16>(Sr[ct][2 * kb], Sr[ct][2 * kb + 1]);
             }
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const F8 a = lds_frag8<BF16>(tKb(B) + 16 * rt * LDK + 32 * kb, LDK, lane);
+            for (int rt = 0; rt < NB; ++rt) {
+                const float4 b4 = *reinterpret_cast<const float4*>(sBeta(B) + 16 * rt + 4 * lg);
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) Rp[ct][rt] = mma8<BF16>(Rp[ct][rt], a, sf[ct][kb]);
+                for (int ct = 0; ct < CT; ++ct) {
+                    const f32x4_t v4 = lds_load4<BF16>(tVt(B) + (col0(ct) + ln) * LDC + 16 * rt + 4 * lg);
+                    Rp[ct][rt] = f32x4_t{-b4.x * v4[0], -b4.y * v4[1], -b4.z * v4[2], -b4.w * v4[3]};
+                }
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const F8 a = lds_frag8<BF16>(tKb(B) + 16 * rt * LDK + 32 * kb, LDK, lane);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) Rp[ct][rt] = mma8<BF16>(Rp[ct][rt], a, sf[ct][kb]);
+                }
             }
+        };
+        auto u_frag8 = [&](int ct, int b) __attribute__((always_inline)) {
+            return F8(__builtin_shufflevector(uf[ct][b], uf[ct][b + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        // U_b = (-T_bb) (R'_b + sum_{c<b} L_bc U_c);  then O^T = S^T Q~^T + U^T A_qk^T,
+        // written to global memory from the C layout: lane (ln, lg) holds
+        // four consecutive value columns of token row 16 rt + ln.
+        auto chain_UO = [&](int B, int c0, int len) __attribute__((always_inline)) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                f32x4_t Y[CT];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) Y[ct] = Rp[ct][b];
+#pragma unroll
+                for (int kp = 0; kp + 1 < b; kp += 2) {
+                    const F8 a = lds_frag8<BF16>(tL(B) + 16 * b * LDC + 16 * kp, LDC, lane);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) Y[ct] = mma8<BF16>(Y[ct], a, u_frag8(ct, kp));
+                }
+                if (b & 1) {
+                    const F4 a = lds_frag4<BF16>(tL(B) + 16 * b * LDC + 16 * (b - 1), LDC, lane);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) Y[ct] = mma4<BF16>(Y[ct], a, uf[ct][b - 1]);
+                }
+                const F4 tb = lds_frag4<BF16>(tT(B) + 16 * b * LDT, LDT, lane);
+                const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) U[ct][b] = mma4<BF16>(z, tb, acc_frag4<BF16>(Y[ct]));
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) uf[ct][b] = acc_frag4<BF16>(U[ct][b]);
+            }
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) {
+                f32x4_t acc[CT];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const F8 bq = lds_frag8<BF16>(tQ(B) + 16 * rt * LDK + 32 * kb, LDK, lane);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], sf[ct][kb], bq);
+                }
+#pragma unroll
+                for (int sp = 0; sp + 1 <= rt; sp += 2) {
+                    const F8 ba = lds_frag8<BF16>(tA(B) + 16 * rt * LDC + 16 * sp, LDC, lane);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], u_frag8(ct, sp), ba);
+                }
+                if (!(rt & 1)) {
+                    const F4 ba = lds_frag4<BF16>(tA(B) + 16 * rt * LDC + 16 * rt, LDC, lane);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) acc[ct] = mma4<BF16>(acc[ct], uf[ct][rt], ba);
+                }
+                const int r = 16 * rt + ln;
+                if (r < len) {
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        const float x[4] = {acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]};
+                        T::store4(oh + (c0 + r) * strideV + col0(ct) + 4 * lg, x);
+                    }
+                }
+            }
+        };
+        // S <- Diag(Gamma_C) S + Kbar^T U
+        auto chain_S = [&](int B) __attribute__((always_inline)) {
+#pragma unroll
+            for (int it = 0; it < DK / 16; ++it) {
+                const float4 g4 = *reinterpret_cast<const float4*>(sGC(B) + 16 * it + 4 * lg);
+                f32x4_t acc[CT];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    acc[ct] = f32x4_t{Sr[ct][it][0] * g4.x, Sr[ct][it][1] * g4.y, Sr[ct][it][2] * g4.z,
+                                      Sr[ct][it][3] * g4.w};
+#pragma unroll
+                for (int kb = 0; kb < NB / 2; ++kb) {
+                    const F8 a = lds_frag8<BF16>(tKbT(B) + 16 * it * LDC + 32 * kb, LDC, lane);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], a, u_frag8(ct, 2 * kb));
+                }
+                if constexpr (NB & 1) {
+                    const F4 a = lds_frag4<BF16>(tKbT(B) + 16 * it * LDC + 16 * (NB - 1), LDC, lane);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) acc[ct] = mma4<BF16>(acc[ct], a, uf[ct][NB - 1]);
+                }
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) Sr[ct][it] = acc[ct];
+            }
+        };
+
+        for (int i = 0; i < nchunks; ++i) {
+            const int B = i & 1;
+            ctr_wait(nPrep, NP * (i + 1), fault);
+            prep3(B);
+            ctr_signal(nSolved, lane);
+            ctr_wait(nSolved, NC * (i + 1), fault);
+            chain_R(B);
+            chain_UO(B, t_beg + i * C, chunk_len(i));
+            chain_S(B);
+            ctr_signal(nFree, lane);
         }
-    };
-    auto u_frag8 = [&](int ct, int b) __attribute__((always_inline)) {
-        return F8(__builtin_shufflevector(uf[ct][b], uf[ct][b + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    // U_b = (-T_bb) (R'_b + sum_{c<b} L_bc U_c);  then O^T = S^T Q~^T + U^T A_qk^T
-    auto chain_UO = [&](int B) __attribute__((always_inline)) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            f32x4_t Y[CT];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) Y[ct] = Rp[ct][b];
-#pragma unroll
-            for (int kp = 0; kp + 1 < b; kp += 2) {
-                const F8 a = lds_frag8<BF16>(tL(B) + 16 * b * LDC + 16 * kp, LDC, lane);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) Y[ct] = mma8<BF16>(Y[ct], a, u_frag8(ct, kp));
-            }
-            if (b & 1) {
-                const F4 a = lds_frag4<BF16>(tL(B) + 16 * b * LDC + 16 * (b - 1), LDC, lane);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) Y[ct] = mma4<BF16>(Y[ct], a, uf[ct][b - 1]);
-            }
-            const F4 tb = lds_frag4<BF16>(tT(B) + 16 * b * LDT, LDT, lane);
-            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+
+        // Every wave's last signal follows all of its waits, so a fault
+        // recorded by any wave is visible after the last rendezvous.
+        if (__hip_atomic_load(fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                U[ct][b] = mma4<BF16>(z, tb, acc_frag4<BF16>(Y[ct]));
-                uf[ct][b] = acc_frag4<BF16>(U[ct][b]);
+#pragma unroll
+                for (int it = 0; it < DK / 16; ++it) Sr[ct][it] = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
             }
         }
 #pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-            f32x4_t acc[CT];
+        for (int ct = 0; ct < CT; ++ct) {
+            const size_t col = static_cast<size_t>(j0 + col0(ct) + ln);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int it = 0; it < DK / 16; ++it) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const F8 bq = lds_frag8<BF16>(tQ(B) + 16 * rt * LDK + 32 * kb, LDK, lane);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], sf[ct][kb], bq);
-            }
-#pragma unroll
-            for (int sp = 0; sp + 1 <= rt; sp += 2) {
-                const F8 ba = lds_frag8<BF16>(tA(B) + 16 * rt * LDC + 16 * sp, LDC, lane);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], u_frag8(ct, sp), ba);
-            }
-            if (!(rt & 1)) {
-                const F4 ba = lds_frag4<BF16>(tA(B) + 16 * rt * LDC + 16 * rt, LDC, lane);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc[ct] = mma4<BF16>(acc[ct], uf[ct][rt], ba);
-            }
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-                lds_store4<BF16>(tO + (16 * rt + ln) * LDV + col0(ct) + 4 * lg, acc[ct][0], acc[ct][1],
-                                 acc[ct][2], acc[ct][3]);
-        }
-    };
-    // S <- Diag(Gamma_C) S + Kbar^T U
-    auto chain_S = [&](int B) __attribute__((always_inline)) {
-#pragma unroll
-        for (int it = 0; it < DK / 16; ++it) {
-            const float4 g4 = *reinterpret_cast<const float4*>(sGC(B) + 16 * it + 4 * lg);
-            f32x4_t acc[CT];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-                acc[ct] = f32x4_t{Sr[ct][it][0] * g4.x, Sr[ct][it][1] * g4.y, Sr[ct][it][2] * g4.z,
-                                  Sr[ct][it][3] * g4.w};
-#pragma unroll
-            for (int kb = 0; kb < NB / 2; ++kb) {
-                const F8 a = lds_frag8<BF16>(tKbT(B) + 16 * it * LDC + 32 * kb, LDC, lane);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], a, u_frag8(ct, 2 * kb));
-            }
-            if constexpr (NB & 1) {
-                const F4 a = lds_frag4<BF16>(tKbT(B) + 16 * it * LDC + 16 * (NB - 1), LDC, lane);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc[ct] = mma4<BF16>(acc[ct], a, uf[ct][NB - 1]);
-            }
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) Sr[ct][it] = acc[ct];
-        }
-    };
-    // coalesced store of the chunk's outputs
-    auto store_O = [&](int c0, int len) __attribute__((always_inline)) {
-        for (int idx = tid; idx < len * (BV / 4); idx += NT) {
-            const int r = idx / (BV / 4);
-            const int cq = idx % (BV / 4);
-            G* dst = oh + (c0 + r) * strideV + 4 * cq;
-            if constexpr (BF16) {
-                *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(tO + r * LDV + 4 * cq);
-            } else {
-                *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(tO + r * LDV + 4 * cq);
+                for (int j = 0; j < 4; ++j) S_T[(pair * DK + 16 * it + 4 * lg + j) * dv + col] = Sr[ct][it][j];
             }
         }
-    };
-    auto chunk_len = [&](int i) __attribute__((always_inline)) { return min(C, t_end - (t_beg + i * C)); };
+    } else if (wave < NC + NP) {
+        // =====================================================================
+        // producer: raw loads, decay prefix and decayed operand tiles
+        // =====================================================================
+        // Lane geometry: lane = cq * NRG + rg owns rows 4 rg .. 4 rg + 3 and
+        // key channels i0 .. i0 + 3 of this wave's channel strip.
+        const int pw = wave - NC;
+        const int rg = lane % NRG;
+        const int cq = lane / NRG;
+        const int gq = pw * QW + cq;
+        const bool qok = NQ >= QW || gq < NQ;  // idle lanes only when d_k < one strip
+        const int i0 = 4 * min(gq, NQ - 1);
+        const int vlane = pw * 64 + lane;
+        const G* const qh = q + static_cast<size_t>(h) * DK;
+        const G* const kh = k + static_cast<size_t>(h) * DK;
+        const float* const lah = log_alpha + static_cast<size_t>(h) * DK;
+        const float* const bh = beta + h;
+        const G* const vh = v + static_cast<size_t>(h) * dv + j0;
 
-    // ---- prologue: prep 1-3 of chunk 0 ---------------------------------------
-    __syncthreads();  // zeroed L / A_qk tiles
-    if (nchunks > 0) {
-        load_chunk(t_beg, chunk_len(0));
-        prep1(0, chunk_len(0));
-        __syncthreads();
-        prep2(0, chunk_len(0));
-        if (nchunks > 1) load_chunk(t_beg + C, chunk_len(1));
-        __syncthreads();
-        prep3(0);
-        __syncthreads();
-    }
+        // Raw inputs of the next chunk, loaded right after the current
+        // chunk's prep consumed the registers.  Rows past the end of the
+        // sequence read as zero (buffer range check), so padded rows need no
+        // masking anywhere.
+        constexpr int GS = static_cast<int>(sizeof(G));
+        const int rowK = strideK * GS;  // bytes per token row of q and k
+        const int rowLA = strideK * 4;
+        const int rowV = strideV * GS;
+        const int rowB = H * 4;
+        const int offK = 4 * rg * rowK + i0 * GS;
+        const int offLA = 4 * rg * rowLA + i0 * 4;
+        const int offB = 4 * rg * rowB;
+        float4 rla[4];
+        R4 rk[4], rq[4], rv[VPT][4];
+        float rb[4];
+        auto load_chunk = [&](int c0, int len) __attribute__((always_inline)) {
+            const size_t tok = static_cast<size_t>(c0) * strideK;
+            const auto bK = buffer_rsrc(kh + tok, len * rowK);
+            const auto bQ = buffer_rsrc(qh + tok, len * rowK);
+            const auto bLA = buffer_rsrc(lah + tok, len * rowLA);
+            const auto bB = buffer_rsrc(bh + static_cast<size_t>(c0) * H, len * rowB);
+            const auto bV = buffer_rsrc(vh + static_cast<size_t>(c0) * strideV, len * rowV);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                rla[rr] = buf_load_f4(bLA, offLA, rr * rowLA);
+                rk[rr] = buf_load_raw4<BF16>(bK, offK, rr * rowK);
+                rq[rr] = buf_load_raw4<BF16>(bQ, offK, rr * rowK);
+                rb[rr] = buf_load_f1(bB, offB, rr * rowB);
+            }
+#pragma unroll
+            for (int vv = 0; vv < VPT; ++vv) {
+                const int idx = vlane + 64 * NP * vv;
+                if (VITEMS % (64 * NP) == 0 || idx < VITEMS) {
+                    const int r0 = 4 * (idx % (C / 4));
+                    const int c4 = 4 * (idx / (C / 4));
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) rv[vv][rr] = buf_load_raw4<BF16>(bV, r0 * rowV + c4 * GS, rr * rowV);
+                }
+            }
+        };
 
-    // ---- steady state: chunk i in buffer i & 1, prep of chunk i+1 in the other
-    for (int i = 0; i < nchunks; ++i) {
-        const int B = i & 1;
-        const bool has_next = i + 1 < nchunks;
-        const int len1 = has_next ? chunk_len(i + 1) : 0;
-        // stage X
-        if (has_next) prep1(1 - B, len1);
-        chain_R(B);
-        __syncthreads();
-        // stage Y
-        if (has_next) {
-            prep2(1 - B, len1);
-            if (i + 2 < nchunks) load_chunk(t_beg + (i + 2) * C, chunk_len(i + 2));
-        }
-        chain_UO(B);
-        __syncthreads();
-        // stage Z
-        if (has_next) prep3(1 - B);
-        chain_S(B);
-        store_O(t_beg + i * C, chunk_len(i));
-        __syncthreads();
-    }
+        // beta, V^T, cumulative decay and the decayed operand tiles of buffer S
+        auto prep12 = [&](int S) __attribute__((always_inline)) {
+            if (pw == 0 && cq == 0)
+                *reinterpret_cast<float4*>(sBeta(S) + 4 * rg) = make_float4(rb[0], rb[1], rb[2], rb[3]);
+#pragma unroll
+            for (int vv = 0; vv < VPT; ++vv) {
+                const int idx = vlane + 64 * NP * vv;
+                if (VITEMS % (64 * NP) == 0 || idx < VITEMS) {
+                    const int r0 = 4 * (idx % (C / 4));
+                    const int c4 = 4 * (idx / (C / 4));
+                    R4 cols[4];
+                    transpose4<BF16>(rv[vv], cols);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) T::lds_put_raw4(tVt(S) + (c4 + c) * LDC + r0, cols[c]);
+                }
+            }
+            if (!qok) return;
+            // log alpha in log2 units; group sums, then an inclusive prefix
+            // over the NRG row groups (consecutive lanes), in a fixed order.
+            float la[4][4], tot[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                la[rr][0] = rla[rr].x;
+                la[rr][1] = rla[rr].y;
+                la[rr][2] = rla[rr].z;
+                la[rr][3] = rla[rr].w;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) tot[c] = ((la[0][c] + la[1][c]) + (la[2][c] + la[3][c])) * kLog2e;
+            float g[4], Gc[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                // Hillis-Steele over segments of NRG lanes; each DPP move runs
+                // on all lanes, the segment boundary is applied afterwards.
+                float x = tot[c];
+                const float s1 = row_shr<1>(x);
+                x += (rg >= 1) ? s1 : 0.f;
+                const float s2 = row_shr<2>(x);
+                x += (rg >= 2) ? s2 : 0.f;
+                if constexpr (NRG > 4) {
+                    const float s4 = row_shr<4>(x);
+                    x += (rg >= 4) ? s4 : 0.f;
+                }
+                const float ex = row_shr<1>(x);
+                g[c] = (rg >= 1) ? ex : 0.f;  // sum of the groups before this one
+                Gc[c] = __builtin_amdgcn_exp2f(__shfl(x, (lane & ~(NRG - 1)) + NRG - 1));
+            }
+            if (rg == 0) *reinterpret_cast<float4*>(sGC(S) + i0) = make_float4(Gc[0], Gc[1], Gc[2], Gc[3]);
+            float kbar[4][4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = 4 * rg + rr;
+                float kk[4], qq[4];
+                T::unpack4(rk[rr], kk);
+                T::unpack4(rq[rr], qq);
+                const float b = rb[rr];
+                float gam[4], kh4[4], bk[4], qg[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    // exp(+-g) as 2^(+-g2): one v_exp_f32 each; |g| stays within
+                    // the numerical contract, where results are normal.
+                    g[c] = __builtin_fmaf(la[rr][c], kLog2e, g[c]);
+                    gam[c] = __builtin_amdgcn_exp2f(g[c]);
+                    kh4[c] = kk[c] * __builtin_amdgcn_exp2f(-g[c]);
+                    kbar[rr][c] = kh4[c] * Gc[c];
+                    bk[c] = (b * kk[c]) * gam[c];
+                    qg[c] = qq[c] * gam[c];
+                }
+                lds_store4<BF16>(tKb(S) + r * LDK + i0, bk[0], bk[1], bk[2], bk[3]);
+                lds_store4<BF16>(tKh(S) + r * LDK + i0, kh4[0], kh4[1], kh4[2], kh4[3]);
+                lds_store4<BF16>(tQ(S) + r * LDK + i0, qg[0], qg[1], qg[2], qg[3]);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                lds_store4<BF16>(tKbT(S) + (i0 + c) * LDC + 4 * rg, kbar[0][c], kbar[1][c], kbar[2][c],
+                                 kbar[3][c]);
+        };
 
-    // ---- final state --------------------------------------------------------
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-        const size_t col = static_cast<size_t>(j0 + col0(ct) + ln);
-#pragma unroll
-        for (int it = 0; it < DK / 16; ++it) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) S_T[(pair * DK + 16 * it + 4 * lg + j) * dv + col] = Sr[ct][it][j];
+        // Chunk m in buffer m & 1.  The raw registers have a single
+        // loop-carried definition (loaded after prep, read by the next prep),
+        // so the loads stay in flight across the hand-offs.
+        if (nchunks > 0) load_chunk(t_beg, chunk_len(0));
+        for (int m = 0; m < nchunks; ++m) {
+            // buffer m & 1 last held chunk m - 2: wait until every consumer released it
+            if (m >= 2) ctr_wait(nFree, NC * (m - 1), fault);
+            prep12(m & 1);
+            ctr_signal(nPrep, lane);
+            if (m + 1 < nchunks) load_chunk(t_beg + (m + 1) * C, chunk_len(m + 1));
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Host launchers.  The workgroup shape follows the value slice width
-// BV = d_v / v_split: 4 waves x 2 tiles (128), 4 x 1 (64), 2 x 1 (32), 1 x 1 (16).
+// Host launchers.  Consumer waves follow the value slice width
+// BV = d_v / v_split: 4 waves x 2 tiles (128), 4 x 1 (64), 2 x 1 (32),
+// 1 x 1 (16); producer waves follow d_k.
 // ---------------------------------------------------------------------------
-template <bool BF16, int DK, int NW, int CT>
+template <bool BF16, int DK, int NC, int CT>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
     using G = typename Elem<BF16>::G;
+    using Sh = PrefillShape<BF16, DK, NC, CT>;
     const unsigned grid = static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H) *
                           static_cast<unsigned>(a.v_split);
-    hipLaunchKernelGGL((prefill_kernel<BF16, DK, NW, CT>), dim3(grid), dim3(64 * NW), 0,
+    hipLaunchKernelGGL((prefill_kernel<BF16, DK, NC, CT>), dim3(grid), dim3(Sh::NT), 0,
                        static_cast<hipStream_t>(a.stream), static_cast<const G*>(a.q),
                        static_cast<const G*>(a.k), static_cast<const G*>(a.v), a.log_alpha, a.beta,
                        a.S0, a.cu_seqlens, a.N, a.H, a.d_v, a.v_split, static_cast<G*>(a.o), a.S_T);
