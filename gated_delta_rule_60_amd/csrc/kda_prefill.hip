@@ -28,24 +28,24 @@
 // walks its sequence chunk by chunk.  Its waves have two roles:
 //   * consumer waves (NC of them) carry the state.  Each owns CT 16-column
 //     tiles of S for the whole sequence, in fp32 registers (MFMA C layout);
-//     the columns of S evolve independently.  Per chunk the consumers first
-//     share the S-independent MFMA work (the Gram products L and A_qk and the
-//     diagonal-block inverses, one job per wave), meet at an LDS counter,
-//     then each forms R, U, O and the next S of its columns with MFMA and
-//     writes its O columns straight from registers.
-//   * producer waves (NP of them) do the vector-ALU part of the prep, one
-//     chunk ahead, into double-buffered LDS tiles: global loads (issued a
+//     the columns of S evolve independently.  The consumers also share the
+//     S-independent MFMA work of the chunk (the Gram products L and A_qk and
+//     the diagonal-block inverses, one job per wave): the jobs of chunk i+1
+//     are computed alongside the recurrence of chunk i (R, U, O and the next
+//     S of the wave's columns) and published through an LDS counter.  O is
+//     written straight from registers.
+//   * producer waves (NP of them) do the vector-ALU part of the prep into
+//     LDS tiles that rotate through three slots: global loads (issued a
 //     chunk ahead), the per-channel cumulative decay (a wave-local prefix
 //     scan: each producer wave owns a strip of key channels for all rows),
 //     the decayed operand tiles and V^T.
 // The roles meet only at monotonic counters in LDS (tiles ready, jobs done,
-// buffer released), so the producers' prep of chunk i+1 runs at the same time
-// as the consumers' recurrence of chunk i on every SIMD.
+// slot released), so the producers' prep of chunks i+1 and i+2 runs at the
+// same time as the consumers' recurrence of chunk i on every SIMD.
 //
-// Only consumer waves issue MFMAs, one consumer per SIMD, and a CU holds one
-// workgroup: on gfx950 a VALU read of an MFMA result a few instructions after
-// the MFMA was observed to see stale accumulators when MFMAs of another wave
-// shared the SIMD's matrix pipe, even with the compiler's wait states.
+// Only consumer waves issue MFMAs (one per SIMD) and only producer waves do
+// the transcendental-heavy vector work, so the two roles mostly use
+// different execution units of a SIMD.
 // All MFMA operands are bf16 (or fp32 for f32 inputs); accumulation and the
 // carried state are fp32.
 #include <type_traits>
@@ -72,14 +72,19 @@ constexpr size_t kLdsBudget = 160 * 1024;
 template <int V>
 using ic = std::integral_constant<int, V>;
 
-// Two buffers of per-chunk tiles plus the workgroup's bookkeeping.  Buffer b
-// starts at b * BUF.
+// Per-chunk tiles in LDS.  The producers' tiles (decayed operands, V^T,
+// Gamma_C, beta) rotate through three slots, so the producers can run two
+// chunks ahead of the recurrence (the consumers read chunk i+1's tiles for
+// its Gram products while they run chunk i); the consumers' job results
+// (L, A_qk, -T_bb) alternate between two buffers.  Slot s starts at
+// s * PBUF, job buffer b at OFF_JOB + b * JBUF.
 template <bool BF16, int DK, int NC, int CT, int C_>
 struct Layout {
     using E = typename Elem<BF16>::E;
     static constexpr int C = C_;
     static constexpr int NB = C / 16;
     static constexpr int BV = 16 * CT * NC;
+    static constexpr int NSLOT = 3;
     static constexpr int PAD = 16 / static_cast<int>(sizeof(E));  // 16 bytes of row padding
     static constexpr int LDK = DK + PAD;
     static constexpr int LDC = C + PAD;
@@ -87,28 +92,29 @@ struct Layout {
     static constexpr size_t ES = sizeof(E);
     static constexpr size_t SZ_KB = align16(C * LDK * ES);      // beta K~, Q~, K^  [C][LDK]
     static constexpr size_t SZ_KBT = align16(DK * LDC * ES);    // Kbar^T           [DK][LDC]
-    static constexpr size_t SZ_L = align16(C * LDC * ES);       // L, A_qk          [C][LDC]
-    static constexpr size_t SZ_T = align16(NB * 16 * LDT * ES);  // -T_bb           [NB][16][LDT]
     static constexpr size_t SZ_VT = align16(BV * LDC * ES);     // V^T              [BV][LDC]
     static constexpr size_t SZ_GC = align16(DK * 4);            // Gamma_C          [DK]
     static constexpr size_t SZ_BETA = align16(C * 4);           // beta             [C]
+    static constexpr size_t SZ_L = align16(C * LDC * ES);       // L, A_qk          [C][LDC]
+    static constexpr size_t SZ_T = align16(NB * 16 * LDT * ES);  // -T_bb           [NB][16][LDT]
+    // producer slot
     static constexpr size_t O_KB = 0;
     static constexpr size_t O_Q = O_KB + SZ_KB;
     static constexpr size_t O_KH = O_Q + SZ_KB;
     static constexpr size_t O_KBT = O_KH + SZ_KB;
-    static constexpr size_t O_L = O_KBT + SZ_KBT;
-    static constexpr size_t O_A = O_L + SZ_L;
-    static constexpr size_t O_T = O_A + SZ_L;
-    static constexpr size_t O_VT = O_T + SZ_T;
+    static constexpr size_t O_VT = O_KBT + SZ_KBT;
     static constexpr size_t O_GC = O_VT + SZ_VT;
     static constexpr size_t O_BETA = O_GC + SZ_GC;
-    static constexpr size_t BUF = O_BETA + SZ_BETA;
-    static constexpr size_t OFF_SEQ = 2 * BUF;
+    static constexpr size_t PBUF = O_BETA + SZ_BETA;
+    // job buffer
+    static constexpr size_t OFF_JOB = NSLOT * PBUF;
+    static constexpr size_t O_L = 0;
+    static constexpr size_t O_A = O_L + SZ_L;
+    static constexpr size_t O_T = O_A + SZ_L;
+    static constexpr size_t JBUF = O_T + SZ_T;
+    static constexpr size_t OFF_SEQ = OFF_JOB + 2 * JBUF;
     static constexpr size_t OFF_CTR = OFF_SEQ + align16((kSortMax + 1) * 4);
-    static constexpr size_t BYTES = OFF_CTR + 32;
-    // Allocation: more than half of a CU's LDS, so that a CU never holds two
-    // workgroups (each SIMD then runs the MFMAs of one consumer wave only).
-    static constexpr size_t ALLOC = BYTES > kLdsBudget / 2 + 16 ? BYTES : kLdsBudget / 2 + 16;
+    static constexpr size_t BYTES = OFF_CTR + 64;
 };
 
 // The chunk length depends only on the storage type and d_k (sized for the
@@ -209,6 +215,20 @@ __device__ __forceinline__ float buf_load_f1(__amdgpu_buffer_rsrc_t r, int voff,
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// four fp32 values as four consecutive storage elements (bf16: round to
+// nearest even)
+template <bool BF16>
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, int voff, const f32x4_t& x) {
+    if constexpr (BF16) {
+        bf16x4_t h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = static_cast<__bf16>(x[j]);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, h), r, voff, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), r, voff, 0, 0);
+    }
+}
+
 // four consecutive storage elements, raw
 template <bool BF16>
 __device__ __forceinline__ typename Elem<BF16>::R4 buf_load_raw4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
@@ -229,7 +249,10 @@ __device__ __forceinline__ float row_shr(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + D, 0xF, 0xF, true));
 }
 
-// Inter-wave hand-off through monotonic counters in LDS.  signal: once this
+// Inter-wave hand-off through monotonic counters in LDS.  A counter is
+// either a sum (every wave of a group adds one per chunk: only sound among
+// waves that cannot run a whole chunk ahead of one another) or one wave's
+// own progress (it stores the number of chunks it has completed).  signal: once this
 // wave's earlier LDS reads and writes have completed, add one.  wait: spin
 // until the counter reaches target.  LDS accesses of one wave are performed
 // in order, so data written before a signal is visible after the wait.
@@ -246,6 +269,12 @@ __device__ __forceinline__ void ctr_signal(int* ctr, int lane) {
 // write NaN final states, which no caller can mistake for a result.
 constexpr int kSpinMax = 1 << 24;
 
+__device__ __forceinline__ void ctr_publish(int* ctr, int value, int lane) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) __hip_atomic_store(ctr, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void ctr_wait(int* ctr, int target, int* fault) {
     int spins = 0;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
@@ -256,6 +285,11 @@ __device__ __forceinline__ void ctr_wait(int* ctr, int target, int* fault) {
         __builtin_amdgcn_s_sleep(1);
     }
     asm volatile("" ::: "memory");
+}
+
+// Waits until each of n progress counters has reached target.
+__device__ __forceinline__ void ctr_wait_each(int* ctrs, int n, int target, int* fault) {
+    for (int w = 0; w < n; ++w) ctr_wait(ctrs + w, target, fault);
 }
 
 }  // namespace
@@ -280,27 +314,32 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
     constexpr int KB = DK / 32;  // 32-deep k blocks over key channels
     constexpr int NRG = Sh::NRG, QW = Sh::QW, NQ = Sh::NQ, VPT = Sh::VPT, VITEMS = Sh::VITEMS;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Sh::ALLOC];
-#define KDA_TILE(name, type, off) \
-    auto name = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<type*>(smem + b * Sh::BUF + (off)); }
-    KDA_TILE(tKb, E, Sh::O_KB);
-    KDA_TILE(tQ, E, Sh::O_Q);
-    KDA_TILE(tKh, E, Sh::O_KH);
-    KDA_TILE(tKbT, E, Sh::O_KBT);
-    KDA_TILE(tL, E, Sh::O_L);
-    KDA_TILE(tA, E, Sh::O_A);
-    KDA_TILE(tT, E, Sh::O_T);
-    KDA_TILE(tVt, E, Sh::O_VT);
-    KDA_TILE(sGC, float, Sh::O_GC);
-    KDA_TILE(sBeta, float, Sh::O_BETA);
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Sh::BYTES];
+#define KDA_TILE(name, type, base, stride, off) \
+    auto name = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<type*>(smem + (base) + b * (stride) + (off)); }
+    // producer slots 0..2
+    KDA_TILE(tKb, E, 0, Sh::PBUF, Sh::O_KB);
+    KDA_TILE(tQ, E, 0, Sh::PBUF, Sh::O_Q);
+    KDA_TILE(tKh, E, 0, Sh::PBUF, Sh::O_KH);
+    KDA_TILE(tKbT, E, 0, Sh::PBUF, Sh::O_KBT);
+    KDA_TILE(tVt, E, 0, Sh::PBUF, Sh::O_VT);
+    KDA_TILE(sGC, float, 0, Sh::PBUF, Sh::O_GC);
+    KDA_TILE(sBeta, float, 0, Sh::PBUF, Sh::O_BETA);
+    // job buffers 0..1
+    KDA_TILE(tL, E, Sh::OFF_JOB, Sh::JBUF, Sh::O_L);
+    KDA_TILE(tA, E, Sh::OFF_JOB, Sh::JBUF, Sh::O_A);
+    KDA_TILE(tT, E, Sh::OFF_JOB, Sh::JBUF, Sh::O_T);
 #undef KDA_TILE
     int* const sSeq = reinterpret_cast<int*>(smem + Sh::OFF_SEQ);
     // Monotonic counters, one signal per wave per chunk:
     int* const ctr = reinterpret_cast<int*>(smem + Sh::OFF_CTR);
-    int* const nPrep = ctr + 0;    // producers: decayed tiles written
-    int* const nSolved = ctr + 1;  // consumers: their L, A_qk, -T_bb jobs written
-    int* const nFree = ctr + 2;    // consumers: buffer of the chunk released
-    int* const fault = ctr + 3;    // a bounded wait gave up
+    // Sum counters are only used among consumer waves, which bound one
+    // another at every chunk; producers never wait for one another, so each
+    // producer wave reports its own progress.
+    int* const nSolved = ctr + 0;   // consumers: their L, A_qk, -T_bb jobs written
+    int* const nFree = ctr + 1;     // consumers: producer slot of the chunk released
+    int* const fault = ctr + 2;     // a bounded wait gave up
+    int* const prodDone = ctr + 4;  // [NP] chunks completed by each producer wave
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -364,7 +403,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
             tA(b)[idx] = T::to_e(0.f);
         }
     }
-    if (tid < 4) ctr[tid] = 0;
+    if (tid < 16) ctr[tid] = 0;
     __syncthreads();
 
     // Issue priority follows the critical path: the consumers' recurrence is
@@ -375,6 +414,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         // =====================================================================
         __builtin_amdgcn_s_setprio(3);
         G* const oh = o + static_cast<size_t>(h) * dv + j0;
+        constexpr int GS = static_cast<int>(sizeof(G));
         auto col0 = [&](int ct) __attribute__((always_inline)) { return 16 * (CT * wave + ct); };
         // Sr[ct][it][j] = S[16 it + 4 lg + j][col]
         f32x4_t Sr[CT][DK / 16];
@@ -402,74 +442,83 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         // C-layout tile already held: the A operand of X is the C layout of
         // X^T, the B operand of X is the C layout of X.  Both layouts of N
         // come from the Gram MFMAs (P and P^T).
-        auto prep3 = [&](int S) __attribute__((always_inline)) {
-            for (int job = wave; job < Sh::NJOB; job += NC) {
-                int st, rt;
-                if (job < NB) {
-                    st = rt = job;
-                } else {
-                    int tix = job - NB;  // enumerate st < rt
-                    rt = 1;
-                    while (tix >= rt) {
-                        tix -= rt;
-                        ++rt;
-                    }
-                    st = tix;
-                }
-                const bool diag = st == rt;
-                const E* Ab = tKh(S) + 16 * st * LDK;
-                const E* Bk = tKb(S) + 16 * rt * LDK;
-                const E* Bq = tQ(S) + 16 * rt * LDK;
-                f32x4_t accL = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f}, accN = {0.f, 0.f, 0.f, 0.f};
+        //
+        // Results of one job, kept in registers until they are stored.
+        struct Job {
+            f32x4_t l, a, t;  // L and A_qk values of the block; -T_bb (diagonal jobs)
+        };
+        static_assert(NB <= 2, "job table covers chunks of up to two 16-row blocks");
+        constexpr int NJOB = Sh::NJOB;
+        constexpr int JPW = (NJOB + NC - 1) / NC;  // jobs per consumer wave
+        // job -> block: 0 -> (0,0), 1 -> (1,1), 2 -> (st 0, rt 1); jobs past the
+        // last one compute the last job again and are never stored.
+        auto job_of = [&](int t) __attribute__((always_inline)) { return wave + NC * t; };
+        auto job_st = [&](int jc) __attribute__((always_inline)) { return jc == 2 ? 0 : jc; };
+        auto job_rt = [&](int jc) __attribute__((always_inline)) { return jc == 2 ? 1 : jc; };
+        // Straight-line (no branches), so that it interleaves with the recurrence.
+        auto prep3_compute = [&](int S, int t) __attribute__((always_inline)) {  // S: producer slot
+            const int jc = min(job_of(t), NJOB - 1);
+            const int st = job_st(jc), rt = job_rt(jc);
+            const E* Ab = tKh(S) + 16 * st * LDK;
+            const E* Bk = tKb(S) + 16 * rt * LDK;
+            const E* Bq = tQ(S) + 16 * rt * LDK;
+            f32x4_t accL = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f}, accN = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const F8 a = lds_frag8<BF16>(Ab + 32 * kb, LDK, lane);
-                    const F8 bk = lds_frag8<BF16>(Bk + 32 * kb, LDK, lane);
-                    accL = mma8<BF16>(accL, a, bk);
-                    accA = mma8<BF16>(accA, a, lds_frag8<BF16>(Bq + 32 * kb, LDK, lane));
-                    if (diag) accN = mma8<BF16>(accN, bk, a);  // P^T: C layout of N
-                }
+            for (int kb = 0; kb < KB; ++kb) {
+                const F8 a = lds_frag8<BF16>(Ab + 32 * kb, LDK, lane);
+                const F8 bk = lds_frag8<BF16>(Bk + 32 * kb, LDK, lane);
+                accL = mma8<BF16>(accL, a, bk);
+                accA = mma8<BF16>(accA, a, lds_frag8<BF16>(Bq + 32 * kb, LDK, lane));
+                accN = mma8<BF16>(accN, bk, a);  // P^T: C layout of N (used by diagonal jobs)
+            }
+            Job res;
+            const int r = 16 * rt + ln;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int s2 = 16 * st + 4 * lg + j;
+                res.l[j] = (s2 < r) ? accL[j] : 0.f;
+                res.a[j] = (s2 <= r) ? accA[j] : 0.f;
+            }
+            // C layout: lane (ln, lg), value j is element (row 4 lg + j, col ln).
+            f32x4_t Nt, Nc;  // C layouts of N^T and N (strictly lower N)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                Nt[j] = res.l[j];
+                Nc[j] = (ln < 4 * lg + j) ? accN[j] : 0.f;
+            }
+            auto eye = [&](f32x4_t x, float sgn) __attribute__((always_inline)) {
+                f32x4_t y;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) y[j] = sgn * x[j] + ((4 * lg + j == ln) ? 1.f : 0.f);
+                return y;
+            };
+            auto f4 = [&](const f32x4_t& x) __attribute__((always_inline)) { return acc_frag4<BF16>(x); };
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            // depth 1
+            const f32x4_t N2 = mma4<BF16>(z, f4(Nt), f4(Nc));
+            const f32x4_t N2t = mma4<BF16>(z, f4(Nc), f4(Nt));
+            // depth 2: P1 = (I - N)(I + N^2)
+            const f32x4_t P1 = mma4<BF16>(z, f4(eye(Nt, -1.f)), f4(eye(N2, 1.f)));
+            const f32x4_t N4 = mma4<BF16>(z, f4(N2t), f4(N2));
+            const f32x4_t N4t = mma4<BF16>(z, f4(N2), f4(N2t));
+            // depth 3: P2 = (I + N^4) P1, and (N^8)^T
+            const f32x4_t P2 = mma4<BF16>(z, f4(eye(N4t, 1.f)), f4(P1));
+            const f32x4_t N8t = mma4<BF16>(z, f4(N4), f4(N4t));
+            // depth 4: T^T = P2^T (I + N^8)^T
+            const f32x4_t Tt = mma4<BF16>(z, f4(P2), f4(eye(N8t, 1.f)));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) res.t[j] = -Tt[j];
+            return res;
+        };
+        auto prep3_store = [&](int S, int t, const Job& res) __attribute__((always_inline)) {  // S: job buffer
+            const int job = job_of(t);
+            if (job < NJOB) {
+                const int st = job_st(job), rt = job_rt(job);
                 const int r = 16 * rt + ln;
-                float vl[4], va[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int s2 = 16 * st + 4 * lg + j;
-                    vl[j] = (s2 < r) ? accL[j] : 0.f;
-                    va[j] = (s2 <= r) ? accA[j] : 0.f;
-                }
-                lds_store4<BF16>(tL(S) + r * LDC + 16 * st + 4 * lg, vl[0], vl[1], vl[2], vl[3]);
-                lds_store4<BF16>(tA(S) + r * LDC + 16 * st + 4 * lg, va[0], va[1], va[2], va[3]);
-                if (diag) {
-                    // C layout: lane (ln, lg), value j is element (row 4 lg + j, col ln).
-                    f32x4_t Nt, Nc;  // C layouts of N^T and N (strictly lower N)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        Nt[j] = vl[j];
-                        Nc[j] = (ln < 4 * lg + j) ? accN[j] : 0.f;
-                    }
-                    auto eye = [&](f32x4_t x, float sgn) __attribute__((always_inline)) {
-                        f32x4_t y;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) y[j] = sgn * x[j] + ((4 * lg + j == ln) ? 1.f : 0.f);
-                        return y;
-                    };
-                    auto f4 = [&](const f32x4_t& x) __attribute__((always_inline)) { return acc_frag4<BF16>(x); };
-                    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-                    // depth 1
-                    const f32x4_t N2 = mma4<BF16>(z, f4(Nt), f4(Nc));
-                    const f32x4_t N2t = mma4<BF16>(z, f4(Nc), f4(Nt));
-                    // depth 2: P1 = (I - N)(I + N^2)
-                    const f32x4_t P1 = mma4<BF16>(z, f4(eye(Nt, -1.f)), f4(eye(N2, 1.f)));
-                    const f32x4_t N4 = mma4<BF16>(z, f4(N2t), f4(N2));
-                    const f32x4_t N4t = mma4<BF16>(z, f4(N2), f4(N2t));
-                    // depth 3: P2 = (I + N^4) P1, and (N^8)^T
-                    const f32x4_t P2 = mma4<BF16>(z, f4(eye(N4t, 1.f)), f4(P1));
-                    const f32x4_t N8t = mma4<BF16>(z, f4(N4), f4(N4t));
-                    // depth 4: T^T = P2^T (I + N^8)^T
-                    const f32x4_t Tt = mma4<BF16>(z, f4(P2), f4(eye(N8t, 1.f)));
-                    // lane (ln, lg) holds T[ln][4 lg + j]: store -T row-major
-                    lds_store4<BF16>(tT(S) + (rt * 16 + ln) * LDT + 4 * lg, -Tt[0], -Tt[1], -Tt[2], -Tt[3]);
-                }
+                lds_store4<BF16>(tL(S) + r * LDC + 16 * st + 4 * lg, res.l[0], res.l[1], res.l[2], res.l[3]);
+                lds_store4<BF16>(tA(S) + r * LDC + 16 * st + 4 * lg, res.a[0], res.a[1], res.a[2], res.a[3]);
+                // lane (ln, lg) holds T[ln][4 lg + j]: -T row-major
+                if (st == rt) lds_store4<BF16>(tT(S) + r * LDT + 4 * lg, res.t[0], res.t[1], res.t[2], res.t[3]);
             }
         };
 
@@ -507,7 +556,8 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         // U_b = (-T_bb) (R'_b + sum_{c<b} L_bc U_c);  then O^T = S^T Q~^T + U^T A_qk^T,
         // written to global memory from the C layout: lane (ln, lg) holds
         // four consecutive value columns of token row 16 rt + ln.
-        auto chain_UO = [&](int B, int c0, int len) __attribute__((always_inline)) {
+        auto chain_UO = [&](int B, int J, int c0, int len) __attribute__((always_inline)) {
+            const auto bO = buffer_rsrc(oh + static_cast<size_t>(c0) * strideV, len * strideV * GS);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 f32x4_t Y[CT];
@@ -515,16 +565,16 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                 for (int ct = 0; ct < CT; ++ct) Y[ct] = Rp[ct][b];
 #pragma unroll
                 for (int kp = 0; kp + 1 < b; kp += 2) {
-                    const F8 a = lds_frag8<BF16>(tL(B) + 16 * b * LDC + 16 * kp, LDC, lane);
+                    const F8 a = lds_frag8<BF16>(tL(J) + 16 * b * LDC + 16 * kp, LDC, lane);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) Y[ct] = mma8<BF16>(Y[ct], a, u_frag8(ct, kp));
                 }
                 if (b & 1) {
-                    const F4 a = lds_frag4<BF16>(tL(B) + 16 * b * LDC + 16 * (b - 1), LDC, lane);
+                    const F4 a = lds_frag4<BF16>(tL(J) + 16 * b * LDC + 16 * (b - 1), LDC, lane);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) Y[ct] = mma4<BF16>(Y[ct], a, uf[ct][b - 1]);
                 }
-                const F4 tb = lds_frag4<BF16>(tT(B) + 16 * b * LDT, LDT, lane);
+                const F4 tb = lds_frag4<BF16>(tT(J) + 16 * b * LDT, LDT, lane);
                 const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) U[ct][b] = mma4<BF16>(z, tb, acc_frag4<BF16>(Y[ct]));
@@ -544,23 +594,19 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                 }
 #pragma unroll
                 for (int sp = 0; sp + 1 <= rt; sp += 2) {
-                    const F8 ba = lds_frag8<BF16>(tA(B) + 16 * rt * LDC + 16 * sp, LDC, lane);
+                    const F8 ba = lds_frag8<BF16>(tA(J) + 16 * rt * LDC + 16 * sp, LDC, lane);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], u_frag8(ct, sp), ba);
                 }
                 if (!(rt & 1)) {
-                    const F4 ba = lds_frag4<BF16>(tA(B) + 16 * rt * LDC + 16 * rt, LDC, lane);
+                    const F4 ba = lds_frag4<BF16>(tA(J) + 16 * rt * LDC + 16 * rt, LDC, lane);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) acc[ct] = mma4<BF16>(acc[ct], uf[ct][rt], ba);
                 }
-                const int r = 16 * rt + ln;
-                if (r < len) {
+                // rows past the end of the sequence fall outside bO and are dropped
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) {
-                        const float x[4] = {acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]};
-                        T::store4(oh + (c0 + r) * strideV + col0(ct) + 4 * lg, x);
-                    }
-                }
+                for (int ct = 0; ct < CT; ++ct)
+                    buf_store4<BF16>(bO, ((16 * rt + ln) * strideV + col0(ct) + 4 * lg) * GS, acc[ct]);
             }
         };
         // S <- Diag(Gamma_C) S + Kbar^T U
@@ -589,16 +635,39 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
             }
         };
 
-        for (int i = 0; i < nchunks; ++i) {
-            const int B = i & 1;
-            ctr_wait(nPrep, NP * (i + 1), fault);
-            prep3(B);
+        // Software pipeline: the jobs of chunk i+1 are computed in registers
+        // alongside the recurrence of chunk i (from the next producer slot)
+        // and stored after it.  On the last chunk they run on stale tiles and
+        // are not stored.  Chunk i: producer slot P = i mod 3, job buffer i & 1.
+        Job jobs[JPW];
+        if (nchunks > 0) {
+            ctr_wait_each(prodDone, NP, 1, fault);
+#pragma unroll
+            for (int t = 0; t < JPW; ++t) {
+                jobs[t] = prep3_compute(0, t);
+                prep3_store(0, t, jobs[t]);
+            }
             ctr_signal(nSolved, lane);
-            ctr_wait(nSolved, NC * (i + 1), fault);
-            chain_R(B);
-            chain_UO(B, t_beg + i * C, chunk_len(i));
-            chain_S(B);
+        }
+        int P = 0;
+        for (int i = 0; i < nchunks; ++i) {
+            const int J = i & 1;
+            const int Pn = P == 2 ? 0 : P + 1;
+            const bool has_next = i + 1 < nchunks;
+            ctr_wait(nSolved, NC * (i + 1), fault);              // jobs of chunk i stored
+            if (has_next) ctr_wait_each(prodDone, NP, i + 2, fault);  // tiles of chunk i+1 written
+#pragma unroll
+            for (int t = 0; t < JPW; ++t) jobs[t] = prep3_compute(Pn, t);
+            chain_R(P);
+            chain_UO(P, J, t_beg + i * C, chunk_len(i));
+            chain_S(P);
             ctr_signal(nFree, lane);
+            if (has_next) {
+#pragma unroll
+                for (int t = 0; t < JPW; ++t) prep3_store(1 - J, t, jobs[t]);
+                ctr_signal(nSolved, lane);
+            }
+            P = Pn;
         }
 
         // Every wave's last signal follows all of its waits, so a fault
@@ -757,16 +826,18 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                                  kbar[3][c]);
         };
 
-        // Chunk m in buffer m & 1.  The raw registers have a single
-        // loop-carried definition (loaded after prep, read by the next prep),
-        // so the loads stay in flight across the hand-offs.
+        // The raw registers have a single loop-carried definition (loaded
+        // after prep, read by the next prep), so the loads stay in flight
+        // across the hand-offs.
         if (nchunks > 0) load_chunk(t_beg, chunk_len(0));
+        int P = 0;  // slot of chunk m: m mod 3
         for (int m = 0; m < nchunks; ++m) {
-            // buffer m & 1 last held chunk m - 2: wait until every consumer released it
-            if (m >= 2) ctr_wait(nFree, NC * (m - 1), fault);
-            prep12(m & 1);
-            ctr_signal(nPrep, lane);
+            // slot P last held chunk m - 3: wait until every consumer released it
+            if (m >= 3) ctr_wait(nFree, NC * (m - 2), fault);
+            prep12(P);
+            ctr_publish(prodDone + pw, m + 1, lane);
             if (m + 1 < nchunks) load_chunk(t_beg + (m + 1) * C, chunk_len(m + 1));
+            P = P == 2 ? 0 : P + 1;
         }
     }
 }
