@@ -431,7 +431,8 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
 
         // Job (st, rt), st <= rt, computes the tiles at block (rt, st) of
         // L = strictly_lower(beta K~ K^T) and A_qk = lower_incl(Q~ K^T),
-        // sharing the K^ operand.  They are computed transposed,
+        // sharing the K^ operand (the LDS tile holds K~; beta is applied to
+        // the rows of the product).  They are computed transposed,
         // P[s][r] = K^_s . X_r, so that each lane's four C-layout values are
         // four consecutive columns of row r.
         //
@@ -473,18 +474,23 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
             }
             Job res;
             const int r = 16 * rt + ln;
+            // L = strictly_lower(beta K~ K^T): beta of row r, per lane in P,
+            // per value (rows 16 rt + 4 lg + j) in P^T
+            const float br = sBeta(S)[r];
+            const float4 bn = *reinterpret_cast<const float4*>(sBeta(S) + 16 * rt + 4 * lg);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int s2 = 16 * st + 4 * lg + j;
-                res.l[j] = (s2 < r) ? accL[j] : 0.f;
+                res.l[j] = (s2 < r) ? br * accL[j] : 0.f;
                 res.a[j] = (s2 <= r) ? accA[j] : 0.f;
             }
             // C layout: lane (ln, lg), value j is element (row 4 lg + j, col ln).
             f32x4_t Nt, Nc;  // C layouts of N^T and N (strictly lower N)
+            const float bnj[4] = {bn.x, bn.y, bn.z, bn.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 Nt[j] = res.l[j];
-                Nc[j] = (ln < 4 * lg + j) ? accN[j] : 0.f;
+                Nc[j] = (ln < 4 * lg + j) ? bnj[j] * accN[j] : 0.f;
             }
             auto eye = [&](f32x4_t x, float sgn) __attribute__((always_inline)) {
                 f32x4_t y;
@@ -526,7 +532,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         f32x4_t Rp[CT][NB], U[CT][NB];
         F4 uf[CT][NB];
 
-        // R' = beta K~ S - beta V  (= -R)
+        // R' = beta (K~ S - V)  (= -R)
         auto chain_R = [&](int B) __attribute__((always_inline)) {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
@@ -536,11 +542,10 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
             }
 #pragma unroll
             for (int rt = 0; rt < NB; ++rt) {
-                const float4 b4 = *reinterpret_cast<const float4*>(sBeta(B) + 16 * rt + 4 * lg);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
                     const f32x4_t v4 = lds_load4<BF16>(tVt(B) + (col0(ct) + ln) * LDC + 16 * rt + 4 * lg);
-                    Rp[ct][rt] = f32x4_t{-b4.x * v4[0], -b4.y * v4[1], -b4.z * v4[2], -b4.w * v4[3]};
+                    Rp[ct][rt] = f32x4_t{-v4[0], -v4[1], -v4[2], -v4[3]};
                 }
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
@@ -548,6 +553,12 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) Rp[ct][rt] = mma8<BF16>(Rp[ct][rt], a, sf[ct][kb]);
                 }
+                // rows of R' scaled by beta (lane holds rows 16 rt + 4 lg + j)
+                const float4 b4 = *reinterpret_cast<const float4*>(sBeta(B) + 16 * rt + 4 * lg);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    Rp[ct][rt] = f32x4_t{b4.x * Rp[ct][rt][0], b4.y * Rp[ct][rt][1], b4.z * Rp[ct][rt][2],
+                                         b4.w * Rp[ct][rt][3]};
             }
         };
         auto u_frag8 = [&](int ct, int b) __attribute__((always_inline)) {
@@ -707,10 +718,11 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         const float* const bh = beta + h;
         const G* const vh = v + static_cast<size_t>(h) * dv + j0;
 
-        // Raw inputs of the next chunk, loaded right after the current
-        // chunk's prep consumed the registers.  Rows past the end of the
-        // sequence read as zero (buffer range check), so padded rows need no
-        // masking anywhere.
+        // Raw inputs of the next chunk, loaded right after the current chunk's
+        // prep consumed the registers (a single loop-carried definition, so
+        // the loads stay in flight across the hand-offs).  Rows past the end
+        // of the sequence read as zero (buffer range check), so padded rows
+        // need no masking anywhere.
         constexpr int GS = static_cast<int>(sizeof(G));
         const int rowK = strideK * GS;  // bytes per token row of q and k
         const int rowLA = strideK * 4;
@@ -718,24 +730,28 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         const int rowB = H * 4;
         const int offK = 4 * rg * rowK + i0 * GS;
         const int offLA = 4 * rg * rowLA + i0 * 4;
-        const int offB = 4 * rg * rowB;
+        const bool loads_beta = pw == 0 && lane < C;  // beta of row `lane`, for the consumers
         float4 rla[4];
         R4 rk[4], rq[4], rv[VPT][4];
-        float rb[4];
-        auto load_chunk = [&](int c0, int len) __attribute__((always_inline)) {
+        float rbeta = 0.f;
+        struct Rsrc {
+            __amdgpu_buffer_rsrc_t k, q, la, v, b;
+        };
+        auto rsrc_of = [&](int m) __attribute__((always_inline)) {
+            const int c0 = t_beg + m * C;
+            const int len = chunk_len(m);
             const size_t tok = static_cast<size_t>(c0) * strideK;
-            const auto bK = buffer_rsrc(kh + tok, len * rowK);
-            const auto bQ = buffer_rsrc(qh + tok, len * rowK);
-            const auto bLA = buffer_rsrc(lah + tok, len * rowLA);
-            const auto bB = buffer_rsrc(bh + static_cast<size_t>(c0) * H, len * rowB);
-            const auto bV = buffer_rsrc(vh + static_cast<size_t>(c0) * strideV, len * rowV);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                rla[rr] = buf_load_f4(bLA, offLA, rr * rowLA);
-                rk[rr] = buf_load_raw4<BF16>(bK, offK, rr * rowK);
-                rq[rr] = buf_load_raw4<BF16>(bQ, offK, rr * rowK);
-                rb[rr] = buf_load_f1(bB, offB, rr * rowB);
-            }
+            return Rsrc{buffer_rsrc(kh + tok, len * rowK), buffer_rsrc(qh + tok, len * rowK),
+                        buffer_rsrc(lah + tok, len * rowLA),
+                        buffer_rsrc(vh + static_cast<size_t>(c0) * strideV, len * rowV),
+                        buffer_rsrc(bh + static_cast<size_t>(c0) * H, len * rowB)};
+        };
+        auto load_row = [&](const Rsrc& r, int rr) __attribute__((always_inline)) {
+            rla[rr] = buf_load_f4(r.la, offLA, rr * rowLA);
+            rk[rr] = buf_load_raw4<BF16>(r.k, offK, rr * rowK);
+            rq[rr] = buf_load_raw4<BF16>(r.q, offK, rr * rowK);
+        };
+        auto load_v = [&](const Rsrc& r) __attribute__((always_inline)) {
 #pragma unroll
             for (int vv = 0; vv < VPT; ++vv) {
                 const int idx = vlane + 64 * NP * vv;
@@ -743,15 +759,17 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                     const int r0 = 4 * (idx % (C / 4));
                     const int c4 = 4 * (idx / (C / 4));
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) rv[vv][rr] = buf_load_raw4<BF16>(bV, r0 * rowV + c4 * GS, rr * rowV);
+                    for (int rr = 0; rr < 4; ++rr) rv[vv][rr] = buf_load_raw4<BF16>(r.v, r0 * rowV + c4 * GS, rr * rowV);
                 }
             }
         };
+        auto load_beta = [&](const Rsrc& r) __attribute__((always_inline)) {
+            if (loads_beta) rbeta = buf_load_f1(r.b, lane * rowB, 0);
+        };
 
-        // beta, V^T, cumulative decay and the decayed operand tiles of buffer S
+        // beta, V^T, cumulative decay and the decayed operand tiles of slot S
         auto prep12 = [&](int S) __attribute__((always_inline)) {
-            if (pw == 0 && cq == 0)
-                *reinterpret_cast<float4*>(sBeta(S) + 4 * rg) = make_float4(rb[0], rb[1], rb[2], rb[3]);
+            if (loads_beta) sBeta(S)[lane] = rbeta;
 #pragma unroll
             for (int vv = 0; vv < VPT; ++vv) {
                 const int idx = vlane + 64 * NP * vv;
@@ -803,8 +821,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                 float kk[4], qq[4];
                 T::unpack4(rk[rr], kk);
                 T::unpack4(rq[rr], qq);
-                const float b = rb[rr];
-                float gam[4], kh4[4], bk[4], qg[4];
+                float gam[4], kh4[4], kg[4], qg[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     // exp(+-g) as 2^(+-g2): one v_exp_f32 each; |g| stays within
@@ -813,10 +830,10 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                     gam[c] = __builtin_amdgcn_exp2f(g[c]);
                     kh4[c] = kk[c] * __builtin_amdgcn_exp2f(-g[c]);
                     kbar[rr][c] = kh4[c] * Gc[c];
-                    bk[c] = (b * kk[c]) * gam[c];
+                    kg[c] = kk[c] * gam[c];
                     qg[c] = qq[c] * gam[c];
                 }
-                lds_store4<BF16>(tKb(S) + r * LDK + i0, bk[0], bk[1], bk[2], bk[3]);
+                lds_store4<BF16>(tKb(S) + r * LDK + i0, kg[0], kg[1], kg[2], kg[3]);
                 lds_store4<BF16>(tKh(S) + r * LDK + i0, kh4[0], kh4[1], kh4[2], kh4[3]);
                 lds_store4<BF16>(tQ(S) + r * LDK + i0, qg[0], qg[1], qg[2], qg[3]);
             }
@@ -826,17 +843,21 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                                  kbar[3][c]);
         };
 
-        // The raw registers have a single loop-carried definition (loaded
-        // after prep, read by the next prep), so the loads stay in flight
-        // across the hand-offs.
-        if (nchunks > 0) load_chunk(t_beg, chunk_len(0));
+        auto load_chunk = [&](int m) __attribute__((always_inline)) {
+            const Rsrc r = rsrc_of(m);
+            load_beta(r);
+            load_v(r);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) load_row(r, rr);
+        };
+        if (nchunks > 0) load_chunk(0);
         int P = 0;  // slot of chunk m: m mod 3
         for (int m = 0; m < nchunks; ++m) {
             // slot P last held chunk m - 3: wait until every consumer released it
             if (m >= 3) ctr_wait(nFree, NC * (m - 2), fault);
             prep12(P);
             ctr_publish(prodDone + pw, m + 1, lane);
-            if (m + 1 < nchunks) load_chunk(t_beg + (m + 1) * C, chunk_len(m + 1));
+            if (m + 1 < nchunks) load_chunk(m + 1);
             P = P == 2 ? 0 : P + 1;
         }
     }
