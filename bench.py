@@ -28,7 +28,9 @@ sys.path.insert(0, _ROOT)
 METRIC = "KDA prefill tokens/s (T=32k,H=32,d=128) + decode step µs; % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
-CHUNK = 64
+# chunk length of the prefill kernel for bf16 inputs at d_k = 128 (32 tokens;
+# 16 where a 32-token chunk's LDS tiles exceed the 160 KB of one CU)
+CHUNK = 32
 
 
 def prefill_bytes(T_tot: int, N: int, H: int, dk: int, dv: int, esize: int) -> int:

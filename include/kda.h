@@ -30,7 +30,7 @@
  *    the caller's next synchronisation.
  *  - Results are deterministic: the same inputs give the same bits.
  *  - Numerical contract: log_alpha finite and <= 0 with the sum of log_alpha
- *    over any 64 consecutive tokens of a sequence >= -80 per channel (the
+ *    over any 32 consecutive tokens of a sequence >= -80 per channel (the
  *    chunked prefill evaluates exp(+-that sum) in fp32); beta finite.
  */
 #ifndef KDA_H
