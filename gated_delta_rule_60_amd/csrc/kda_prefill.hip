@@ -78,6 +78,10 @@ using ic = std::integral_constant<int, V>;
 // its Gram products while they run chunk i); the consumers' job results
 // (L, A_qk, -T_bb) alternate between two buffers.  Slot s starts at
 // s * PBUF, job buffer b at OFF_JOB + b * JBUF.
+//
+// Operand tiles (the producers' tiles) are unpadded and swizzled in 16-byte
+// units (see quad_off): UK units per row of a [C][DK] tile, UT per row of a
+// [rows][C] tile.  Job tiles are padded row-major.
 template <bool BF16, int DK, int NC, int CT, int C_>
 struct Layout {
     using E = typename Elem<BF16>::E;
@@ -85,18 +89,20 @@ struct Layout {
     static constexpr int NB = C / 16;
     static constexpr int BV = 16 * CT * NC;
     static constexpr int NSLOT = 3;
-    static constexpr int PAD = 16 / static_cast<int>(sizeof(E));  // 16 bytes of row padding
-    static constexpr int LDK = DK + PAD;
-    static constexpr int LDC = C + PAD;
-    static constexpr int LDT = 16 + PAD;
     static constexpr size_t ES = sizeof(E);
-    static constexpr size_t SZ_KB = align16(C * LDK * ES);      // beta K~, Q~, K^  [C][LDK]
-    static constexpr size_t SZ_KBT = align16(DK * LDC * ES);    // Kbar^T           [DK][LDC]
-    static constexpr size_t SZ_VT = align16(BV * LDC * ES);     // V^T              [BV][LDC]
-    static constexpr size_t SZ_GC = align16(DK * 4);            // Gamma_C          [DK]
-    static constexpr size_t SZ_BETA = align16(C * 4);           // beta             [C]
-    static constexpr size_t SZ_L = align16(C * LDC * ES);       // L, A_qk          [C][LDC]
-    static constexpr size_t SZ_T = align16(NB * 16 * LDT * ES);  // -T_bb           [NB][16][LDT]
+    static constexpr int UK = static_cast<int>(DK * ES / 16);
+    static constexpr int UT = static_cast<int>(C * ES / 16);
+    static_assert(UT >= 4, "a [rows][C] operand tile row spans at least 4 units");
+    static constexpr int PAD = 16 / static_cast<int>(sizeof(E));  // 16 bytes of row padding
+    static constexpr int LDJ = C + PAD;
+    static constexpr int LDT = 16 + PAD;
+    static constexpr size_t SZ_KB = C * DK * ES;                 // K~, Q~, K^  [C][DK]
+    static constexpr size_t SZ_KBT = DK * C * ES;                // Kbar^T      [DK][C]
+    static constexpr size_t SZ_VT = BV * C * ES;                 // V^T         [BV][C]
+    static constexpr size_t SZ_GC = align16(DK * 4);             // Gamma_C     [DK]
+    static constexpr size_t SZ_BETA = align16(C * 4);            // beta        [C]
+    static constexpr size_t SZ_L = align16(C * LDJ * ES);        // L, A_qk     [C][LDJ]
+    static constexpr size_t SZ_T = align16(NB * 16 * LDT * ES);  // -T_bb       [NB][16][LDT]
     // producer slot
     static constexpr size_t O_KB = 0;
     static constexpr size_t O_Q = O_KB + SZ_KB;
@@ -169,6 +175,65 @@ __device__ __forceinline__ f32x4_t lds_load4(const typename Elem<BF16>::E* p) {
     } else {
         return *reinterpret_cast<const f32x4_t*>(p);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Swizzled operand tiles.  A row of an operand tile is a sequence of 16-byte
+// units; a "quad" is four consecutive elements along the row (logical quad
+// Q holds elements 4Q .. 4Q+3).
+//   bf16: the quads of each 32-element block kb are interleaved so that a
+//         lane's eight MFMA operand values (quads g and g + 4 of the block,
+//         the slot order of the fragments) are one 16-byte unit:
+//         quad Q -> unit 4 (Q >> 3) + (Q & 3), half (Q >> 2) & 1.
+//   fp32: quad Q -> unit Q.
+// The unit index is then XORed with swz<U>(row), U = units per row.  The
+// swizzles keep the consumers' 16-byte fragment reads (16 rows by two
+// quad groups per LDS cycle) and the producers' 8-byte quad writes (eight
+// rows 4 apart, or eight quads of one row) free of bank conflicts on gfx950
+// (64 banks of 4 bytes for 16-byte reads and for writes).
+// ---------------------------------------------------------------------------
+template <int U>
+__device__ __forceinline__ int swz(int r) {
+    static_assert(U >= 4 && (U & (U - 1)) == 0, "units per row: a power of two >= 4");
+    if constexpr (U >= 16) return 2 * ((r ^ (r >> 2)) & 7);
+    else if constexpr (U == 8) return (r ^ (r >> 2)) & 7;
+    else return (2 * ((r >> 2) & 1)) ^ ((r >> 3) & 1);
+}
+
+// byte offset of logical quad Q of row r in a tile with U units per row
+template <bool BF16, int U>
+__device__ __forceinline__ int quad_off(int r, int Q) {
+    if constexpr (BF16) {
+        const int unit = 4 * (Q >> 3) + (Q & 3);
+        return 16 * (U * r + (unit ^ swz<U>(r))) + 8 * ((Q >> 2) & 1);
+    } else {
+        return 16 * (U * r + (Q ^ swz<U>(r)));
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ typename Elem<BF16>::E* tile_at(void* tile, int off) {
+    return reinterpret_cast<typename Elem<BF16>::E*>(static_cast<unsigned char*>(tile) + off);
+}
+
+// MFMA fragment of a 32-deep block kb of row r, lane group g (frag8 slot order)
+template <bool BF16, int U>
+__device__ __forceinline__ typename Elem<BF16>::F8 tile_frag8(const void* tile, int r, int kb, int g) {
+    const unsigned char* t = static_cast<const unsigned char*>(tile);
+    if constexpr (BF16) {
+        return *reinterpret_cast<const bf16x8_t*>(t + 16 * (U * r + ((4 * kb + g) ^ swz<U>(r))));
+    } else {
+        const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(t + 16 * (U * r + ((8 * kb + g) ^ swz<U>(r))));
+        const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(t + 16 * (U * r + ((8 * kb + g + 4) ^ swz<U>(r))));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
+// one quad (a 16-deep fragment, or four C-layout values) of row r
+template <bool BF16, int U>
+__device__ __forceinline__ typename Elem<BF16>::F4 tile_quad(const void* tile, int r, int Q) {
+    return *reinterpret_cast<const typename Elem<BF16>::F4*>(static_cast<const unsigned char*>(tile) +
+                                                              quad_off<BF16, U>(r, Q));
 }
 
 // Transposes a 4x4 block given as four raw row quads into four column quads.
@@ -310,7 +375,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
     using F4 = typename T::F4;
     constexpr int C = Sh::C, NB = Sh::NB, NT = Sh::NT, BV = Sh::BV;
     constexpr int NP = Sh::NP;
-    constexpr int LDK = Sh::LDK, LDC = Sh::LDC, LDT = Sh::LDT;
+    constexpr int LDJ = Sh::LDJ, LDT = Sh::LDT, UK = Sh::UK, UT = Sh::UT;
     constexpr int KB = DK / 32;  // 32-deep k blocks over key channels
     constexpr int NRG = Sh::NRG, QW = Sh::QW, NQ = Sh::NQ, VPT = Sh::VPT, VITEMS = Sh::VITEMS;
 
@@ -396,7 +461,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
     const int strideV = H * dv;
 
     // Upper block-triangles of L and A_qk stay zero for the whole kernel.
-    for (int idx = tid; idx < C * LDC; idx += NT) {
+    for (int idx = tid; idx < C * LDJ; idx += NT) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             tL(b)[idx] = T::to_e(0.f);
@@ -460,16 +525,13 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         auto prep3_compute = [&](int S, int t) __attribute__((always_inline)) {  // S: producer slot
             const int jc = min(job_of(t), NJOB - 1);
             const int st = job_st(jc), rt = job_rt(jc);
-            const E* Ab = tKh(S) + 16 * st * LDK;
-            const E* Bk = tKb(S) + 16 * rt * LDK;
-            const E* Bq = tQ(S) + 16 * rt * LDK;
             f32x4_t accL = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f}, accN = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const F8 a = lds_frag8<BF16>(Ab + 32 * kb, LDK, lane);
-                const F8 bk = lds_frag8<BF16>(Bk + 32 * kb, LDK, lane);
+                const F8 a = tile_frag8<BF16, UK>(tKh(S), 16 * st + ln, kb, lg);
+                const F8 bk = tile_frag8<BF16, UK>(tKb(S), 16 * rt + ln, kb, lg);
                 accL = mma8<BF16>(accL, a, bk);
-                accA = mma8<BF16>(accA, a, lds_frag8<BF16>(Bq + 32 * kb, LDK, lane));
+                accA = mma8<BF16>(accA, a, tile_frag8<BF16, UK>(tQ(S), 16 * rt + ln, kb, lg));
                 accN = mma8<BF16>(accN, bk, a);  // P^T: C layout of N (used by diagonal jobs)
             }
             Job res;
@@ -521,8 +583,8 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
             if (job < NJOB) {
                 const int st = job_st(job), rt = job_rt(job);
                 const int r = 16 * rt + ln;
-                lds_store4<BF16>(tL(S) + r * LDC + 16 * st + 4 * lg, res.l[0], res.l[1], res.l[2], res.l[3]);
-                lds_store4<BF16>(tA(S) + r * LDC + 16 * st + 4 * lg, res.a[0], res.a[1], res.a[2], res.a[3]);
+                lds_store4<BF16>(tL(S) + r * LDJ + 16 * st + 4 * lg, res.l[0], res.l[1], res.l[2], res.l[3]);
+                lds_store4<BF16>(tA(S) + r * LDJ + 16 * st + 4 * lg, res.a[0], res.a[1], res.a[2], res.a[3]);
                 // lane (ln, lg) holds T[ln][4 lg + j]: -T row-major
                 if (st == rt) lds_store4<BF16>(tT(S) + r * LDT + 4 * lg, res.t[0], res.t[1], res.t[2], res.t[3]);
             }
@@ -544,12 +606,12 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
             for (int rt = 0; rt < NB; ++rt) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    const f32x4_t v4 = lds_load4<BF16>(tVt(B) + (col0(ct) + ln) * LDC + 16 * rt + 4 * lg);
+                    const f32x4_t v4 = lds_load4<BF16>(tile_at<BF16>(tVt(B), quad_off<BF16, UT>(col0(ct) + ln, 4 * rt + lg)));
                     Rp[ct][rt] = f32x4_t{-v4[0], -v4[1], -v4[2], -v4[3]};
                 }
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
-                    const F8 a = lds_frag8<BF16>(tKb(B) + 16 * rt * LDK + 32 * kb, LDK, lane);
+                    const F8 a = tile_frag8<BF16, UK>(tKb(B), 16 * rt + ln, kb, lg);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) Rp[ct][rt] = mma8<BF16>(Rp[ct][rt], a, sf[ct][kb]);
                 }
@@ -576,12 +638,12 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                 for (int ct = 0; ct < CT; ++ct) Y[ct] = Rp[ct][b];
 #pragma unroll
                 for (int kp = 0; kp + 1 < b; kp += 2) {
-                    const F8 a = lds_frag8<BF16>(tL(J) + 16 * b * LDC + 16 * kp, LDC, lane);
+                    const F8 a = lds_frag8<BF16>(tL(J) + 16 * b * LDJ + 16 * kp, LDJ, lane);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) Y[ct] = mma8<BF16>(Y[ct], a, u_frag8(ct, kp));
                 }
                 if (b & 1) {
-                    const F4 a = lds_frag4<BF16>(tL(J) + 16 * b * LDC + 16 * (b - 1), LDC, lane);
+                    const F4 a = lds_frag4<BF16>(tL(J) + 16 * b * LDJ + 16 * (b - 1), LDJ, lane);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) Y[ct] = mma4<BF16>(Y[ct], a, uf[ct][b - 1]);
                 }
@@ -599,18 +661,18 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                 for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
-                    const F8 bq = lds_frag8<BF16>(tQ(B) + 16 * rt * LDK + 32 * kb, LDK, lane);
+                    const F8 bq = tile_frag8<BF16, UK>(tQ(B), 16 * rt + ln, kb, lg);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], sf[ct][kb], bq);
                 }
 #pragma unroll
                 for (int sp = 0; sp + 1 <= rt; sp += 2) {
-                    const F8 ba = lds_frag8<BF16>(tA(J) + 16 * rt * LDC + 16 * sp, LDC, lane);
+                    const F8 ba = lds_frag8<BF16>(tA(J) + 16 * rt * LDJ + 16 * sp, LDJ, lane);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], u_frag8(ct, sp), ba);
                 }
                 if (!(rt & 1)) {
-                    const F4 ba = lds_frag4<BF16>(tA(J) + 16 * rt * LDC + 16 * rt, LDC, lane);
+                    const F4 ba = lds_frag4<BF16>(tA(J) + 16 * rt * LDJ + 16 * rt, LDJ, lane);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) acc[ct] = mma4<BF16>(acc[ct], uf[ct][rt], ba);
                 }
@@ -632,12 +694,12 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                                       Sr[ct][it][3] * g4.w};
 #pragma unroll
                 for (int kb = 0; kb < NB / 2; ++kb) {
-                    const F8 a = lds_frag8<BF16>(tKbT(B) + 16 * it * LDC + 32 * kb, LDC, lane);
+                    const F8 a = tile_frag8<BF16, UT>(tKbT(B), 16 * it + ln, kb, lg);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], a, u_frag8(ct, 2 * kb));
                 }
                 if constexpr (NB & 1) {
-                    const F4 a = lds_frag4<BF16>(tKbT(B) + 16 * it * LDC + 16 * (NB - 1), LDC, lane);
+                    const F4 a = tile_quad<BF16, UT>(tKbT(B), 16 * it + ln, 4 * (NB - 1) + lg);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) acc[ct] = mma4<BF16>(acc[ct], a, uf[ct][NB - 1]);
                 }
@@ -779,7 +841,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                     R4 cols[4];
                     transpose4<BF16>(rv[vv], cols);
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) T::lds_put_raw4(tVt(S) + (c4 + c) * LDC + r0, cols[c]);
+                    for (int c = 0; c < 4; ++c) T::lds_put_raw4(tile_at<BF16>(tVt(S), quad_off<BF16, UT>(c4 + c, r0 / 4)), cols[c]);
                 }
             }
             if (!qok) return;
@@ -833,13 +895,14 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                     kg[c] = kk[c] * gam[c];
                     qg[c] = qq[c] * gam[c];
                 }
-                lds_store4<BF16>(tKb(S) + r * LDK + i0, kg[0], kg[1], kg[2], kg[3]);
-                lds_store4<BF16>(tKh(S) + r * LDK + i0, kh4[0], kh4[1], kh4[2], kh4[3]);
-                lds_store4<BF16>(tQ(S) + r * LDK + i0, qg[0], qg[1], qg[2], qg[3]);
+                const int off = quad_off<BF16, UK>(r, i0 / 4);
+                lds_store4<BF16>(tile_at<BF16>(tKb(S), off), kg[0], kg[1], kg[2], kg[3]);
+                lds_store4<BF16>(tile_at<BF16>(tKh(S), off), kh4[0], kh4[1], kh4[2], kh4[3]);
+                lds_store4<BF16>(tile_at<BF16>(tQ(S), off), qg[0], qg[1], qg[2], qg[3]);
             }
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                lds_store4<BF16>(tKbT(S) + (i0 + c) * LDC + 4 * rg, kbar[0][c], kbar[1][c], kbar[2][c],
+                lds_store4<BF16>(tile_at<BF16>(tKbT(S), quad_off<BF16, UT>(i0 + c, rg)), kbar[0][c], kbar[1][c], kbar[2][c],
                                  kbar[3][c]);
         };
 
