@@ -118,7 +118,8 @@ struct Layout {
     static constexpr size_t O_A = O_L + SZ_L;
     static constexpr size_t O_T = O_A + SZ_L;
     static constexpr size_t JBUF = O_T + SZ_T;
-    static constexpr size_t OFF_SEQ = OFF_JOB + 2 * JBUF;
+    static constexpr size_t OFF_SCAN = OFF_JOB + 2 * JBUF;  // producers' scan scratch: [NP][64] float4
+    static constexpr size_t OFF_SEQ = OFF_SCAN + 4 * 64 * 16;
     static constexpr size_t OFF_CTR = OFF_SEQ + align16((kSortMax + 1) * 4);
     static constexpr size_t BYTES = OFF_CTR + 64;
 };
@@ -143,6 +144,7 @@ struct PrefillShape : ChosenLayout<BF16, DK, NC, CT> {
     static constexpr int NQ = DK / 4;        // channel quads
     static constexpr int NP = NQ > QW ? NQ / QW : 1;
     static_assert(NQ <= QW || NQ % QW == 0, "channel strips tile d_k");
+    static_assert(NP <= 4, "scan scratch holds four producer waves");
     static constexpr int NJOB = Base::NB * (Base::NB + 1) / 2;  // Gram/inverse jobs per chunk
     static constexpr int NW = NC + NP;
     static constexpr int NT = 64 * NW;
@@ -263,6 +265,10 @@ __device__ __forceinline__ void transpose4(const typename Elem<BF16>::R4 (&rows)
 // or past `bytes` returns zero without touching memory.  Per-chunk resources
 // make every load one instruction (a per-lane offset fixed for the whole
 // sequence plus a scalar row offset) and zero the rows past a sequence end.
+// A buffer offset beyond every range this kernel builds: the load returns 0
+// without touching memory.
+constexpr int kNoAccess = 0x7FFFFF00;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
@@ -303,15 +309,6 @@ __device__ __forceinline__ typename Elem<BF16>::R4 buf_load_raw4(__amdgpu_buffer
     } else {
         return buf_load_f4(r, voff, soff);
     }
-}
-
-// x of lane (l - D) within the same 16-lane row, 0 where there is none.
-// A DPP read from a lane that is masked off also yields 0, so callers must
-// call this with every lane of the wave active (not inside a lane-dependent
-// branch, which includes either arm of a conditional expression).
-template <int D>
-__device__ __forceinline__ float row_shr(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + D, 0xF, 0xF, true));
 }
 
 // Inter-wave hand-off through monotonic counters in LDS.  A counter is
@@ -765,11 +762,12 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         // =====================================================================
         // producer: raw loads, decay prefix and decayed operand tiles
         // =====================================================================
-        // Lane geometry: lane = cq * NRG + rg owns rows 4 rg .. 4 rg + 3 and
-        // key channels i0 .. i0 + 3 of this wave's channel strip.
+        // Lane geometry: lane = rg * QW + cq owns rows 4 rg .. 4 rg + 3 and
+        // key channels i0 .. i0 + 3 of this wave's channel strip, so that
+        // consecutive lanes load consecutive bytes of a row.
         const int pw = wave - NC;
-        const int rg = lane % NRG;
-        const int cq = lane / NRG;
+        const int rg = lane / QW;
+        const int cq = lane % QW;
         const int gq = pw * QW + cq;
         const bool qok = NQ >= QW || gq < NQ;  // idle lanes only when d_k < one strip
         const int i0 = 4 * min(gq, NQ - 1);
@@ -780,11 +778,14 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         const float* const bh = beta + h;
         const G* const vh = v + static_cast<size_t>(h) * dv + j0;
 
-        // Raw inputs of the next chunk, loaded right after the current chunk's
-        // prep consumed the registers (a single loop-carried definition, so
-        // the loads stay in flight across the hand-offs).  Rows past the end
-        // of the sequence read as zero (buffer range check), so padded rows
-        // need no masking anywhere.
+        // Raw inputs of chunks m+1 and m+2 are in flight while chunk m is
+        // prepared: two register sets, even chunks in set 0 and odd chunks in
+        // set 1, each reloaded right after its chunk's prep consumed it
+        // (one set, one chunk ahead, where the raw tiles are large: fp32).
+        // Every load is unconditional (rows past the end of the sequence, and
+        // chunks past the last, fall outside the buffer ranges and read as
+        // zero), so the compiler's wait counts stay exact and a wait for one
+        // set never waits for the other.
         constexpr int GS = static_cast<int>(sizeof(G));
         const int rowK = strideK * GS;  // bytes per token row of q and k
         const int rowLA = strideK * 4;
@@ -793,96 +794,99 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         const int offK = 4 * rg * rowK + i0 * GS;
         const int offLA = 4 * rg * rowLA + i0 * 4;
         const bool loads_beta = pw == 0 && lane < C;  // beta of row `lane`, for the consumers
-        float4 rla[4];
-        R4 rk[4], rq[4], rv[VPT][4];
-        float rbeta = 0.f;
+        constexpr int NSET = BF16 ? 2 : 1;
+        float4 rla[NSET][4];
+        R4 rk[NSET][4], rq[NSET][4], rv[NSET][VPT][4];
+        float rbeta[NSET];
         struct Rsrc {
             __amdgpu_buffer_rsrc_t k, q, la, v, b;
         };
         auto rsrc_of = [&](int m) __attribute__((always_inline)) {
             const int c0 = t_beg + m * C;
-            const int len = chunk_len(m);
+            // chunks past the end: empty ranges, no access (kept in a scalar register)
+            const int len = __builtin_amdgcn_readfirstlane(max(0, chunk_len(m)));
             const size_t tok = static_cast<size_t>(c0) * strideK;
             return Rsrc{buffer_rsrc(kh + tok, len * rowK), buffer_rsrc(qh + tok, len * rowK),
                         buffer_rsrc(lah + tok, len * rowLA),
                         buffer_rsrc(vh + static_cast<size_t>(c0) * strideV, len * rowV),
                         buffer_rsrc(bh + static_cast<size_t>(c0) * H, len * rowB)};
         };
-        auto load_row = [&](const Rsrc& r, int rr) __attribute__((always_inline)) {
-            rla[rr] = buf_load_f4(r.la, offLA, rr * rowLA);
-            rk[rr] = buf_load_raw4<BF16>(r.k, offK, rr * rowK);
-            rq[rr] = buf_load_raw4<BF16>(r.q, offK, rr * rowK);
-        };
-        auto load_v = [&](const Rsrc& r) __attribute__((always_inline)) {
+        auto load_chunk = [&](auto X, int m) __attribute__((always_inline)) {
+            constexpr int x = decltype(X)::value;
+            const Rsrc r = rsrc_of(m);
+            rbeta[x] = buf_load_f1(r.b, loads_beta ? lane * rowB : kNoAccess, 0);
 #pragma unroll
             for (int vv = 0; vv < VPT; ++vv) {
                 const int idx = vlane + 64 * NP * vv;
-                if (VITEMS % (64 * NP) == 0 || idx < VITEMS) {
-                    const int r0 = 4 * (idx % (C / 4));
-                    const int c4 = 4 * (idx / (C / 4));
+                const bool ok = VITEMS % (64 * NP) == 0 || idx < VITEMS;
+                const int c4 = 4 * (idx % (BV / 4));  // value-column quad (fastest: coalesced rows)
+                const int r0 = 4 * (idx / (BV / 4));
+                const int off = ok ? r0 * rowV + c4 * GS : kNoAccess;
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) rv[vv][rr] = buf_load_raw4<BF16>(r.v, r0 * rowV + c4 * GS, rr * rowV);
-                }
+                for (int rr = 0; rr < 4; ++rr) rv[x][vv][rr] = buf_load_raw4<BF16>(r.v, off, rr * rowV);
             }
-        };
-        auto load_beta = [&](const Rsrc& r) __attribute__((always_inline)) {
-            if (loads_beta) rbeta = buf_load_f1(r.b, lane * rowB, 0);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                rla[x][rr] = buf_load_f4(r.la, offLA, rr * rowLA);
+                rk[x][rr] = buf_load_raw4<BF16>(r.k, offK, rr * rowK);
+                rq[x][rr] = buf_load_raw4<BF16>(r.q, offK, rr * rowK);
+            }
         };
 
         // beta, V^T, cumulative decay and the decayed operand tiles of slot S
-        auto prep12 = [&](int S) __attribute__((always_inline)) {
-            if (loads_beta) sBeta(S)[lane] = rbeta;
+        auto prep12 = [&](auto X, int S) __attribute__((always_inline)) {
+            constexpr int x = decltype(X)::value;
+            if (loads_beta) sBeta(S)[lane] = rbeta[x];
 #pragma unroll
             for (int vv = 0; vv < VPT; ++vv) {
                 const int idx = vlane + 64 * NP * vv;
                 if (VITEMS % (64 * NP) == 0 || idx < VITEMS) {
-                    const int r0 = 4 * (idx % (C / 4));
-                    const int c4 = 4 * (idx / (C / 4));
+                    const int c4 = 4 * (idx % (BV / 4));
+                    const int r0 = 4 * (idx / (BV / 4));
                     R4 cols[4];
-                    transpose4<BF16>(rv[vv], cols);
+                    transpose4<BF16>(rv[x][vv], cols);
 #pragma unroll
                     for (int c = 0; c < 4; ++c) T::lds_put_raw4(tile_at<BF16>(tVt(S), quad_off<BF16, UT>(c4 + c, r0 / 4)), cols[c]);
                 }
             }
             if (!qok) return;
-            // log alpha in log2 units; group sums, then an inclusive prefix
-            // over the NRG row groups (consecutive lanes), in a fixed order.
+            // log alpha in log2 units: row-group sums, then the exclusive
+            // prefix over the NRG row groups of each channel (QW lanes apart)
+            // through this wave's LDS scratch, summed in row-group order.
             float la[4][4], tot[4];
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                la[rr][0] = rla[rr].x;
-                la[rr][1] = rla[rr].y;
-                la[rr][2] = rla[rr].z;
-                la[rr][3] = rla[rr].w;
+                la[rr][0] = rla[x][rr].x;
+                la[rr][1] = rla[x][rr].y;
+                la[rr][2] = rla[x][rr].z;
+                la[rr][3] = rla[x][rr].w;
             }
 #pragma unroll
             for (int c = 0; c < 4; ++c) tot[c] = ((la[0][c] + la[1][c]) + (la[2][c] + la[3][c])) * kLog2e;
-            float g[4], Gc[4];
+            float4* const scan = reinterpret_cast<float4*>(smem + Sh::OFF_SCAN) + 64 * pw;
+            scan[lane] = make_float4(tot[0], tot[1], tot[2], tot[3]);
+            float g[4] = {0.f, 0.f, 0.f, 0.f}, sum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                // Hillis-Steele over segments of NRG lanes; each DPP move runs
-                // on all lanes, the segment boundary is applied afterwards.
-                float x = tot[c];
-                const float s1 = row_shr<1>(x);
-                x += (rg >= 1) ? s1 : 0.f;
-                const float s2 = row_shr<2>(x);
-                x += (rg >= 2) ? s2 : 0.f;
-                if constexpr (NRG > 4) {
-                    const float s4 = row_shr<4>(x);
-                    x += (rg >= 4) ? s4 : 0.f;
+            for (int r = 0; r < NRG; ++r) {
+                const float4 t4 = scan[QW * r + cq];
+                const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    g[c] = r < rg ? g[c] + tv[c] : g[c];  // groups before this one
+                    sum[c] += tv[c];
                 }
-                const float ex = row_shr<1>(x);
-                g[c] = (rg >= 1) ? ex : 0.f;  // sum of the groups before this one
-                Gc[c] = __builtin_amdgcn_exp2f(__shfl(x, (lane & ~(NRG - 1)) + NRG - 1));
             }
+            float Gc[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) Gc[c] = __builtin_amdgcn_exp2f(sum[c]);
             if (rg == 0) *reinterpret_cast<float4*>(sGC(S) + i0) = make_float4(Gc[0], Gc[1], Gc[2], Gc[3]);
             float kbar[4][4];
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int r = 4 * rg + rr;
                 float kk[4], qq[4];
-                T::unpack4(rk[rr], kk);
-                T::unpack4(rq[rr], qq);
+                T::unpack4(rk[x][rr], kk);
+                T::unpack4(rq[x][rr], qq);
                 float gam[4], kh4[4], kg[4], qg[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -906,22 +910,29 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                                  kbar[3][c]);
         };
 
-        auto load_chunk = [&](int m) __attribute__((always_inline)) {
-            const Rsrc r = rsrc_of(m);
-            load_beta(r);
-            load_v(r);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) load_row(r, rr);
-        };
-        if (nchunks > 0) load_chunk(0);
-        int P = 0;  // slot of chunk m: m mod 3
-        for (int m = 0; m < nchunks; ++m) {
+        // Chunk m uses register set m mod NSET and LDS slot m mod 3.  With
+        // two sets, an odd chunk count ends with one virtual chunk past the
+        // end (zero inputs): its tiles go to a slot every consumer has
+        // released and nothing reads them.
+        load_chunk(ic<0>{}, 0);
+        if constexpr (NSET == 2) {
+            // issued in this order on every path into the loop, so the waits
+            // for set 0 count set 1's loads as issued after it
+            asm volatile("" ::: "memory");
+            load_chunk(ic<1>{}, 1);
+        }
+        int P = 0;
+        auto step = [&](auto X, int m) __attribute__((always_inline)) {
             // slot P last held chunk m - 3: wait until every consumer released it
             if (m >= 3) ctr_wait(nFree, NC * (m - 2), fault);
-            prep12(P);
+            prep12(X, P);
             ctr_publish(prodDone + pw, m + 1, lane);
-            if (m + 1 < nchunks) load_chunk(m + 1);
+            load_chunk(X, m + NSET);
             P = P == 2 ? 0 : P + 1;
+        };
+        for (int m = 0; m < nchunks; m += NSET) {
+            step(ic<0>{}, m);
+            if constexpr (NSET == 2) step(ic<1>{}, m + 1);
         }
     }
 }
