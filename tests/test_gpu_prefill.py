@@ -52,6 +52,23 @@ def test_small_cases_every_split(case):
     _run_case(*case, seed=sum(case[0]) + case[2])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("la_range", [(0.5, 2.5), (2.5, 2.5)], ids=["mixed", "max"])
+def test_strong_decay_at_the_contract_limit(dtype, la_range):
+    """log alpha down to -2.5 per token and channel: the decay summed over 32
+    consecutive tokens reaches the -80 limit of the numerical contract ("max":
+    exactly), so the chunk's exponentials span e^(+-80)."""
+    x = inputs.make_prefill_inputs([700, 33, 1], 2, 128, 128, dtype, seed=11,
+                                   log_alpha_range=la_range, s0_std=1.0)
+    ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens)
+    d = upload(x)
+    for split in valid_splits(128):
+        log(f"  strong decay {la_range} {dtype} v_split={split}")
+        o, ST = kda.prefill(**d, v_split=split)
+        assert_close(host(o), ref_o, dtype, "o")
+        assert_close(host(ST), ref_S, dtype, "S_T")
+
+
 def test_workload_t256_fp32():
     x = inputs.make_workload("prefill_t256_h2_d32_f32")
     ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens)
