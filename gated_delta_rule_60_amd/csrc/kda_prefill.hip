@@ -243,16 +243,18 @@ template <bool BF16>
 __device__ __forceinline__ void transpose4(const typename Elem<BF16>::R4 (&rows)[4],
                                            typename Elem<BF16>::R4 (&cols)[4]) {
     if constexpr (BF16) {
-        // rows[r] = {x: c0 | c1 << 16, y: c2 | c3 << 16}
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int sh = (c & 1) ? 16 : 0;
-            uint32_t e[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) e[r] = (((c < 2) ? rows[r].x : rows[r].y) >> sh) & 0xFFFFu;
-            cols[c].x = e[0] | (e[1] << 16);
-            cols[c].y = e[2] | (e[3] << 16);
-        }
+        // rows[r] = {x: c0 | c1 << 16, y: c2 | c3 << 16}.  v_perm_b32 picks
+        // bytes of {S0 (bytes 4..7), S1 (bytes 0..3)}: the low or high 16
+        // bits of two rows form one 32-bit word of a column.
+        constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;
+        cols[0].x = __builtin_amdgcn_perm(rows[1].x, rows[0].x, kLo);
+        cols[0].y = __builtin_amdgcn_perm(rows[3].x, rows[2].x, kLo);
+        cols[1].x = __builtin_amdgcn_perm(rows[1].x, rows[0].x, kHi);
+        cols[1].y = __builtin_amdgcn_perm(rows[3].x, rows[2].x, kHi);
+        cols[2].x = __builtin_amdgcn_perm(rows[1].y, rows[0].y, kLo);
+        cols[2].y = __builtin_amdgcn_perm(rows[3].y, rows[2].y, kLo);
+        cols[3].x = __builtin_amdgcn_perm(rows[1].y, rows[0].y, kHi);
+        cols[3].y = __builtin_amdgcn_perm(rows[3].y, rows[2].y, kHi);
     } else {
         cols[0] = make_float4(rows[0].x, rows[1].x, rows[2].x, rows[3].x);
         cols[1] = make_float4(rows[0].y, rows[1].y, rows[2].y, rows[3].y);
