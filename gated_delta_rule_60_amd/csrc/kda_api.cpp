@@ -90,8 +90,8 @@ kda_status kda_prefill_split(const void* q, const void* k, const void* v, const 
     if (T_tot > INT32_MAX) return fail(KDA_ERR_INVALID_ARG, "T_tot must fit in int32 (cu_seqlens is int32)");
     if (T_tot * H * static_cast<int64_t>(d_k > d_v ? d_k : d_v) > INT32_MAX)
         return fail(KDA_ERR_INVALID_ARG, "q, k, v, o and log_alpha must each hold fewer than 2^31 elements");
-    if (static_cast<int64_t>(H) * (d_k > d_v ? d_k : d_v) > (int64_t{1} << 24))
-        return fail(KDA_ERR_INVALID_ARG, "H * max(d_k, d_v) must not exceed 2^24");
+    if (static_cast<int64_t>(H) * (d_k > d_v ? d_k : d_v) > (int64_t{1} << 20))
+        return fail(KDA_ERR_INVALID_ARG, "H * max(d_k, d_v) must not exceed 2^20");
     const void* ptrs[] = {q, k, v, log_alpha, o, S0, S_T};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");

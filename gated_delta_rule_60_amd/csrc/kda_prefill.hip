@@ -118,8 +118,8 @@ struct Layout {
     static constexpr size_t O_A = O_L + SZ_L;
     static constexpr size_t O_T = O_A + SZ_L;
     static constexpr size_t JBUF = O_T + SZ_T;
-    static constexpr size_t OFF_SCAN = OFF_JOB + 2 * JBUF;  // producers' scan scratch: [NP][64] float4
-    static constexpr size_t OFF_SEQ = OFF_SCAN + 4 * 64 * 16;
+    static constexpr size_t OFF_SCAN = OFF_JOB + 2 * JBUF;  // producers' scan scratch: [8][64] float4
+    static constexpr size_t OFF_SEQ = OFF_SCAN + 8 * 64 * 16;
     static constexpr size_t OFF_CTR = OFF_SEQ + align16((kSortMax + 1) * 4);
     static constexpr size_t BYTES = OFF_CTR + 64;
 };
@@ -142,15 +142,21 @@ struct PrefillShape : ChosenLayout<BF16, DK, NC, CT> {
     static constexpr int NRG = Base::C / 4;  // row groups of 4 rows
     static constexpr int QW = 64 / NRG;      // channel quads per producer wave
     static constexpr int NQ = DK / 4;        // channel quads
-    static constexpr int NP = NQ > QW ? NQ / QW : 1;
+    static constexpr int NPS = NQ > QW ? NQ / QW : 1;  // channel strips: producer waves per chunk
     static_assert(NQ <= QW || NQ % QW == 0, "channel strips tile d_k");
-    static_assert(NP <= 4, "scan scratch holds four producer waves");
+    // With one 16-column state tile per consumer wave, the consumers'
+    // registers leave room for a third wave per SIMD: two producer waves per
+    // strip then take alternate chunks, each with two chunk periods for its
+    // loads and prep.
+    static constexpr int PP = CT == 1 && NC == 4 ? 2 : 1;
+    static constexpr int NP = PP * NPS;
+    static_assert(NP <= 8, "scan scratch and progress counters hold eight producer waves");
     static constexpr int NJOB = Base::NB * (Base::NB + 1) / 2;  // Gram/inverse jobs per chunk
     static constexpr int NW = NC + NP;
     static constexpr int NT = 64 * NW;
     static_assert(NW <= 16, "at most 16 waves per workgroup");
     static constexpr int VITEMS = (Base::C / 4) * (Base::BV / 4);  // 4x4 blocks of V
-    static constexpr int VPT = (VITEMS + 64 * NP - 1) / (64 * NP);
+    static constexpr int VPT = (VITEMS + 64 * NPS - 1) / (64 * NPS);
 };
 
 template <bool BF16>
@@ -263,12 +269,25 @@ __device__ __forceinline__ void transpose4(const typename Elem<BF16>::R4 (&rows)
     }
 }
 
+// four consecutive storage elements from LDS, raw
+template <bool BF16>
+__device__ __forceinline__ typename Elem<BF16>::R4 lds_get_raw4(const typename Elem<BF16>::E* p) {
+    if constexpr (BF16) {
+        return *reinterpret_cast<const uint2*>(p);
+    } else {
+        return *reinterpret_cast<const float4*>(p);
+    }
+}
+
 // Raw buffer resource over [base, base + bytes): a load at a byte offset at
 // or past `bytes` returns zero without touching memory.  Per-chunk resources
 // make every load one instruction (a per-lane offset fixed for the whole
 // sequence plus a scalar row offset) and zero the rows past a sequence end.
-// A buffer offset beyond every range this kernel builds: the load returns 0
-// without touching memory.
+// A buffer offset beyond every range this kernel builds: a load returns 0 and
+// a store is dropped, without touching memory.  Ranges span at most one
+// chunk's rows of one tensor (C rows of H * max(d_k, d_v) elements, at most
+// 2^27 bytes under the host's limit H * max(d_k, d_v) <= 2^20), and the
+// offset plus a few rows' stride stays below 2^32.
 constexpr int kNoAccess = 0x7FFFFF00;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
@@ -299,6 +318,19 @@ __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, int voff, c
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, h), r, voff, 0, 0);
     } else {
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), r, voff, 0, 0);
+    }
+}
+
+// four consecutive storage elements, raw (stores past the range are dropped)
+template <bool BF16>
+__device__ __forceinline__ void buf_store_raw4(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                               const typename Elem<BF16>::R4& x) {
+    if constexpr (BF16) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{x.x, x.y}, r, voff, soff, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4_t{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)}, r,
+            voff, soff, 0);
     }
 }
 
@@ -373,7 +405,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
     using F8 = typename T::F8;
     using F4 = typename T::F4;
     constexpr int C = Sh::C, NB = Sh::NB, NT = Sh::NT, BV = Sh::BV;
-    constexpr int NP = Sh::NP;
+    constexpr int NP = Sh::NP, NPS = Sh::NPS, PP = Sh::PP;
     constexpr int LDJ = Sh::LDJ, LDT = Sh::LDT, UK = Sh::UK, UT = Sh::UT;
     constexpr int KB = DK / 32;  // 32-deep k blocks over key channels
     constexpr int NRG = Sh::NRG, QW = Sh::QW, NQ = Sh::NQ, VPT = Sh::VPT, VITEMS = Sh::VITEMS;
@@ -403,7 +435,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
     int* const nSolved = ctr + 0;   // consumers: their L, A_qk, -T_bb jobs written
     int* const nFree = ctr + 1;     // consumers: producer slot of the chunk released
     int* const fault = ctr + 2;     // a bounded wait gave up
-    int* const prodDone = ctr + 4;  // [NP] chunks completed by each producer wave
+    int* const prodDone = ctr + 4;  // [NP] chunks completed by each producer wave (ctr + 4 .. ctr + 11)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -477,8 +509,6 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         // consumer: the recurrence of value columns j0 + 16 (CT wave + ct) + ...
         // =====================================================================
         __builtin_amdgcn_s_setprio(3);
-        G* const oh = o + static_cast<size_t>(h) * dv + j0;
-        constexpr int GS = static_cast<int>(sizeof(G));
         auto col0 = [&](int ct) __attribute__((always_inline)) { return 16 * (CT * wave + ct); };
         // Sr[ct][it][j] = S[16 it + 4 lg + j][col]
         f32x4_t Sr[CT][DK / 16];
@@ -628,8 +658,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         // U_b = (-T_bb) (R'_b + sum_{c<b} L_bc U_c);  then O^T = S^T Q~^T + U^T A_qk^T,
         // written to global memory from the C layout: lane (ln, lg) holds
         // four consecutive value columns of token row 16 rt + ln.
-        auto chain_UO = [&](int B, int J, int c0, int len) __attribute__((always_inline)) {
-            const auto bO = buffer_rsrc(oh + static_cast<size_t>(c0) * strideV, len * strideV * GS);
+        auto chain_UO = [&](int B, int J) __attribute__((always_inline)) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 f32x4_t Y[CT];
@@ -653,6 +682,11 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) uf[ct][b] = acc_frag4<BF16>(U[ct][b]);
             }
+            // O = Q~ S + A_qk U for this wave's columns.  In the C layout lane
+            // (ln, lg) holds tokens 16 rt + 4 lg .. + 3 of value column
+            // 16 ct + ln: one O^T quad, staged in the wave's own rows of this
+            // slot's V^T tile (read above, in chain_R).  The producers store
+            // it to global memory, in row order, when they refill the slot.
 #pragma unroll
             for (int rt = 0; rt < NB; ++rt) {
                 f32x4_t acc[CT];
@@ -660,25 +694,25 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                 for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
-                    const F8 bq = tile_frag8<BF16, UK>(tQ(B), 16 * rt + ln, kb, lg);
+                    const F8 aq = tile_frag8<BF16, UK>(tQ(B), 16 * rt + ln, kb, lg);
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], sf[ct][kb], bq);
+                    for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], aq, sf[ct][kb]);
                 }
 #pragma unroll
                 for (int sp = 0; sp + 1 <= rt; sp += 2) {
-                    const F8 ba = lds_frag8<BF16>(tA(J) + 16 * rt * LDJ + 16 * sp, LDJ, lane);
+                    const F8 aa = lds_frag8<BF16>(tA(J) + 16 * rt * LDJ + 16 * sp, LDJ, lane);
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], u_frag8(ct, sp), ba);
+                    for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], aa, u_frag8(ct, sp));
                 }
                 if (!(rt & 1)) {
-                    const F4 ba = lds_frag4<BF16>(tA(J) + 16 * rt * LDJ + 16 * rt, LDJ, lane);
+                    const F4 aa = lds_frag4<BF16>(tA(J) + 16 * rt * LDJ + 16 * rt, LDJ, lane);
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) acc[ct] = mma4<BF16>(acc[ct], uf[ct][rt], ba);
+                    for (int ct = 0; ct < CT; ++ct) acc[ct] = mma4<BF16>(acc[ct], aa, uf[ct][rt]);
                 }
-                // rows past the end of the sequence fall outside bO and are dropped
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
-                    buf_store4<BF16>(bO, ((16 * rt + ln) * strideV + col0(ct) + 4 * lg) * GS, acc[ct]);
+                    lds_store4<BF16>(tile_at<BF16>(tVt(B), quad_off<BF16, UT>(col0(ct) + ln, 4 * rt + lg)),
+                                     acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
             }
         };
         // S <- Diag(Gamma_C) S + Kbar^T U
@@ -711,36 +745,57 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         // alongside the recurrence of chunk i (from the next producer slot)
         // and stored after it.  On the last chunk they run on stale tiles and
         // are not stored.  Chunk i: producer slot P = i mod 3, job buffer i & 1.
-        Job jobs[JPW];
-        if (nchunks > 0) {
-            ctr_wait_each(prodDone, NP, 1, fault);
+        // tiles of chunk m: written by the NPS producer waves of its parity
+        auto wait_tiles = [&](int m) __attribute__((always_inline)) {
+            ctr_wait_each(prodDone + (PP == 2 ? (m & 1) * NPS : 0), NPS, m + 1, fault);
+        };
+        // With at least as many consumer waves as jobs, the waves without a
+        // job run a copy of the loop that has none (a wave-uniform branch);
+        // otherwise every wave runs its jobs, the extra ones on a repeated
+        // job index whose results are never stored.
+        auto run = [&](auto WithJobs) __attribute__((always_inline)) {
+            constexpr bool kJobs = decltype(WithJobs)::value;
+            Job jobs[JPW];
+            if (nchunks > 0) {
+                wait_tiles(0);
+                if constexpr (kJobs) {
 #pragma unroll
-            for (int t = 0; t < JPW; ++t) {
-                jobs[t] = prep3_compute(0, t);
-                prep3_store(0, t, jobs[t]);
-            }
-            ctr_signal(nSolved, lane);
-        }
-        int P = 0;
-        for (int i = 0; i < nchunks; ++i) {
-            const int J = i & 1;
-            const int Pn = P == 2 ? 0 : P + 1;
-            const bool has_next = i + 1 < nchunks;
-            ctr_wait(nSolved, NC * (i + 1), fault);              // jobs of chunk i stored
-            if (has_next) ctr_wait_each(prodDone, NP, i + 2, fault);  // tiles of chunk i+1 written
-#pragma unroll
-            for (int t = 0; t < JPW; ++t) jobs[t] = prep3_compute(Pn, t);
-            chain_R(P);
-            chain_UO(P, J, t_beg + i * C, chunk_len(i));
-            chain_S(P);
-            ctr_signal(nFree, lane);
-            if (has_next) {
-#pragma unroll
-                for (int t = 0; t < JPW; ++t) prep3_store(1 - J, t, jobs[t]);
+                    for (int t = 0; t < JPW; ++t) {
+                        jobs[t] = prep3_compute(0, t);
+                        prep3_store(0, t, jobs[t]);
+                    }
+                }
                 ctr_signal(nSolved, lane);
             }
-            P = Pn;
-        }
+            int P = 0;
+            for (int i = 0; i < nchunks; ++i) {
+                const int J = i & 1;
+                const int Pn = P == 2 ? 0 : P + 1;
+                const bool has_next = i + 1 < nchunks;
+                ctr_wait(nSolved, NC * (i + 1), fault);  // jobs of chunk i stored
+                if (has_next) wait_tiles(i + 1);
+                if constexpr (kJobs) {
+#pragma unroll
+                    for (int t = 0; t < JPW; ++t) jobs[t] = prep3_compute(Pn, t);
+                }
+                chain_R(P);
+                chain_UO(P, J);
+                chain_S(P);
+                ctr_signal(nFree, lane);
+                if (has_next) {
+                    if constexpr (kJobs) {
+#pragma unroll
+                        for (int t = 0; t < JPW; ++t) prep3_store(1 - J, t, jobs[t]);
+                    }
+                    ctr_signal(nSolved, lane);
+                }
+                P = Pn;
+            }
+        };
+        if (NC < NJOB || wave < NJOB)
+            run(std::true_type{});
+        else
+            run(std::false_type{});
 
         // Every wave's last signal follows all of its waits, so a fault
         // recorded by any wave is visible after the last rendezvous.
@@ -768,12 +823,14 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         // key channels i0 .. i0 + 3 of this wave's channel strip, so that
         // consecutive lanes load consecutive bytes of a row.
         const int pw = wave - NC;
+        const int strip = pw % NPS;  // channel strip
+        const int par = pw / NPS;    // parity of the chunks this wave prepares (PP == 2)
         const int rg = lane / QW;
         const int cq = lane % QW;
-        const int gq = pw * QW + cq;
+        const int gq = strip * QW + cq;
         const bool qok = NQ >= QW || gq < NQ;  // idle lanes only when d_k < one strip
         const int i0 = 4 * min(gq, NQ - 1);
-        const int vlane = pw * 64 + lane;
+        const int vlane = strip * 64 + lane;
         const G* const qh = q + static_cast<size_t>(h) * DK;
         const G* const kh = k + static_cast<size_t>(h) * DK;
         const float* const lah = log_alpha + static_cast<size_t>(h) * DK;
@@ -795,8 +852,8 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         const int rowB = H * 4;
         const int offK = 4 * rg * rowK + i0 * GS;
         const int offLA = 4 * rg * rowLA + i0 * 4;
-        const bool loads_beta = pw == 0 && lane < C;  // beta of row `lane`, for the consumers
-        constexpr int NSET = BF16 ? 2 : 1;
+        const bool loads_beta = strip == 0 && lane < C;  // beta of row `lane`, for the consumers
+        constexpr int NSET = BF16 && PP == 1 ? 2 : 1;
         float4 rla[NSET][4];
         R4 rk[NSET][4], rq[NSET][4], rv[NSET][VPT][4];
         float rbeta[NSET];
@@ -819,8 +876,8 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
             rbeta[x] = buf_load_f1(r.b, loads_beta ? lane * rowB : kNoAccess, 0);
 #pragma unroll
             for (int vv = 0; vv < VPT; ++vv) {
-                const int idx = vlane + 64 * NP * vv;
-                const bool ok = VITEMS % (64 * NP) == 0 || idx < VITEMS;
+                const int idx = vlane + 64 * NPS * vv;
+                const bool ok = VITEMS % (64 * NPS) == 0 || idx < VITEMS;
                 const int c4 = 4 * (idx % (BV / 4));  // value-column quad (fastest: coalesced rows)
                 const int r0 = 4 * (idx / (BV / 4));
                 const int off = ok ? r0 * rowV + c4 * GS : kNoAccess;
@@ -841,8 +898,8 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
             if (loads_beta) sBeta(S)[lane] = rbeta[x];
 #pragma unroll
             for (int vv = 0; vv < VPT; ++vv) {
-                const int idx = vlane + 64 * NP * vv;
-                if (VITEMS % (64 * NP) == 0 || idx < VITEMS) {
+                const int idx = vlane + 64 * NPS * vv;
+                if (VITEMS % (64 * NPS) == 0 || idx < VITEMS) {
                     const int c4 = 4 * (idx % (BV / 4));
                     const int r0 = 4 * (idx / (BV / 4));
                     R4 cols[4];
@@ -912,29 +969,75 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                                  kbar[3][c]);
         };
 
-        // Chunk m uses register set m mod NSET and LDS slot m mod 3.  With
-        // two sets, an odd chunk count ends with one virtual chunk past the
-        // end (zero inputs): its tiles go to a slot every consumer has
-        // released and nothing reads them.
-        load_chunk(ic<0>{}, 0);
+        // Chunk m uses LDS slot m mod 3.  With two producer waves per strip
+        // (PP == 2) each takes the chunks of its parity; with one, its two
+        // register sets alternate (NSET == 2), and an odd chunk count ends
+        // with one virtual chunk past the end (zero inputs): its tiles go to
+        // a slot every consumer has released and nothing reads them.
+        constexpr int STRIDE = PP * NSET;  // chunks between two uses of one register set
+        const int m0 = PP == 2 ? par : 0;
+        load_chunk(ic<0>{}, m0);
         if constexpr (NSET == 2) {
             // issued in this order on every path into the loop, so the waits
             // for set 0 count set 1's loads as issued after it
             asm volatile("" ::: "memory");
-            load_chunk(ic<1>{}, 1);
+            load_chunk(ic<1>{}, m0 + 1);
         }
-        int P = 0;
+        // O of chunk j, staged by the consumers as O^T quads in the V^T tile
+        // of slot S: exactly the quads this wave's V items cover (so no other
+        // wave writes them before this wave has read them), transposed back
+        // to rows and stored like the V loads, coalesced.  Rows past the end
+        // of the sequence fall outside the range and are dropped.
+        G* const ohp = o + static_cast<size_t>(h) * dv + j0;
+        auto store_o = [&](int j, int S) __attribute__((always_inline)) {
+            const int c0 = t_beg + j * C;
+            const int len = __builtin_amdgcn_readfirstlane(chunk_len(j));
+            const auto r = buffer_rsrc(ohp + static_cast<size_t>(c0) * strideV, len * rowV);
+#pragma unroll
+            for (int vv = 0; vv < VPT; ++vv) {
+                const int idx = vlane + 64 * NPS * vv;
+                const bool ok = VITEMS % (64 * NPS) == 0 || idx < VITEMS;
+                const int c4 = ok ? 4 * (idx % (BV / 4)) : 0;
+                const int r0 = ok ? 4 * (idx / (BV / 4)) : 0;
+                R4 q4[4], rows[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) q4[c] = lds_get_raw4<BF16>(tile_at<BF16>(tVt(S), quad_off<BF16, UT>(c4 + c, r0 / 4)));
+                transpose4<BF16>(q4, rows);
+                const int off = ok ? r0 * rowV + c4 * GS : kNoAccess;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) buf_store_raw4<BF16>(r, off, rr * rowV, rows[rr]);
+            }
+        };
+
+        int P = m0;
         auto step = [&](auto X, int m) __attribute__((always_inline)) {
-            // slot P last held chunk m - 3: wait until every consumer released it
-            if (m >= 3) ctr_wait(nFree, NC * (m - 2), fault);
+            // slot P last held chunk m - 3: wait until every consumer released
+            // it, then store that chunk's O from it
+            if (m >= 3) {
+                ctr_wait(nFree, NC * (m - 2), fault);
+                store_o(m - 3, P);
+            }
             prep12(X, P);
             ctr_publish(prodDone + pw, m + 1, lane);
-            load_chunk(X, m + NSET);
-            P = P == 2 ? 0 : P + 1;
+            load_chunk(X, m + STRIDE);
+            P += PP;
+            if (P >= 3) P -= 3;
         };
-        for (int m = 0; m < nchunks; m += NSET) {
+        int m = m0;
+        for (; m < nchunks; m += STRIDE) {
             step(ic<0>{}, m);
             if constexpr (NSET == 2) step(ic<1>{}, m + 1);
+        }
+        // The last chunks' O stay in slots nobody refills: once every chunk is
+        // done, this wave stores those a continued loop would have.
+        if (m - 3 < nchunks) {
+            ctr_wait(nFree, NC * nchunks, fault);
+            for (; m - 3 < nchunks; m += PP) {
+                if (m >= 3) {
+                    const int j = m - 3;
+                    store_o(j, j % 3);
+                }
+            }
         }
     }
 }

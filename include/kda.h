@@ -72,8 +72,8 @@ typedef enum {
  *              non-decreasing, cu[N] = T_tot.  Its contents are read on the
  *              device only and are not checked (the caller's contract).
  *   N, T_tot, H        >= 1, >= 0, >= 1; T_tot * H * max(d_k, d_v) < 2^31
- *                      and H * max(d_k, d_v) <= 2^24 (32-bit element offsets
- *                      and 32-bit byte extents of one chunk's rows)
+ *                      and H * max(d_k, d_v) <= 2^20 (32-bit element offsets
+ *                      and 32-bit byte ranges of one chunk's rows)
  *   d_k, d_v           each one of 32, 64, 128
  *   dtype              storage type of q, k, v and o
  *   o          device [T_tot, H, d_v]  dtype      outputs (written)

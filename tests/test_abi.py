@@ -66,6 +66,7 @@ def _prefill(**kw):
     (dict(v_split=3), kda.KDA_ERR_INVALID_ARG, "v_split"),
     (dict(v_split=8), kda.KDA_ERR_INVALID_ARG, "v_split"),  # 64 / 8 < 16
     (dict(T_tot=2**31), kda.KDA_ERR_INVALID_ARG, "int32"),
+    (dict(T_tot=1, H=2**20 // 64 + 1), kda.KDA_ERR_INVALID_ARG, "2^20"),
 ])
 def test_prefill_rejects_invalid_arguments(kw, status, needle):
     assert _prefill(**kw) == status
