@@ -143,13 +143,16 @@ def _stream_handle(stream, device) -> int:
 
 
 def prefill(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=None,
-            v_split: int = 0, stream=None):
+            v_split: int = 0, workspace=None, stream=None):
     """KDA chunked prefill on torch tensors; returns (o, S_T).
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
     log_alpha: [T, H, d_k] fp32; beta: [T, H] fp32; S0: [N, H, d_k, d_v] fp32
     or None; cu_seqlens: int32 [N + 1] on the device (None = one sequence).
     ``S_T`` may be ``S0`` itself (in-place update of the states).
+    ``workspace`` (optional): a uint8 device tensor of at least
+    ``kda_prefill_workspace_size(...)`` bytes; one is allocated when needed
+    and not given.
     """
     import torch
     if not q.is_cuda:
@@ -176,7 +179,16 @@ def prefill(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=N
     _need(o, "o", (T, H, dv), q.dtype, dev)
     _need(S_T, "S_T", (N, H, dk, dv), torch.float32, dev)
     ws = kda_prefill_workspace_size(N, T, H, dk, dv, code)
-    wbuf = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+    wbuf = None
+    if ws:
+        if workspace is None:
+            wbuf = torch.empty(ws, dtype=torch.uint8, device=dev)
+        else:
+            if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+            if workspace.numel() < ws:
+                raise ValueError(f"workspace holds {workspace.numel()} bytes; {ws} are needed")
+            wbuf = workspace
     with torch.cuda.device(dev):
         _check(kda_prefill_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
                                  beta.data_ptr(), S0.data_ptr() if S0 is not None else None,

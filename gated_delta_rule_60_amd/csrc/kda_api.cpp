@@ -56,22 +56,18 @@ const char* kda_last_error(void) { return g_last_error.c_str(); }
 
 size_t kda_prefill_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
                                   kda_dtype dtype) {
-    (void)N;
-    (void)T_tot;
-    (void)H;
-    (void)d_k;
-    (void)d_v;
-    (void)dtype;
-    return 0;
+    if (N < 1 || H < 1 || T_tot < 0 || !supported_dim(d_k) || !supported_dim(d_v) ||
+        (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32))
+        return 0;
+    return kda::prefill_workspace_bytes(N, T_tot, H, d_k, d_v, dtype == KDA_DTYPE_BF16);
 }
 
 int32_t kda_prefill_default_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
                                   kda_dtype dtype) {
-    (void)T_tot;
-    if (N < 1 || H < 1 || !supported_dim(d_k) || !supported_dim(d_v) ||
+    if (N < 1 || H < 1 || T_tot < 0 || !supported_dim(d_k) || !supported_dim(d_v) ||
         (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32))
         return 0;
-    return kda::default_v_split(N, H, d_k, d_v, dtype == KDA_DTYPE_BF16);
+    return kda::default_v_split(N, T_tot, H, d_k, d_v, dtype == KDA_DTYPE_BF16);
 }
 
 kda_status kda_prefill_split(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -95,17 +91,24 @@ kda_status kda_prefill_split(const void* q, const void* k, const void* v, const 
     const void* ptrs[] = {q, k, v, log_alpha, o, S0, S_T};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-    if (workspace_bytes < kda_prefill_workspace_size(N, T_tot, H, d_k, d_v, dtype))
+    const size_t ws_need = kda_prefill_workspace_size(N, T_tot, H, d_k, d_v, dtype);
+    if (workspace_bytes < ws_need)
         return fail(KDA_ERR_INVALID_ARG, "workspace smaller than kda_prefill_workspace_size");
-    (void)workspace;
-    if (v_split == 0) v_split = kda::default_v_split(N, H, d_k, d_v, dtype == KDA_DTYPE_BF16);
+    if (ws_need > 0 && !workspace) return fail(KDA_ERR_INVALID_ARG, "workspace must not be NULL");
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (v_split == 0) v_split = kda::default_v_split(N, T_tot, H, d_k, d_v, dtype == KDA_DTYPE_BF16);
     if (!(v_split == 1 || v_split == 2 || v_split == 4 || v_split == 8) || d_v / v_split < 16)
         return fail(KDA_ERR_INVALID_ARG, "v_split must be 1, 2, 4 or 8 with d_v / v_split >= 16");
-    const int64_t grid = static_cast<int64_t>(N) * H * v_split;
-    if (grid > INT32_MAX) return fail(KDA_ERR_INVALID_ARG, "N * H * v_split too large");
+    // Workgroups of the prefill kernel: (sequence or segment, head, value
+    // slice[, identity run]); each has at most 1024 work-items.
+    const bool segmented = kda::prefill_segmented(N, T_tot, H, d_k, d_v);
+    const int64_t units = segmented ? N + T_tot / kda::kSegTokens : N;
+    const int64_t grid = units * H * v_split * (segmented ? 2 : 1);
+    if (grid > (int64_t{1} << 22)) return fail(KDA_ERR_INVALID_ARG, "N * H * v_split too large");
 
     kda::PrefillArgs a{q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
-                       dtype == KDA_DTYPE_BF16, o, S_T, v_split, stream};
+                       dtype == KDA_DTYPE_BF16, o, S_T, v_split, stream, workspace};
     (void)hipGetLastError();  // report only this launch's status
     const hipError_t e = kda::launch_prefill(a);
     if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");

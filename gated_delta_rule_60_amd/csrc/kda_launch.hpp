@@ -8,6 +8,30 @@
 
 namespace kda {
 
+// Segmented prefill.  When a batch has too few (sequence, head) pairs to
+// fill the GPU (N * H < kSegMaxPairs), sequences longer than kSegTokens run
+// as segments of kSegTokens tokens (the last one shorter), each segment of
+// each head in its own workgroups, so one long sequence spreads over many
+// CUs.  A segment after the first starts from the zero state, and an
+// identity run over it (V = 0, S0 = I) gives its transition M and
+// q^_t = M_t^T q_t; fix-up passes then add the true entering state's
+// contribution.  With enough pairs the extra identity work and fix-up
+// traffic cost more than the shorter critical path saves.
+constexpr int kSegTokens = 4096;
+constexpr int kSegMaxPairs = 128;
+
+// The device plan and workspace a segmented launch uses (units == nullptr:
+// whole sequences, one workgroup per (sequence, head, value slice)).
+struct SegView {
+    const int4* units;  // [count] {sequence, segment, token begin, token end}
+    const int* count;   // number of units
+    void* qhat;         // [T_tot][H][d_k] identity-run outputs q^ (storage type)
+    float* mstate;      // [umax][H][d_k][d_k] identity-run final states M
+    float* dstate;      // [umax][H][d_k][d_v] final states of later segments from the
+                        // zero state; the chain pass replaces them with entering states
+    int umax;           // units the grid covers
+};
+
 struct PrefillArgs {
     const void* q;
     const void* k;
@@ -24,6 +48,7 @@ struct PrefillArgs {
     float* S_T;
     int32_t v_split;  // 1, 2, 4, 8; d_v / v_split >= 16
     void* stream;
+    void* workspace;  // at least prefill_workspace_bytes(...) bytes
 };
 
 struct DecodeArgs {
@@ -40,9 +65,18 @@ struct DecodeArgs {
 };
 
 hipError_t launch_prefill(const PrefillArgs& a);
+
+// Whether a prefill of these sizes runs segmented, and the workspace bytes it
+// then needs (0 when it does not).
+bool prefill_segmented(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v);
+size_t prefill_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16);
+// Segmented prefill passes around the prefill kernel (kda_segment.hip): the
+// plan (before it) and the state chain plus output correction (after it).
+hipError_t launch_seg_plan(const PrefillArgs& a, SegView* view);
+hipError_t launch_seg_fixup(const PrefillArgs& a, const SegView& v);
 hipError_t launch_decode(const DecodeArgs& a);
 
 // Launch shape kda_prefill picks for these sizes (see kda_prefill.hip).
-int32_t default_v_split(int32_t N, int32_t H, int32_t d_k, int32_t d_v, bool bf16);
+int32_t default_v_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16);
 
 }  // namespace kda

@@ -396,7 +396,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
     const typename Elem<BF16>::G* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, const float* __restrict__ S0, const int32_t* __restrict__ cu,
     int N, int H, int dv, int v_split, typename Elem<BF16>::G* __restrict__ o,
-    float* __restrict__ S_T) {
+    float* __restrict__ S_T, SegView seg) {
     using Sh = PrefillShape<BF16, DK, NC, CT>;
     using T = Elem<BF16>;
     using E = typename T::E;
@@ -445,45 +445,85 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
 
     // ---- work assignment -------------------------------------------------
     // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs.
-    // Units (sequence, head) are laid out so the value slices of one unit run
-    // back to back on the same XCD (shared q/k/log alpha lines in its L2),
-    // and lower unit ids (dispatched first) are the longer sequences.
-    int unit, slice;
-    {
+    // Units are laid out so the value slices of one unit run back to back on
+    // the same XCD (shared q/k/log alpha lines in its L2), and lower unit ids
+    // (dispatched first) are the longer sequences or segments.
+    //
+    // Whole sequences: a unit is (sequence, head), with v_split value slices.
+    // Segments (seg.units set): a unit is (segment, head), with v_split value
+    // slices and, for a segment after the first, v_split slices of the
+    // identity run (V = 0, S0 = I over the d_k = d_v columns).  A later
+    // segment starts from the zero state; the segment fix-up adds what the
+    // true entering state contributes (linearity in (S0, V)).
+    auto xcd_map = [&](int units, int per_unit, int& unit_id, int& sub) __attribute__((always_inline)) {
         const int b = blockIdx.x;
-        const int units = N * H;
         if ((units & 7) == 0) {
             const int x = b & 7, qq = b >> 3;
-            unit = 8 * (qq / v_split) + x;
-            slice = qq % v_split;
+            unit_id = 8 * (qq / per_unit) + x;
+            sub = qq % per_unit;
         } else {
-            unit = b / v_split;
-            slice = b % v_split;
+            unit_id = b / per_unit;
+            sub = b % per_unit;
         }
-    }
-    const int h = unit % H;
-    const int rank = unit / H;
-    int n = rank;
-    if (N > 1 && N <= kSortMax) {
-        for (int i = tid; i < N; i += NT) sSeq[i] = cu[i + 1] - cu[i];
-        __syncthreads();
-        for (int i = tid; i < N; i += NT) {
-            const int li = sSeq[i];
-            int r = 0;
-            for (int j = 0; j < N; ++j) {
-                const int lj = sSeq[j];
-                r += (lj > li) || (lj == li && j < i);
+    };
+    int n, h, slice, t_beg, t_end;
+    int mode = 0;  // 0: S0 (or zero) start; 1: later segment, zero start; 2: identity run
+    const float* s0p;
+    float* sdst;  // this head's [DK][dv] block of the final state
+    G* obase;     // [T][H][dv] outputs (o, or the identity runs' q^ for mode 2)
+    if (seg.units == nullptr) {
+        int unit;
+        xcd_map(N * H, v_split, unit, slice);
+        h = unit % H;
+        const int rank = unit / H;
+        n = rank;
+        if (N > 1 && N <= kSortMax) {
+            for (int i = tid; i < N; i += NT) sSeq[i] = cu[i + 1] - cu[i];
+            __syncthreads();
+            for (int i = tid; i < N; i += NT) {
+                const int li = sSeq[i];
+                int r = 0;
+                for (int j = 0; j < N; ++j) {
+                    const int lj = sSeq[j];
+                    r += (lj > li) || (lj == li && j < i);
+                }
+                if (r == rank) sSeq[kSortMax] = i;
             }
-            if (r == rank) sSeq[kSortMax] = i;
+            __syncthreads();
+            n = sSeq[kSortMax];
         }
-        __syncthreads();
-        n = sSeq[kSortMax];
+        t_beg = cu[n];
+        t_end = cu[n + 1];
+        const size_t pair = static_cast<size_t>(n) * H + h;
+        s0p = S0 ? S0 + pair * DK * dv : nullptr;
+        sdst = S_T + pair * DK * dv;
+        obase = o;
+    } else {
+        int uh, sub;
+        xcd_map(seg.umax * H, 2 * v_split, uh, sub);
+        const int u = uh / H;
+        h = uh % H;
+        if (u >= *seg.count) return;  // whole workgroup: before any barrier
+        const int4 it = seg.units[u];
+        n = it.x;
+        t_beg = it.z;
+        t_end = it.w;
+        if (sub >= v_split) {
+            if (it.y == 0) return;  // the first segment needs no identity run
+            mode = 2;
+            slice = sub - v_split;
+        } else {
+            mode = it.y == 0 ? 0 : 1;
+            slice = sub;
+        }
+        const size_t pair = static_cast<size_t>(n) * H + h;
+        const size_t blk = static_cast<size_t>(u) * H + h;
+        s0p = mode == 0 && S0 ? S0 + pair * DK * dv : nullptr;
+        sdst = mode == 0 ? S_T + pair * DK * dv : (mode == 1 ? seg.dstate : seg.mstate) + blk * DK * dv;
+        obase = mode == 2 ? static_cast<G*>(seg.qhat) : o;
     }
-    const int t_beg = cu[n];
-    const int t_end = cu[n + 1];
     const int nchunks = (t_end - t_beg + C - 1) / C;
     const int j0 = slice * BV;  // first value column of this workgroup
-    const size_t pair = static_cast<size_t>(n) * H + h;
     auto chunk_len = [&](int i) __attribute__((always_inline)) { return min(C, t_end - (t_beg + i * C)); };
 
     // Per-token offsets below fit in 32 bits (the host rejects tensors of
@@ -519,7 +559,10 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
             for (int it = 0; it < DK / 16; ++it) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    Sr[ct][it][j] = S0 ? S0[(pair * DK + 16 * it + 4 * lg + j) * dv + col] : 0.f;
+                {
+                    const size_t row = 16 * it + 4 * lg + j;
+                    Sr[ct][it][j] = s0p ? s0p[row * dv + col] : (mode == 2 && row == col ? 1.f : 0.f);
+                }
             }
         }
 
@@ -812,7 +855,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
 #pragma unroll
             for (int it = 0; it < DK / 16; ++it) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) S_T[(pair * DK + 16 * it + 4 * lg + j) * dv + col] = Sr[ct][it][j];
+                for (int j = 0; j < 4; ++j) sdst[(16 * it + 4 * lg + j) * dv + col] = Sr[ct][it][j];
             }
         }
     } else if (wave < NC + NP) {
@@ -867,7 +910,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
             const size_t tok = static_cast<size_t>(c0) * strideK;
             return Rsrc{buffer_rsrc(kh + tok, len * rowK), buffer_rsrc(qh + tok, len * rowK),
                         buffer_rsrc(lah + tok, len * rowLA),
-                        buffer_rsrc(vh + static_cast<size_t>(c0) * strideV, len * rowV),
+                        buffer_rsrc(vh + static_cast<size_t>(c0) * strideV, mode == 2 ? 0 : len * rowV),
                         buffer_rsrc(bh + static_cast<size_t>(c0) * H, len * rowB)};
         };
         auto load_chunk = [&](auto X, int m) __attribute__((always_inline)) {
@@ -988,7 +1031,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         // wave writes them before this wave has read them), transposed back
         // to rows and stored like the V loads, coalesced.  Rows past the end
         // of the sequence fall outside the range and are dropped.
-        G* const ohp = o + static_cast<size_t>(h) * dv + j0;
+        G* const ohp = obase + static_cast<size_t>(h) * dv + j0;
         auto store_o = [&](int j, int S) __attribute__((always_inline)) {
             const int c0 = t_beg + j * C;
             const int len = __builtin_amdgcn_readfirstlane(chunk_len(j));
@@ -1048,47 +1091,58 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
 // 1 x 1 (16); producer waves follow d_k.
 // ---------------------------------------------------------------------------
 template <bool BF16, int DK, int NC, int CT>
-static hipError_t launch_prefill_t(const PrefillArgs& a) {
+static hipError_t launch_prefill_t(const PrefillArgs& a, const SegView& seg) {
     using G = typename Elem<BF16>::G;
     using Sh = PrefillShape<BF16, DK, NC, CT>;
-    const unsigned grid = static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H) *
-                          static_cast<unsigned>(a.v_split);
+    const unsigned units = seg.units ? static_cast<unsigned>(seg.umax) : static_cast<unsigned>(a.N);
+    const unsigned per_unit = static_cast<unsigned>(a.v_split) * (seg.units ? 2u : 1u);
+    const unsigned grid = units * static_cast<unsigned>(a.H) * per_unit;
     hipLaunchKernelGGL((prefill_kernel<BF16, DK, NC, CT>), dim3(grid), dim3(Sh::NT), 0,
                        static_cast<hipStream_t>(a.stream), static_cast<const G*>(a.q),
                        static_cast<const G*>(a.k), static_cast<const G*>(a.v), a.log_alpha, a.beta,
-                       a.S0, a.cu_seqlens, a.N, a.H, a.d_v, a.v_split, static_cast<G*>(a.o), a.S_T);
+                       a.S0, a.cu_seqlens, a.N, a.H, a.d_v, a.v_split, static_cast<G*>(a.o), a.S_T, seg);
     return hipGetLastError();
 }
 
 template <bool BF16, int DK>
-static hipError_t launch_prefill_dk(const PrefillArgs& a) {
+static hipError_t launch_prefill_dk(const PrefillArgs& a, const SegView& seg) {
     switch (a.d_v / a.v_split) {
-        case 128: return launch_prefill_t<BF16, DK, 4, 2>(a);
-        case 64: return launch_prefill_t<BF16, DK, 4, 1>(a);
-        case 32: return launch_prefill_t<BF16, DK, 2, 1>(a);
-        case 16: return launch_prefill_t<BF16, DK, 1, 1>(a);
+        case 128: return launch_prefill_t<BF16, DK, 4, 2>(a, seg);
+        case 64: return launch_prefill_t<BF16, DK, 4, 1>(a, seg);
+        case 32: return launch_prefill_t<BF16, DK, 2, 1>(a, seg);
+        case 16: return launch_prefill_t<BF16, DK, 1, 1>(a, seg);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <bool BF16>
-static hipError_t launch_prefill_dt(const PrefillArgs& a) {
+static hipError_t launch_prefill_dt(const PrefillArgs& a, const SegView& seg) {
     switch (a.d_k) {
-        case 32: return launch_prefill_dk<BF16, 32>(a);
-        case 64: return launch_prefill_dk<BF16, 64>(a);
-        case 128: return launch_prefill_dk<BF16, 128>(a);
+        case 32: return launch_prefill_dk<BF16, 32>(a, seg);
+        case 64: return launch_prefill_dk<BF16, 64>(a, seg);
+        case 128: return launch_prefill_dk<BF16, 128>(a, seg);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {
-    return a.bf16 ? launch_prefill_dt<true>(a) : launch_prefill_dt<false>(a);
+    SegView seg{};
+    const bool segmented = prefill_segmented(a.N, a.T_tot, a.H, a.d_k, a.d_v);
+    if (segmented) {
+        if (a.workspace == nullptr) return hipErrorInvalidValue;
+        const hipError_t e = launch_seg_plan(a, &seg);
+        if (e != hipSuccess) return e;
+    }
+    const hipError_t e = a.bf16 ? launch_prefill_dt<true>(a, seg) : launch_prefill_dt<false>(a, seg);
+    if (e != hipSuccess || !segmented) return e;
+    return launch_seg_fixup(a, seg);
 }
 
-int32_t default_v_split(int32_t N, int32_t H, int32_t d_k, int32_t d_v, bool bf16) {
-    (void)d_k;
+int32_t default_v_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16) {
     (void)bf16;
-    const int64_t units = static_cast<int64_t>(N) * H;
+    // Segmented runs: one unit per segment (bounded by N + T_tot / kSegTokens).
+    const int64_t seqs = prefill_segmented(N, T_tot, H, d_k, d_v) ? N + T_tot / kSegTokens : N;
+    const int64_t units = seqs * H;
     int32_t split = 1;
     // Aim for at least ~192 workgroups on the 256 CUs; every split shares the
     // same per-column arithmetic, so this only changes the launch shape.

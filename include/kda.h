@@ -79,11 +79,26 @@ typedef enum {
  *   o          device [T_tot, H, d_v]  dtype      outputs (written)
  *   S_T        device [N, H, d_k, d_v] float32    final states (written); may
  *              be the same pointer as S0.  An empty sequence gives S_T = S0.
- *   workspace, workspace_bytes   scratch of at least
- *              kda_prefill_workspace_size(...) bytes (currently 0; NULL allowed)
+ *   workspace, workspace_bytes   device scratch of at least
+ *              kda_prefill_workspace_size(...) bytes, 256-byte aligned (NULL
+ *              allowed when that size is 0).  Owned by the caller; the
+ *              library uses it until the work queued on `stream` ends, so
+ *              calls that may overlap need separate workspaces.
  *   stream     hipStream_t or NULL
  * q, k, v, log_alpha, beta and o may be NULL when T_tot == 0.  No state
  * crosses a sequence boundary.
+ *
+ * Long sequences.  When d_k == d_v, T_tot > 4096 and N * H < 128 (too few
+ * (sequence, head) pairs to fill the GPU), a sequence longer than 4096
+ * tokens runs as segments of 4096 tokens (the last one shorter) that are
+ * processed in parallel: a later segment starts from the zero state, an
+ * identity run over it (V = 0, S0 = I) gives its transition matrix M and the
+ * transformed queries M_t^T q_t, and fix-up passes chain the segments'
+ * entering states and add their contribution to the outputs.  The
+ * recurrence is linear in (S0, V), so this changes rounding only.  The split
+ * of a sequence depends on its own length and on whether the batch runs
+ * segmented: a sequence gives the same bits in any batch on the same side
+ * of that rule.
  */
 kda_status kda_prefill(const void* q, const void* k, const void* v,
                        const float* log_alpha, const float* beta, const float* S0,
@@ -107,7 +122,11 @@ kda_status kda_prefill_split(const void* q, const void* k, const void* v,
                              void* workspace, size_t workspace_bytes, int32_t v_split,
                              void* stream);
 
-/* Bytes of workspace kda_prefill needs for these sizes (0 in this version). */
+/* Bytes of workspace kda_prefill needs for these sizes: 0 unless the batch
+ * runs segmented (d_k == d_v, T_tot > 4096, N * H < 128); then the segment
+ * plan, the identity runs' outputs ([T_tot, H, d_k] in dtype) and two fp32
+ * [d_k, d_v] states per (segment, head) for at most N + T_tot / 4096
+ * segments.  0 for unsupported sizes. */
 size_t kda_prefill_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
                                   int32_t d_v, kda_dtype dtype);
 

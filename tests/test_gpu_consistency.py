@@ -28,9 +28,14 @@ def test_deterministic_and_split_invariant_bits(dtype):
             assert torch.equal(o, o0) and torch.equal(S, S0), f"v_split={split} rep={rep}"
 
 
-def test_packing_does_not_change_bits():
+@pytest.mark.parametrize("lengths", [[100, 0, 130, 64], [9000, 100, 0, 4097]],
+                         ids=["short", "segmented"])
+def test_packing_does_not_change_bits(lengths):
+    """A sequence gives the same bits alone or in any batch; with a batch
+    over 4096 tokens the long sequences run in segments, which depend on the
+    sequence's own length only."""
     import torch
-    x = _x([100, 0, 130, 64])
+    x = _x(lengths)
     d = upload(x)
     o, S = kda.prefill(**d)
     for n in range(x.N):
@@ -42,9 +47,10 @@ def test_packing_does_not_change_bits():
         assert torch.equal(on, o[a:b]) and torch.equal(Sn[0], S[n]), f"sequence {n}"
 
 
-def test_in_place_state_and_empty_sequences():
+@pytest.mark.parametrize("lengths", [[70, 0, 0, 10], [70, 0, 0, 4500]], ids=["short", "segmented"])
+def test_in_place_state_and_empty_sequences(lengths):
     import torch
-    x = _x([70, 0, 0, 10])
+    x = _x(lengths)
     d = upload(x)
     o, S = kda.prefill(**d)
     assert torch.equal(S[1], d["S0"][1]) and torch.equal(S[2], d["S0"][2])
@@ -68,9 +74,10 @@ def test_zero_tokens_copies_state():
     assert torch.count_nonzero(S) == 0
 
 
-def test_every_output_is_written():
+@pytest.mark.parametrize("lengths", [[1, 63, 64, 65, 127], [1, 4097, 5000, 65]], ids=["short", "segmented"])
+def test_every_output_is_written(lengths):
     import torch
-    x = _x([1, 63, 64, 65, 127], H=3)
+    x = _x(lengths, H=3)
     d = upload(x)
     o = torch.full((x.T_tot, 3, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
     ST = torch.full((x.N, 3, 128, 128), float("nan"), device="cuda")

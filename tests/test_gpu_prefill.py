@@ -69,6 +69,44 @@ def test_strong_decay_at_the_contract_limit(dtype, la_range):
         assert_close(host(ST), ref_S, dtype, "S_T")
 
 
+SEGMENTED = [
+    # lengths (some over 4096 tokens: run as 4096-token segments), H, d_k = d_v, dtype, s0
+    ([2 * 4096 + 77, 300, 4096, 4097], 2, 128, "bf16", True),
+    ([3 * 4096 + 5, 10], 1, 128, "f32", True),
+    ([4100, 0, 9000], 2, 64, "bf16", True),
+    ([8192, 1], 2, 32, "f32", False),
+]
+
+
+@pytest.mark.parametrize("case", SEGMENTED, ids=lambda c: f"L{'-'.join(map(str, c[0]))}_H{c[1]}_d{c[2]}_{c[3]}")
+def test_long_sequences_in_segments(case):
+    """Sequences past 4096 tokens run as parallel segments chained by the
+    fix-up passes: every output and final state against the oracle, and the
+    same bits for every launch shape."""
+    import torch
+    lengths, H, d, dtype, s0 = case
+    x = inputs.make_prefill_inputs(lengths, H, d, d, dtype, seed=sum(lengths) + d,
+                                   s0_std=1.0 if s0 else None)
+    code = kda.KDA_DTYPE_BF16 if dtype == "bf16" else kda.KDA_DTYPE_F32
+    assert kda.kda_prefill_workspace_size(x.N, x.T_tot, H, d, d, code) > 0
+    log(f"  oracle {lengths} H={H} d={d} {dtype}")
+    ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens)
+    dd = upload(x)
+    first = None
+    for split in valid_splits(d):
+        log(f"  segmented prefill v_split={split}")
+        o, ST = kda.prefill(**dd, v_split=split)
+        if first is None:
+            assert_close(host(o), ref_o, dtype, "o")
+            assert_close(host(ST), ref_S, dtype, "S_T")
+            for n in range(x.N):
+                a, b = x.cu_seqlens[n], x.cu_seqlens[n + 1]
+                assert_close(host(o[a:b]), ref_o[a:b], dtype, f"o sequence {n} (len {b - a})")
+            first = (o, ST)
+        else:
+            assert torch.equal(o, first[0]) and torch.equal(ST, first[1]), f"v_split={split}"
+
+
 def test_workload_t256_fp32():
     x = inputs.make_workload("prefill_t256_h2_d32_f32")
     ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens)
