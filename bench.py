@@ -11,6 +11,7 @@ the same run.  Inputs are seeded synthetic data already resident in HBM.
 Prints ONE JSON line.  ``value`` is prefill tokens/s; ``roofline`` is the
 prefill kernel against HBM bandwidth (algorithmic bytes / measured kernel
 time); ``decode`` holds the decode step's microseconds and its own roofline;
+``gdn`` the same prefill with one gate per token and head (Gated DeltaNet);
 ``cpu_baseline`` is the fp64 oracle on a bounded sample of the same
 workload, timed on this host's cores.
 """
@@ -33,11 +34,13 @@ BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
 CHUNK = 32
 
 
-def prefill_bytes(T_tot: int, N: int, H: int, dk: int, dv: int, esize: int) -> int:
+def prefill_bytes(T_tot: int, N: int, H: int, dk: int, dv: int, esize: int,
+                  scalar_gate: bool = False) -> int:
     """Algorithmic HBM bytes of one prefill: read q, k, v (esize each), log_alpha
-    (fp32), beta (fp32), write o (esize) per token-head; read S0 and write S_T
-    (fp32) per (sequence, head)."""
-    per_token_head = esize * (2 * dk + dv) + 4 * dk + 4 + esize * dv
+    (fp32: d_k values per token-head, one with a scalar gate), beta (fp32),
+    write o (esize) per token-head; read S0 and write S_T (fp32) per
+    (sequence, head)."""
+    per_token_head = esize * (2 * dk + dv) + 4 * (1 if scalar_gate else dk) + 4 + esize * dv
     return per_token_head * T_tot * H + 2 * 4 * dk * dv * N * H
 
 
@@ -118,7 +121,9 @@ def cpu_baseline(x, seconds: float):
             "cpu": cpu}
 
 
-def bench_prefill(kda, torch, x, steps: int, warmup: int, v_split: int):
+def bench_prefill(kda, torch, x, steps: int, warmup: int, v_split: int, scalar_gate: bool = False):
+    """Event-timed launches of kda_prefill (or gdn_prefill with the gate of
+    channel 0 per token and head when ``scalar_gate``)."""
 
     dev = torch.device("cuda:0")
     td = torch.bfloat16 if x.dtype == "bf16" else torch.float32
@@ -128,16 +133,18 @@ def bench_prefill(kda, torch, x, steps: int, warmup: int, v_split: int):
 
     # two resident input sets, alternated, so a step never starts with the
     # previous step's inputs sitting in the 256 MB MALL
+    la = x.log_alpha[:, :, 0].copy() if scalar_gate else x.log_alpha
+    run = kda.gdn_prefill_t if scalar_gate else kda.prefill
     sets = []
     for rot in range(2):
-        d = dict(q=up(x.q, td), k=up(x.k, td), v=up(x.v, td), log_alpha=up(x.log_alpha),
+        d = dict(q=up(x.q, td), k=up(x.k, td), v=up(x.v, td), log_alpha=up(la),
                  beta=up(x.beta), S0=None if x.S0 is None else up(x.S0),
                  cu_seqlens=torch.from_numpy(x.cu_seqlens).to(dev))
         d["o"] = torch.empty((x.T_tot, x.H, x.d_v), dtype=td, device=dev)
         d["S_T"] = torch.empty((x.N, x.H, x.d_k, x.d_v), dtype=torch.float32, device=dev)
         sets.append(d)
     for i in range(warmup):
-        kda.prefill(**sets[i % 2], v_split=v_split)
+        run(**sets[i % 2], v_split=v_split)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -146,7 +153,7 @@ def bench_prefill(kda, torch, x, steps: int, warmup: int, v_split: int):
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
-        kda.prefill(**sets[i % 2], v_split=v_split)
+        run(**sets[i % 2], v_split=v_split)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -223,6 +230,7 @@ def main():
     ap.add_argument("--decode-inputs", type=int, default=16,
                     help="distinct pre-generated decode-step inputs, cycled")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gdn", action="store_true", help="skip the scalar-gate (Gated DeltaNet) prefill line")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", type=float, default=0.0,
@@ -295,6 +303,19 @@ def main():
                          "traffic": measured_traffic("decode_step_kernel", "decode_n256_h32_d128_bf16",
                                                      ["kda_decode.hip", "kda_device.hpp"]),
                          "kernel": "kda::decode_step_kernel", "alg_bytes_per_launch": db},
+        }
+    if not args.no_gdn:
+        _, gms = bench_prefill(kda, torch, x, args.steps, args.warmup, split, scalar_gate=True)
+        g_avg_ms = sum(gms) / len(gms)
+        gb = prefill_bytes(x.T_tot, x.N, x.H, x.d_k, x.d_v, esize, scalar_gate=True)
+        gwl = args.workload + "_gdn"
+        out["gdn"] = {
+            "workload": gwl, "what": "gdn_prefill: one gate per token and head (channel 0 of the workload's gates)",
+            "tokens_per_s": x.T_tot / (g_avg_ms * 1e-3), "kernel_ms_avg": g_avg_ms, "kernel_ms_min": min(gms),
+            "roofline": {"bound": "hbm", "achieved": gb / (g_avg_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gb / (g_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("prefill_kernel", gwl, ["kda_prefill.hip", "kda_device.hpp"]),
+                         "kernel": "kda::prefill_kernel (scalar gate)", "alg_bytes_per_launch": gb},
         }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)

@@ -3,7 +3,8 @@
 The KDA recurrence S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1}
 + beta_t k_t v_t^T with read-out o_t = S_t^T q_t ("Kimi Linear：让长上下文大模型
 真正实用的线性注意力架构", section 三.5; per-channel alpha, section 三.1), as a
-chunk-parallel prefill and an in-place decode step, in hand-written HIP
+chunk-parallel prefill and an in-place decode step (and the scalar-gate
+Gated DeltaNet case of the same recurrence), in hand-written HIP
 kernels behind the C ABI of include/kda.h (libkda.so).
 
 ``import gated_delta_rule_60_amd`` does not load the library; the first call
@@ -18,6 +19,11 @@ from ._lib import (  # noqa: F401
     KDA_OK,
     KDAError,
     decode_step,
+    gdn_decode_step,
+    gdn_decode_step_t,
+    gdn_prefill,
+    gdn_prefill_split,
+    gdn_prefill_t,
     kda_decode_step,
     kda_last_error,
     kda_prefill,

@@ -35,6 +35,12 @@ SIGNATURES = {
     "kda_prefill_default_split": (_i32, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int]),
     "kda_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _i32, _i32, _i32, _i32,
                                        ctypes.c_int, _vp, _vp]),
+    "gdn_prefill": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32, _i32,
+                                   ctypes.c_int, _vp, _fp, _vp, _sz, _vp]),
+    "gdn_prefill_split": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32,
+                                         _i32, ctypes.c_int, _vp, _fp, _vp, _sz, _i32, _vp]),
+    "gdn_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _i32, _i32, _i32, _i32,
+                                       ctypes.c_int, _vp, _vp]),
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_last_error": (ctypes.c_char_p, []),
     "kda_version": (_i32, []),
@@ -96,6 +102,22 @@ def kda_decode_step(q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype, o, strea
     return load().kda_decode_step(q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype, o, stream)
 
 
+def gdn_prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
+                workspace, workspace_bytes, stream) -> int:
+    return load().gdn_prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype,
+                              o, S_T, workspace, workspace_bytes, stream)
+
+
+def gdn_prefill_split(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
+                      workspace, workspace_bytes, v_split, stream) -> int:
+    return load().gdn_prefill_split(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
+                                    dtype, o, S_T, workspace, workspace_bytes, v_split, stream)
+
+
+def gdn_decode_step(q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype, o, stream) -> int:
+    return load().gdn_decode_step(q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype, o, stream)
+
+
 def kda_status_string(status: int) -> str:
     return load().kda_status_string(status).decode()
 
@@ -142,12 +164,13 @@ def _stream_handle(stream, device) -> int:
     return int(s.cuda_stream)
 
 
-def prefill(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=None,
-            v_split: int = 0, workspace=None, stream=None):
-    """KDA chunked prefill on torch tensors; returns (o, S_T).
+def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream,
+             scalar_gate: bool):
+    """Chunked prefill on torch tensors; returns (o, S_T).
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
-    log_alpha: [T, H, d_k] fp32; beta: [T, H] fp32; S0: [N, H, d_k, d_v] fp32
+    log_alpha: [T, H, d_k] fp32 ([T, H] with ``scalar_gate``); beta: [T, H]
+    fp32; S0: [N, H, d_k, d_v] fp32
     or None; cu_seqlens: int32 [N + 1] on the device (None = one sequence).
     ``S_T`` may be ``S0`` itself (in-place update of the states).
     ``workspace`` (optional): a uint8 device tensor of at least
@@ -167,7 +190,7 @@ def prefill(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=N
     _need(q, "q", (T, H, dk), q.dtype, dev)
     _need(k, "k", (T, H, dk), q.dtype, dev)
     _need(v, "v", (T, H, dv), q.dtype, dev)
-    _need(log_alpha, "log_alpha", (T, H, dk), torch.float32, dev)
+    _need(log_alpha, "log_alpha", (T, H) if scalar_gate else (T, H, dk), torch.float32, dev)
     _need(beta, "beta", (T, H), torch.float32, dev)
     _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
     if S0 is not None:
@@ -189,8 +212,9 @@ def prefill(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=N
             if workspace.numel() < ws:
                 raise ValueError(f"workspace holds {workspace.numel()} bytes; {ws} are needed")
             wbuf = workspace
+    call = gdn_prefill_split if scalar_gate else kda_prefill_split
     with torch.cuda.device(dev):
-        _check(kda_prefill_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
+        _check(call(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
                                  beta.data_ptr(), S0.data_ptr() if S0 is not None else None,
                                  cu_seqlens.data_ptr(), N, T, H, dk, dv, code, o.data_ptr(),
                                  S_T.data_ptr(), wbuf.data_ptr() if wbuf is not None else None, ws,
@@ -198,8 +222,23 @@ def prefill(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=N
     return o, S_T
 
 
-def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
-    """One KDA decode step; S [N, H, d_k, d_v] fp32 is updated in place.
+def prefill(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=None,
+            v_split: int = 0, workspace=None, stream=None):
+    """KDA chunked prefill (per-channel gates, log_alpha [T, H, d_k]) on torch
+    tensors; returns (o, S_T).  Arguments as in ``_prefill``."""
+    return _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream, False)
+
+
+def gdn_prefill_t(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=None,
+                  v_split: int = 0, workspace=None, stream=None):
+    """Gated DeltaNet chunked prefill (one gate per token and head, log_alpha
+    [T, H]) on torch tensors; returns (o, S_T).  Arguments as in ``_prefill``."""
+    return _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream, True)
+
+
+
+def _decode(q, k, v, log_alpha, beta, S, o, stream, scalar_gate: bool):
+    """One decode step; S [N, H, d_k, d_v] fp32 is updated in place.
     Returns o [N, H, d_v] in q's dtype."""
     import torch
     if not q.is_cuda:
@@ -211,14 +250,27 @@ def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
     _need(q, "q", (N, H, dk), q.dtype, dev)
     _need(k, "k", (N, H, dk), q.dtype, dev)
     _need(v, "v", (N, H, dv), q.dtype, dev)
-    _need(log_alpha, "log_alpha", (N, H, dk), torch.float32, dev)
+    _need(log_alpha, "log_alpha", (N, H) if scalar_gate else (N, H, dk), torch.float32, dev)
     _need(beta, "beta", (N, H), torch.float32, dev)
     _need(S, "S", (N, H, dk, dv), torch.float32, dev)
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     _need(o, "o", (N, H, dv), q.dtype, dev)
+    call = gdn_decode_step if scalar_gate else kda_decode_step
     with torch.cuda.device(dev):
-        _check(kda_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
+        _check(call(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
                                beta.data_ptr(), S.data_ptr(), N, H, dk, dv, code, o.data_ptr(),
                                _stream_handle(stream, dev)))
     return o
+
+
+def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
+    """One KDA decode step (log_alpha [N, H, d_k]); S [N, H, d_k, d_v] fp32 is
+    updated in place.  Returns o [N, H, d_v] in q's dtype."""
+    return _decode(q, k, v, log_alpha, beta, S, o, stream, False)
+
+
+def gdn_decode_step_t(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
+    """One Gated DeltaNet decode step (log_alpha [N, H]); S is updated in
+    place.  Returns o [N, H, d_v] in q's dtype."""
+    return _decode(q, k, v, log_alpha, beta, S, o, stream, True)

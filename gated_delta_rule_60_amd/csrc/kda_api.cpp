@@ -70,11 +70,18 @@ int32_t kda_prefill_default_split(int32_t N, int64_t T_tot, int32_t H, int32_t d
     return kda::default_v_split(N, T_tot, H, d_k, d_v, dtype == KDA_DTYPE_BF16);
 }
 
-kda_status kda_prefill_split(const void* q, const void* k, const void* v, const float* log_alpha,
-                             const float* beta, const float* S0, const int32_t* cu_seqlens,
-                             int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
-                             kda_dtype dtype, void* o, float* S_T, void* workspace,
-                             size_t workspace_bytes, int32_t v_split, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the per-channel (KDA) and scalar (GDN) gate entry points: the
+// scalar gate changes only the shape of log_alpha ([T_tot, H], 4-byte
+// aligned).
+kda_status prefill_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
+                        int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
+                        float* S_T, void* workspace, size_t workspace_bytes, int32_t v_split,
+                        void* stream, bool scalar_gate) {
     g_last_error.clear();
     if (N < 1 || H < 1 || T_tot < 0)
         return fail(KDA_ERR_INVALID_ARG, "need N >= 1, H >= 1 and T_tot >= 0");
@@ -88,9 +95,11 @@ kda_status kda_prefill_split(const void* q, const void* k, const void* v, const 
         return fail(KDA_ERR_INVALID_ARG, "q, k, v, o and log_alpha must each hold fewer than 2^31 elements");
     if (static_cast<int64_t>(H) * (d_k > d_v ? d_k : d_v) > (int64_t{1} << 20))
         return fail(KDA_ERR_INVALID_ARG, "H * max(d_k, d_v) must not exceed 2^20");
-    const void* ptrs[] = {q, k, v, log_alpha, o, S0, S_T};
+    const void* ptrs[] = {q, k, v, scalar_gate ? nullptr : log_alpha, o, S0, S_T};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (scalar_gate && log_alpha && (reinterpret_cast<uintptr_t>(log_alpha) & 3u) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "log_alpha must be 4-byte aligned");
     const size_t ws_need = kda_prefill_workspace_size(N, T_tot, H, d_k, d_v, dtype);
     if (workspace_bytes < ws_need)
         return fail(KDA_ERR_INVALID_ARG, "workspace smaller than kda_prefill_workspace_size");
@@ -108,39 +117,84 @@ kda_status kda_prefill_split(const void* q, const void* k, const void* v, const 
     if (grid > (int64_t{1} << 22)) return fail(KDA_ERR_INVALID_ARG, "N * H * v_split too large");
 
     kda::PrefillArgs a{q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
-                       dtype == KDA_DTYPE_BF16, o, S_T, v_split, stream, workspace};
+                       dtype == KDA_DTYPE_BF16, o, S_T, v_split, stream, workspace, scalar_gate};
     (void)hipGetLastError();  // report only this launch's status
     const hipError_t e = kda::launch_prefill(a);
     if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
     return KDA_OK;
 }
 
-kda_status kda_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
-                       const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
-                       int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
-                       float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
-    return kda_prefill_split(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype,
-                             o, S_T, workspace, workspace_bytes, 0, stream);
-}
-
-kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
-                           const float* beta, float* S, int32_t N, int32_t H, int32_t d_k,
-                           int32_t d_v, kda_dtype dtype, void* o, void* stream) {
+kda_status decode_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                       const float* beta, float* S, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                       kda_dtype dtype, void* o, void* stream, bool scalar_gate) {
     g_last_error.clear();
     if (N < 1 || H < 1) return fail(KDA_ERR_INVALID_ARG, "need N >= 1 and H >= 1");
     const kda_status ds = check_dims(d_k, d_v, dtype);
     if (ds != KDA_OK) return ds;
     if (!q || !k || !v || !log_alpha || !beta || !S || !o)
         return fail(KDA_ERR_INVALID_ARG, "q, k, v, log_alpha, beta, S and o must not be NULL");
-    const void* ptrs[] = {q, k, v, log_alpha, S, o};
+    const void* ptrs[] = {q, k, v, scalar_gate ? nullptr : log_alpha, S, o};
     for (const void* p : ptrs)
-        if (!aligned16(p)) return fail(KDA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+        if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (scalar_gate && (reinterpret_cast<uintptr_t>(log_alpha) & 3u) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "log_alpha must be 4-byte aligned");
     if (static_cast<int64_t>(N) * H > INT32_MAX) return fail(KDA_ERR_INVALID_ARG, "N * H too large");
-    kda::DecodeArgs a{q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype == KDA_DTYPE_BF16, o, stream};
+    kda::DecodeArgs a{q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype == KDA_DTYPE_BF16, o, stream,
+                      scalar_gate};
     (void)hipGetLastError();  // report only this launch's status
     const hipError_t e = kda::launch_decode(a);
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill_split(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, const float* S0, const int32_t* cu_seqlens,
+                             int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
+                             kda_dtype dtype, void* o, float* S_T, void* workspace,
+                             size_t workspace_bytes, int32_t v_split, void* stream) {
+    return prefill_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
+                        workspace, workspace_bytes, v_split, stream, false);
+}
+
+kda_status kda_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
+                       const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
+                       int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
+                       float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
+                        workspace, workspace_bytes, 0, stream, false);
+}
+
+kda_status gdn_prefill_split(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, const float* S0, const int32_t* cu_seqlens,
+                             int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
+                             kda_dtype dtype, void* o, float* S_T, void* workspace,
+                             size_t workspace_bytes, int32_t v_split, void* stream) {
+    return prefill_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
+                        workspace, workspace_bytes, v_split, stream, true);
+}
+
+kda_status gdn_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
+                       const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
+                       int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
+                       float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
+                        workspace, workspace_bytes, 0, stream, true);
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* beta, float* S, int32_t N, int32_t H, int32_t d_k,
+                           int32_t d_v, kda_dtype dtype, void* o, void* stream) {
+    return decode_impl(q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype, o, stream, false);
+}
+
+kda_status gdn_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* beta, float* S, int32_t N, int32_t H, int32_t d_k,
+                           int32_t d_v, kda_dtype dtype, void* o, void* stream) {
+    return decode_impl(q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype, o, stream, true);
 }
 
 }  // extern "C"

@@ -14,6 +14,9 @@
 // per CU walks the (sequence, head) pairs, and each workgroup loads the
 // next pair's state while it reduces and updates the current one.  State
 // accesses are non-temporal (each byte is touched once per step).
+//
+// A scalar gate (Gated DeltaNet, one alpha per head: the same page, section
+// 三.1) reads one log alpha per pair and uses it for every channel.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -44,7 +47,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_step_kernel(
     const typename Elem<BF16>::G* __restrict__ q, const typename Elem<BF16>::G* __restrict__ k,
     const typename Elem<BF16>::G* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, float* __restrict__ S, int npairs,
-    typename Elem<BF16>::G* __restrict__ o) {
+    typename Elem<BF16>::G* __restrict__ o, int la_pair, int la_chan) {
     using T = Elem<BF16>;
     using Sh = DecodeShape<DK, DV>;
     constexpr int NT = Sh::NT, CQ = Sh::CQ, NRG = Sh::NRG, RPT = Sh::RPT;
@@ -80,7 +83,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_step_kernel(
         for (int i = tid; i < DK; i += NT) {
             s_k[i] = T::to_f32(k[tk + i]);
             s_q[i] = T::to_f32(q[tk + i]);
-            s_a[i] = exp_e(log_alpha[tk + i]);
+            s_a[i] = exp_e(log_alpha[static_cast<size_t>(la_pair) * pair + la_chan * i]);
         }
         __syncthreads();
 
@@ -187,7 +190,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
                        dim3(DecodeShape<DK, DV>::NT), 0, static_cast<hipStream_t>(a.stream),
                        static_cast<const G*>(a.q), static_cast<const G*>(a.k),
                        static_cast<const G*>(a.v), a.log_alpha, a.beta, a.S, static_cast<int>(npairs),
-                       static_cast<G*>(a.o));
+                       static_cast<G*>(a.o), a.scalar_gate ? 1 : DK, a.scalar_gate ? 0 : 1);
     return hipGetLastError();
 }
 

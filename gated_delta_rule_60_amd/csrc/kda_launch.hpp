@@ -49,6 +49,7 @@ struct PrefillArgs {
     int32_t v_split;  // 1, 2, 4, 8; d_v / v_split >= 16
     void* stream;
     void* workspace;  // at least prefill_workspace_bytes(...) bytes
+    bool scalar_gate = false;  // log_alpha is [T_tot, H] (one gate per token and head)
 };
 
 struct DecodeArgs {
@@ -62,6 +63,7 @@ struct DecodeArgs {
     bool bf16;
     void* o;
     void* stream;
+    bool scalar_gate = false;  // log_alpha is [N, H] (one gate per sequence and head)
 };
 
 hipError_t launch_prefill(const PrefillArgs& a);

@@ -390,7 +390,10 @@ __device__ __forceinline__ void ctr_wait_each(int* ctrs, int n, int target, int*
 
 }  // namespace
 
-template <bool BF16, int DK, int NC, int CT>
+// SG: scalar gate (one log alpha per token and head, [T, H]: Gated DeltaNet);
+// otherwise one per key channel ([T, H, d_k]: KDA).  A scalar gate is the
+// per-channel computation with the value repeated over the channels.
+template <bool BF16, int DK, int NC, int CT, bool SG>
 __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_kernel(
     const typename Elem<BF16>::G* __restrict__ q, const typename Elem<BF16>::G* __restrict__ k,
     const typename Elem<BF16>::G* __restrict__ v, const float* __restrict__ log_alpha,
@@ -876,7 +879,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         const int vlane = strip * 64 + lane;
         const G* const qh = q + static_cast<size_t>(h) * DK;
         const G* const kh = k + static_cast<size_t>(h) * DK;
-        const float* const lah = log_alpha + static_cast<size_t>(h) * DK;
+        const float* const lah = log_alpha + static_cast<size_t>(h) * (SG ? 1 : DK);
         const float* const bh = beta + h;
         const G* const vh = v + static_cast<size_t>(h) * dv + j0;
 
@@ -890,11 +893,12 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
         // set never waits for the other.
         constexpr int GS = static_cast<int>(sizeof(G));
         const int rowK = strideK * GS;  // bytes per token row of q and k
-        const int rowLA = strideK * 4;
+        const int strideLA = SG ? H : strideK;  // floats per token row of log alpha
+        const int rowLA = strideLA * 4;
         const int rowV = strideV * GS;
         const int rowB = H * 4;
         const int offK = 4 * rg * rowK + i0 * GS;
-        const int offLA = 4 * rg * rowLA + i0 * 4;
+        const int offLA = 4 * rg * rowLA + (SG ? 0 : i0 * 4);
         const bool loads_beta = strip == 0 && lane < C;  // beta of row `lane`, for the consumers
         constexpr int NSET = BF16 && PP == 1 ? 2 : 1;
         float4 rla[NSET][4];
@@ -909,7 +913,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
             const int len = __builtin_amdgcn_readfirstlane(max(0, chunk_len(m)));
             const size_t tok = static_cast<size_t>(c0) * strideK;
             return Rsrc{buffer_rsrc(kh + tok, len * rowK), buffer_rsrc(qh + tok, len * rowK),
-                        buffer_rsrc(lah + tok, len * rowLA),
+                        buffer_rsrc(lah + static_cast<size_t>(c0) * strideLA, len * rowLA),
                         buffer_rsrc(vh + static_cast<size_t>(c0) * strideV, mode == 2 ? 0 : len * rowV),
                         buffer_rsrc(bh + static_cast<size_t>(c0) * H, len * rowB)};
         };
@@ -929,7 +933,12 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
             }
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                rla[x][rr] = buf_load_f4(r.la, offLA, rr * rowLA);
+                if constexpr (SG) {
+                    const float a = buf_load_f1(r.la, offLA, rr * rowLA);
+                    rla[x][rr] = make_float4(a, a, a, a);
+                } else {
+                    rla[x][rr] = buf_load_f4(r.la, offLA, rr * rowLA);
+                }
                 rk[x][rr] = buf_load_raw4<BF16>(r.k, offK, rr * rowK);
                 rq[x][rr] = buf_load_raw4<BF16>(r.q, offK, rr * rowK);
             }
@@ -1090,27 +1099,33 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
 // BV = d_v / v_split: 4 waves x 2 tiles (128), 4 x 1 (64), 2 x 1 (32),
 // 1 x 1 (16); producer waves follow d_k.
 // ---------------------------------------------------------------------------
-template <bool BF16, int DK, int NC, int CT>
+template <bool BF16, int DK, int NC, int CT, bool SG>
 static hipError_t launch_prefill_t(const PrefillArgs& a, const SegView& seg) {
     using G = typename Elem<BF16>::G;
     using Sh = PrefillShape<BF16, DK, NC, CT>;
     const unsigned units = seg.units ? static_cast<unsigned>(seg.umax) : static_cast<unsigned>(a.N);
     const unsigned per_unit = static_cast<unsigned>(a.v_split) * (seg.units ? 2u : 1u);
     const unsigned grid = units * static_cast<unsigned>(a.H) * per_unit;
-    hipLaunchKernelGGL((prefill_kernel<BF16, DK, NC, CT>), dim3(grid), dim3(Sh::NT), 0,
+    hipLaunchKernelGGL((prefill_kernel<BF16, DK, NC, CT, SG>), dim3(grid), dim3(Sh::NT), 0,
                        static_cast<hipStream_t>(a.stream), static_cast<const G*>(a.q),
                        static_cast<const G*>(a.k), static_cast<const G*>(a.v), a.log_alpha, a.beta,
                        a.S0, a.cu_seqlens, a.N, a.H, a.d_v, a.v_split, static_cast<G*>(a.o), a.S_T, seg);
     return hipGetLastError();
 }
 
+template <bool BF16, int DK, int NC, int CT>
+static hipError_t launch_prefill_sg(const PrefillArgs& a, const SegView& seg) {
+    return a.scalar_gate ? launch_prefill_t<BF16, DK, NC, CT, true>(a, seg)
+                         : launch_prefill_t<BF16, DK, NC, CT, false>(a, seg);
+}
+
 template <bool BF16, int DK>
 static hipError_t launch_prefill_dk(const PrefillArgs& a, const SegView& seg) {
     switch (a.d_v / a.v_split) {
-        case 128: return launch_prefill_t<BF16, DK, 4, 2>(a, seg);
-        case 64: return launch_prefill_t<BF16, DK, 4, 1>(a, seg);
-        case 32: return launch_prefill_t<BF16, DK, 2, 1>(a, seg);
-        case 16: return launch_prefill_t<BF16, DK, 1, 1>(a, seg);
+        case 128: return launch_prefill_sg<BF16, DK, 4, 2>(a, seg);
+        case 64: return launch_prefill_sg<BF16, DK, 4, 1>(a, seg);
+        case 32: return launch_prefill_sg<BF16, DK, 2, 1>(a, seg);
+        case 16: return launch_prefill_sg<BF16, DK, 1, 1>(a, seg);
         default: return hipErrorInvalidValue;
     }
 }

@@ -153,6 +153,41 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
                            void* stream);
 
+/*
+ * Gated DeltaNet: the scalar-gate case of the same recurrence, with one
+ * forgetting rate per head instead of one per key channel (the page's
+ * section 三.1 contrasts the two):
+ *
+ *     S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   a_t = exp(log_alpha[t, h])
+ *
+ * gdn_prefill, gdn_prefill_split and gdn_decode_step take the arguments of
+ * kda_prefill, kda_prefill_split and kda_decode_step, with these changes:
+ *   - log_alpha is device [T_tot, H] (prefill) or [N, H] (decode), float32,
+ *     4-byte aligned;
+ *   - the numerical contract applies to the per-head decay;
+ *   - the workspace is sized by kda_prefill_workspace_size, and the launch
+ *     shape by kda_prefill_default_split.
+ * Results are bit-identical to the kda_* calls with log_alpha repeated over
+ * the d_k channels.
+ */
+kda_status gdn_prefill(const void* q, const void* k, const void* v,
+                       const float* log_alpha, const float* beta, const float* S0,
+                       const int32_t* cu_seqlens, int32_t N, int64_t T_tot, int32_t H,
+                       int32_t d_k, int32_t d_v, kda_dtype dtype, void* o, float* S_T,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+kda_status gdn_prefill_split(const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, const float* S0,
+                             const int32_t* cu_seqlens, int32_t N, int64_t T_tot, int32_t H,
+                             int32_t d_k, int32_t d_v, kda_dtype dtype, void* o, float* S_T,
+                             void* workspace, size_t workspace_bytes, int32_t v_split,
+                             void* stream);
+
+kda_status gdn_decode_step(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, float* S, int32_t N,
+                           int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
+                           void* stream);
+
 /* Static text for a status code. */
 const char* kda_status_string(kda_status status);
 

@@ -22,7 +22,8 @@ import numpy as np
 
 from .build import build_oracle, library_path
 
-__all__ = ["prefill", "decode_step", "build_oracle", "library_path", "load", "bind"]
+__all__ = ["prefill", "decode_step", "gdn_prefill", "gdn_decode_step", "build_oracle", "library_path",
+           "load", "bind"]
 
 _LIB = None
 
@@ -149,3 +150,24 @@ def decode_step(q, k, v, log_alpha, beta, S: np.ndarray,
     if rc != 0:
         raise RuntimeError(f"kda_oracle_decode_step failed with status {rc}")
     return o
+
+
+def gdn_prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, **kw):
+    """Gated DeltaNet: one forgetting rate per head and token (log_alpha
+    [T, H]) instead of one per key channel, the contrast drawn in section 三.1
+    of the same page.  It is the recurrence above with alpha_t[i] = a_t for
+    every channel i, so the same fp64 loop runs on log_alpha repeated over
+    the d_k channels."""
+    q = np.asarray(q)
+    la = np.asarray(log_alpha, dtype=np.float32)
+    la = np.ascontiguousarray(np.broadcast_to(la[:, :, None], la.shape + (q.shape[2],)))
+    return prefill(q, k, v, la, beta, S0, cu_seqlens, **kw)
+
+
+def gdn_decode_step(q, k, v, log_alpha, beta, S: np.ndarray, **kw):
+    """One Gated DeltaNet decode step (log_alpha [N, H]); S is updated in
+    place, as in ``decode_step``."""
+    q = np.asarray(q)
+    la = np.asarray(log_alpha, dtype=np.float32)
+    la = np.ascontiguousarray(np.broadcast_to(la[:, :, None], la.shape + (q.shape[2],)))
+    return decode_step(q, k, v, la, beta, S, **kw)

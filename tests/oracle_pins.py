@@ -116,19 +116,28 @@ def pin_deltanet_when_alpha_is_one(lib):
 
 def pin_gated_deltanet_scalar_gate(lib):
     """alpha_t[i] == a_t for every channel: Gated DeltaNet (one forgetting rate
-    per head, page section 三.1), S_t = a_t (I - b k k^T) S_{t-1} + b k v^T."""
+    per head, page section 三.1), S_t = a_t (I - b k k^T) S_{t-1} + b k v^T,
+    written as matrices; checks the oracle's scalar-gate entry points
+    (prefill over two sequences and decode steps)."""
     rng = np.random.default_rng(102)
-    q, k, v, la, beta, S0, cu = _random_case(rng, [20], H=2, dk=4, dv=5)
-    la[:] = la[:, :, :1]
-    o, ST = oracle.prefill(q, k, v, la, beta, S0, cu, lib=lib)
-    for h in range(2):
-        S = S0[0, h].copy()
-        for t in range(20):
-            a = np.exp(np.float64(la[t, h, 0]))
-            kt = k[t, h].astype(np.float64)[:, None]
-            S = a * ((np.eye(4) - beta[t, h] * kt @ kt.T) @ S) + beta[t, h] * kt @ v[t, h][None, :].astype(np.float64)
-            _close(o[t, h], S.T @ q[t, h].astype(np.float64), f"o[{t},{h}]")
-        _close(ST[0, h], S, "S_T")
+    lengths = [20, 7]
+    q, k, v, la, beta, S0, cu = _random_case(rng, lengths, H=2, dk=4, dv=5)
+    la2 = np.ascontiguousarray(la[:, :, 0])
+    o, ST = oracle.gdn_prefill(q, k, v, la2, beta, S0, cu, lib=lib)
+    for n in range(2):
+        for h in range(2):
+            S = S0[n, h].copy()
+            for t in range(cu[n], cu[n + 1]):
+                a = np.exp(np.float64(la2[t, h]))
+                kt = k[t, h].astype(np.float64)[:, None]
+                S = a * ((np.eye(4) - beta[t, h] * kt @ kt.T) @ S) + beta[t, h] * kt @ v[t, h][None, :].astype(np.float64)
+                _close(o[t, h], S.T @ q[t, h].astype(np.float64), f"o[{t},{h}]")
+            _close(ST[n, h], S, f"S_T[{n},{h}]")
+    # decode: the first 5 tokens of sequence 0 as steps of a batch of one
+    S = S0[:1].copy()
+    for t in range(5):
+        od = oracle.gdn_decode_step(q[t:t + 1], k[t:t + 1], v[t:t + 1], la2[t:t + 1], beta[t:t + 1], S, lib=lib)
+        _close(od[0], o[t], f"decode o[{t}]")
 
 
 def pin_exact_retrieval(lib):

@@ -83,6 +83,21 @@ def test_prefill_entry_point_validates_too():
     assert rc == kda.KDA_ERR_UNSUPPORTED
 
 
+def test_gdn_entry_points_validate_the_per_head_gate():
+    args = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, S0=None, cu_seqlens=FAKE, N=1, T_tot=64, H=2,
+                d_k=64, d_v=64, dtype=BF16, o=FAKE, S_T=FAKE, workspace=None, workspace_bytes=0,
+                v_split=0, stream=None)
+    # [T, H] fp32: 4-byte alignment is enough, 2 is not
+    assert kda.gdn_prefill_split(log_alpha=FAKE + 2, **args) == kda.KDA_ERR_INVALID_ARG
+    assert "4-byte" in kda.kda_last_error()
+    assert kda.gdn_prefill_split(log_alpha=None, **args) == kda.KDA_ERR_INVALID_ARG
+    assert kda.gdn_prefill_split(log_alpha=FAKE, **dict(args, d_k=48)) == kda.KDA_ERR_UNSUPPORTED
+    assert kda.gdn_decode_step(FAKE, FAKE, FAKE, FAKE + 2, FAKE, FAKE, 4, 2, 64, 64, BF16, FAKE,
+                               None) == kda.KDA_ERR_INVALID_ARG
+    assert kda.gdn_decode_step(FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 2, 64, 64, BF16, FAKE,
+                               None) == kda.KDA_ERR_INVALID_ARG
+
+
 def _decode(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, log_alpha=FAKE, beta=FAKE, S=FAKE, N=4, H=2, d_k=128, d_v=128,
              dtype=F32, o=FAKE, stream=None)
