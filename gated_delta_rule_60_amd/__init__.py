@@ -17,6 +17,8 @@ from ._lib import (  # noqa: F401
     KDA_ERR_INVALID_ARG,
     KDA_ERR_UNSUPPORTED,
     KDA_OK,
+    KDA_PREFILL_SCALAR_GATE,
+    KDA_PREFILL_WIDE_DECAY,
     KDAError,
     decode_step,
     gdn_decode_step,
@@ -28,6 +30,7 @@ from ._lib import (  # noqa: F401
     kda_last_error,
     kda_prefill,
     kda_prefill_default_split,
+    kda_prefill_ex,
     kda_prefill_split,
     kda_prefill_workspace_size,
     kda_status_string,

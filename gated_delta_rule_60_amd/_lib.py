@@ -19,6 +19,8 @@ KDA_ERR_UNSUPPORTED = 2
 KDA_ERR_HIP = 3
 KDA_DTYPE_BF16 = 0
 KDA_DTYPE_F32 = 1
+KDA_PREFILL_SCALAR_GATE = 1
+KDA_PREFILL_WIDE_DECAY = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -31,6 +33,8 @@ SIGNATURES = {
                                    ctypes.c_int, _vp, _fp, _vp, _sz, _vp]),
     "kda_prefill_split": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32,
                                          _i32, ctypes.c_int, _vp, _fp, _vp, _sz, _i32, _vp]),
+    "kda_prefill_ex": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32, _i32,
+                                      ctypes.c_int, _vp, _fp, _vp, _sz, _i32, ctypes.c_uint32, _vp]),
     "kda_prefill_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int]),
     "kda_prefill_default_split": (_i32, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int]),
     "kda_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _i32, _i32, _i32, _i32,
@@ -88,6 +92,12 @@ def kda_prefill_split(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k
                       workspace, workspace_bytes, v_split, stream) -> int:
     return load().kda_prefill_split(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
                                     dtype, o, S_T, workspace, workspace_bytes, v_split, stream)
+
+
+def kda_prefill_ex(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
+                   workspace, workspace_bytes, v_split, flags, stream) -> int:
+    return load().kda_prefill_ex(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
+                                 dtype, o, S_T, workspace, workspace_bytes, v_split, flags, stream)
 
 
 def kda_prefill_workspace_size(N, T_tot, H, d_k, d_v, dtype) -> int:
@@ -165,7 +175,7 @@ def _stream_handle(stream, device) -> int:
 
 
 def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream,
-             scalar_gate: bool):
+             scalar_gate: bool, wide_decay: bool = False):
     """Chunked prefill on torch tensors; returns (o, S_T).
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
@@ -175,7 +185,8 @@ def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspac
     ``S_T`` may be ``S0`` itself (in-place update of the states).
     ``workspace`` (optional): a uint8 device tensor of at least
     ``kda_prefill_workspace_size(...)`` bytes; one is allocated when needed
-    and not given.
+    and not given.  ``wide_decay`` selects the wide-decay kernel variant
+    (KDA_PREFILL_WIDE_DECAY).
     """
     import torch
     if not q.is_cuda:
@@ -212,28 +223,30 @@ def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspac
             if workspace.numel() < ws:
                 raise ValueError(f"workspace holds {workspace.numel()} bytes; {ws} are needed")
             wbuf = workspace
-    call = gdn_prefill_split if scalar_gate else kda_prefill_split
+    flags = (KDA_PREFILL_SCALAR_GATE if scalar_gate else 0) | (KDA_PREFILL_WIDE_DECAY if wide_decay else 0)
     with torch.cuda.device(dev):
-        _check(call(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
-                                 beta.data_ptr(), S0.data_ptr() if S0 is not None else None,
-                                 cu_seqlens.data_ptr(), N, T, H, dk, dv, code, o.data_ptr(),
-                                 S_T.data_ptr(), wbuf.data_ptr() if wbuf is not None else None, ws,
-                                 int(v_split), _stream_handle(stream, dev)))
+        _check(kda_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
+                              beta.data_ptr(), S0.data_ptr() if S0 is not None else None,
+                              cu_seqlens.data_ptr(), N, T, H, dk, dv, code, o.data_ptr(),
+                              S_T.data_ptr(), wbuf.data_ptr() if wbuf is not None else None, ws,
+                              int(v_split), flags, _stream_handle(stream, dev)))
     return o, S_T
 
 
 def prefill(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=None,
-            v_split: int = 0, workspace=None, stream=None):
+            v_split: int = 0, workspace=None, wide_decay: bool = False, stream=None):
     """KDA chunked prefill (per-channel gates, log_alpha [T, H, d_k]) on torch
     tensors; returns (o, S_T).  Arguments as in ``_prefill``."""
-    return _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream, False)
+    return _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream, False,
+                    wide_decay)
 
 
 def gdn_prefill_t(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=None,
-                  v_split: int = 0, workspace=None, stream=None):
+                  v_split: int = 0, workspace=None, wide_decay: bool = False, stream=None):
     """Gated DeltaNet chunked prefill (one gate per token and head, log_alpha
     [T, H]) on torch tensors; returns (o, S_T).  Arguments as in ``_prefill``."""
-    return _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream, True)
+    return _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream, True,
+                    wide_decay)
 
 
 

@@ -74,15 +74,18 @@ int32_t kda_prefill_default_split(int32_t N, int64_t T_tot, int32_t H, int32_t d
 
 namespace {
 
-// Shared by the per-channel (KDA) and scalar (GDN) gate entry points: the
-// scalar gate changes only the shape of log_alpha ([T_tot, H], 4-byte
-// aligned).
+// Shared by every prefill entry point.  KDA_PREFILL_SCALAR_GATE changes only
+// the shape of log_alpha ([T_tot, H], 4-byte aligned); KDA_PREFILL_WIDE_DECAY
+// selects the wide-decay kernel variant.
 kda_status prefill_impl(const void* q, const void* k, const void* v, const float* log_alpha,
                         const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
                         int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
                         float* S_T, void* workspace, size_t workspace_bytes, int32_t v_split,
-                        void* stream, bool scalar_gate) {
+                        uint32_t flags, void* stream) {
     g_last_error.clear();
+    if ((flags & ~static_cast<uint32_t>(KDA_PREFILL_SCALAR_GATE | KDA_PREFILL_WIDE_DECAY)) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "unknown bits in flags");
+    const bool scalar_gate = (flags & KDA_PREFILL_SCALAR_GATE) != 0;
     if (N < 1 || H < 1 || T_tot < 0)
         return fail(KDA_ERR_INVALID_ARG, "need N >= 1, H >= 1 and T_tot >= 0");
     const kda_status ds = check_dims(d_k, d_v, dtype);
@@ -117,7 +120,8 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
     if (grid > (int64_t{1} << 22)) return fail(KDA_ERR_INVALID_ARG, "N * H * v_split too large");
 
     kda::PrefillArgs a{q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
-                       dtype == KDA_DTYPE_BF16, o, S_T, v_split, stream, workspace, scalar_gate};
+                       dtype == KDA_DTYPE_BF16, o, S_T, v_split, stream, workspace, scalar_gate,
+                       (flags & KDA_PREFILL_WIDE_DECAY) != 0};
     (void)hipGetLastError();  // report only this launch's status
     const hipError_t e = kda::launch_prefill(a);
     if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
@@ -157,7 +161,16 @@ kda_status kda_prefill_split(const void* q, const void* k, const void* v, const 
                              kda_dtype dtype, void* o, float* S_T, void* workspace,
                              size_t workspace_bytes, int32_t v_split, void* stream) {
     return prefill_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
-                        workspace, workspace_bytes, v_split, stream, false);
+                        workspace, workspace_bytes, v_split, 0, stream);
+}
+
+kda_status kda_prefill_ex(const void* q, const void* k, const void* v, const float* log_alpha,
+                          const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
+                          int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
+                          float* S_T, void* workspace, size_t workspace_bytes, int32_t v_split,
+                          uint32_t flags, void* stream) {
+    return prefill_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
+                        workspace, workspace_bytes, v_split, flags, stream);
 }
 
 kda_status kda_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -165,7 +178,7 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
                        int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
                        float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
-                        workspace, workspace_bytes, 0, stream, false);
+                        workspace, workspace_bytes, 0, 0, stream);
 }
 
 kda_status gdn_prefill_split(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -174,7 +187,7 @@ kda_status gdn_prefill_split(const void* q, const void* k, const void* v, const 
                              kda_dtype dtype, void* o, float* S_T, void* workspace,
                              size_t workspace_bytes, int32_t v_split, void* stream) {
     return prefill_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
-                        workspace, workspace_bytes, v_split, stream, true);
+                        workspace, workspace_bytes, v_split, KDA_PREFILL_SCALAR_GATE, stream);
 }
 
 kda_status gdn_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -182,7 +195,7 @@ kda_status gdn_prefill(const void* q, const void* k, const void* v, const float*
                        int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
                        float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
-                        workspace, workspace_bytes, 0, stream, true);
+                        workspace, workspace_bytes, 0, KDA_PREFILL_SCALAR_GATE, stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,

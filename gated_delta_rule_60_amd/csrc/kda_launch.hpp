@@ -50,6 +50,7 @@ struct PrefillArgs {
     void* stream;
     void* workspace;  // at least prefill_workspace_bytes(...) bytes
     bool scalar_gate = false;  // log_alpha is [T_tot, H] (one gate per token and head)
+    bool wide_decay = false;   // exponents of strongly decaying channels from the chunk's middle row
 };
 
 struct DecodeArgs {

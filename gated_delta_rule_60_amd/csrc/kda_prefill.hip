@@ -68,6 +68,10 @@ constexpr size_t align16(size_t x) { return (x + 15) & ~static_cast<size_t>(15);
 // this many sequences; larger batches run in natural order.
 constexpr int kSortMax = 64;
 constexpr size_t kLdsBudget = 160 * 1024;
+// Wide-decay variant: a channel whose decay over one chunk is below
+// -kRefSwitchLog2 (log2 units, about e^-69) takes its exponents relative to
+// the chunk's middle row.
+constexpr float kRefSwitchLog2 = 100.f;
 
 template <int V>
 using ic = std::integral_constant<int, V>;
@@ -82,7 +86,7 @@ using ic = std::integral_constant<int, V>;
 // Operand tiles (the producers' tiles) are unpadded and swizzled in 16-byte
 // units (see quad_off): UK units per row of a [C][DK] tile, UT per row of a
 // [rows][C] tile.  Job tiles are padded row-major.
-template <bool BF16, int DK, int NC, int CT, int C_>
+template <bool BF16, int DK, int NC, int CT, int C_, bool WIDE>
 struct Layout {
     using E = typename Elem<BF16>::E;
     static constexpr int C = C_;
@@ -101,6 +105,7 @@ struct Layout {
     static constexpr size_t SZ_VT = BV * C * ES;                 // V^T         [BV][C]
     static constexpr size_t SZ_GC = align16(DK * 4);             // Gamma_C     [DK]
     static constexpr size_t SZ_BETA = align16(C * 4);            // beta        [C]
+    static constexpr size_t SZ_GM = WIDE ? align16(DK * 4) : 0;  // 2^ref       [DK] (wide decay)
     static constexpr size_t SZ_L = align16(C * LDJ * ES);        // L, A_qk     [C][LDJ]
     static constexpr size_t SZ_T = align16(NB * 16 * LDT * ES);  // -T_bb       [NB][16][LDT]
     // producer slot
@@ -111,7 +116,8 @@ struct Layout {
     static constexpr size_t O_VT = O_KBT + SZ_KBT;
     static constexpr size_t O_GC = O_VT + SZ_VT;
     static constexpr size_t O_BETA = O_GC + SZ_GC;
-    static constexpr size_t PBUF = O_BETA + SZ_BETA;
+    static constexpr size_t O_GM = O_BETA + SZ_BETA;
+    static constexpr size_t PBUF = O_GM + SZ_GM;
     // job buffer
     static constexpr size_t OFF_JOB = NSLOT * PBUF;
     static constexpr size_t O_L = 0;
@@ -125,19 +131,20 @@ struct Layout {
 };
 
 // The chunk length depends only on the storage type and d_k (sized for the
-// widest value slice, 128 columns), so that every value-slice split of a
-// problem runs the same chunk algebra and gives the same bits.
+// widest value slice, 128 columns, of the larger wide-decay layout), so that
+// every value-slice split and both decay variants of a problem run the same
+// chunk algebra and give the same bits.
 template <bool BF16, int DK>
-constexpr int kChunk = Layout<BF16, DK, 4, 2, 32>::BYTES <= kLdsBudget ? 32 : 16;
+constexpr int kChunk = Layout<BF16, DK, 4, 2, 32, true>::BYTES <= kLdsBudget ? 32 : 16;
 
-template <bool BF16, int DK, int NC, int CT>
-using ChosenLayout = Layout<BF16, DK, NC, CT, kChunk<BF16, DK>>;
+template <bool BF16, int DK, int NC, int CT, bool WIDE>
+using ChosenLayout = Layout<BF16, DK, NC, CT, kChunk<BF16, DK>, WIDE>;
 
 // Wave roles, in this order: NC consumers (all MFMA work), NP producers
 // (vector ALU and memory only).
-template <bool BF16, int DK, int NC, int CT>
-struct PrefillShape : ChosenLayout<BF16, DK, NC, CT> {
-    using Base = ChosenLayout<BF16, DK, NC, CT>;
+template <bool BF16, int DK, int NC, int CT, bool WIDE = false>
+struct PrefillShape : ChosenLayout<BF16, DK, NC, CT, WIDE> {
+    using Base = ChosenLayout<BF16, DK, NC, CT, WIDE>;
     static_assert(Base::BYTES <= kLdsBudget, "LDS budget of one gfx950 workgroup");
     static constexpr int NRG = Base::C / 4;  // row groups of 4 rows
     static constexpr int QW = 64 / NRG;      // channel quads per producer wave
@@ -393,14 +400,16 @@ __device__ __forceinline__ void ctr_wait_each(int* ctrs, int n, int target, int*
 // SG: scalar gate (one log alpha per token and head, [T, H]: Gated DeltaNet);
 // otherwise one per key channel ([T, H, d_k]: KDA).  A scalar gate is the
 // per-channel computation with the value repeated over the channels.
-template <bool BF16, int DK, int NC, int CT, bool SG>
-__global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_kernel(
+// WIDE: wide-decay variant (exponents of strongly decaying channels taken
+// relative to the chunk's middle row, the state operand scaled to match).
+template <bool BF16, int DK, int NC, int CT, bool SG, bool WIDE>
+__global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void prefill_kernel(
     const typename Elem<BF16>::G* __restrict__ q, const typename Elem<BF16>::G* __restrict__ k,
     const typename Elem<BF16>::G* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, const float* __restrict__ S0, const int32_t* __restrict__ cu,
     int N, int H, int dv, int v_split, typename Elem<BF16>::G* __restrict__ o,
     float* __restrict__ S_T, SegView seg) {
-    using Sh = PrefillShape<BF16, DK, NC, CT>;
+    using Sh = PrefillShape<BF16, DK, NC, CT, WIDE>;
     using T = Elem<BF16>;
     using E = typename T::E;
     using G = typename T::G;
@@ -423,6 +432,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
     KDA_TILE(tKbT, E, 0, Sh::PBUF, Sh::O_KBT);
     KDA_TILE(tVt, E, 0, Sh::PBUF, Sh::O_VT);
     KDA_TILE(sGC, float, 0, Sh::PBUF, Sh::O_GC);
+    KDA_TILE(sGM, float, 0, Sh::PBUF, Sh::O_GM);
     KDA_TILE(sBeta, float, 0, Sh::PBUF, Sh::O_BETA);
     // job buffers 0..1
     KDA_TILE(tL, E, Sh::OFF_JOB, Sh::JBUF, Sh::O_L);
@@ -671,11 +681,25 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
 
         // R' = beta (K~ S - V)  (= -R)
         auto chain_R = [&](int B) __attribute__((always_inline)) {
+            if constexpr (WIDE) {
+                // the S operand of K~ S and Q~ S with its rows (key channels)
+                // scaled by 2^ref of the chunk (exactly 1 for a channel with
+                // the start reference)
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
+                for (int kb = 0; kb < KB; ++kb) {
+                    const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(sGM(B) + 32 * kb + 4 * lg);
+                    const f32x4_t e1 = *reinterpret_cast<const f32x4_t*>(sGM(B) + 32 * kb + 16 + 4 * lg);
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    sf[ct][kb] = acc_frag8<BF16>(Sr[ct][2 * kb], Sr[ct][2 * kb + 1]);
+                    for (int ct = 0; ct < CT; ++ct)
+                        sf[ct][kb] = acc_frag8<BF16>(Sr[ct][2 * kb] * e0, Sr[ct][2 * kb + 1] * e1);
+                }
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+                        sf[ct][kb] = acc_frag8<BF16>(Sr[ct][2 * kb], Sr[ct][2 * kb + 1]);
+                }
             }
 #pragma unroll
             for (int rt = 0; rt < NB; ++rt) {
@@ -991,6 +1015,31 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
 #pragma unroll
             for (int c = 0; c < 4; ++c) Gc[c] = __builtin_amdgcn_exp2f(sum[c]);
             if (rg == 0) *reinterpret_cast<float4*>(sGC(S) + i0) = make_float4(Gc[0], Gc[1], Gc[2], Gc[3]);
+            // Reference point of each channel's exponents: the chunk start; in
+            // the wide-decay variant, the middle row for a channel whose decay
+            // over the chunk would put 2^-g outside the fp32 range (every
+            // exponent is then bounded by the decay of C/2 tokens).
+            float ref[4] = {0.f, 0.f, 0.f, 0.f}, GcR[4] = {Gc[0], Gc[1], Gc[2], Gc[3]};
+            if constexpr (WIDE) {
+                float mid[4] = {0.f, 0.f, 0.f, 0.f};  // rows 0 .. C/2 - 1
+#pragma unroll
+                for (int r = 0; r < NRG / 2; ++r) {
+                    const float4 t4 = scan[QW * r + cq];
+                    mid[0] += t4.x;
+                    mid[1] += t4.y;
+                    mid[2] += t4.z;
+                    mid[3] += t4.w;
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    ref[c] = sum[c] < -kRefSwitchLog2 ? mid[c] : 0.f;
+                    GcR[c] = __builtin_amdgcn_exp2f(sum[c] - ref[c]);
+                }
+                if (rg == 0)
+                    *reinterpret_cast<float4*>(sGM(S) + i0) =
+                        make_float4(__builtin_amdgcn_exp2f(ref[0]), __builtin_amdgcn_exp2f(ref[1]),
+                                    __builtin_amdgcn_exp2f(ref[2]), __builtin_amdgcn_exp2f(ref[3]));
+            }
             float kbar[4][4];
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -1001,12 +1050,18 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
                 float gam[4], kh4[4], kg[4], qg[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    // exp(+-g) as 2^(+-g2): one v_exp_f32 each; |g| stays within
-                    // the numerical contract, where results are normal.
+                    // exp(+-(g - ref)) as 2^(+-(g2 - ref2)): one v_exp_f32 each;
+                    // within the numerical contract the results are normal.
                     g[c] = __builtin_fmaf(la[rr][c], kLog2e, g[c]);
-                    gam[c] = __builtin_amdgcn_exp2f(g[c]);
-                    kh4[c] = kk[c] * __builtin_amdgcn_exp2f(-g[c]);
-                    kbar[rr][c] = kh4[c] * Gc[c];
+                    if constexpr (WIDE) {
+                        gam[c] = __builtin_amdgcn_exp2f(g[c] - ref[c]);
+                        kh4[c] = kk[c] * __builtin_amdgcn_exp2f(ref[c] - g[c]);
+                        kbar[rr][c] = kh4[c] * GcR[c];
+                    } else {
+                        gam[c] = __builtin_amdgcn_exp2f(g[c]);
+                        kh4[c] = kk[c] * __builtin_amdgcn_exp2f(-g[c]);
+                        kbar[rr][c] = kh4[c] * Gc[c];
+                    }
                     kg[c] = kk[c] * gam[c];
                     qg[c] = qq[c] * gam[c];
                 }
@@ -1099,14 +1154,14 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT>::NT)) void prefill_
 // BV = d_v / v_split: 4 waves x 2 tiles (128), 4 x 1 (64), 2 x 1 (32),
 // 1 x 1 (16); producer waves follow d_k.
 // ---------------------------------------------------------------------------
-template <bool BF16, int DK, int NC, int CT, bool SG>
+template <bool BF16, int DK, int NC, int CT, bool SG, bool WIDE>
 static hipError_t launch_prefill_t(const PrefillArgs& a, const SegView& seg) {
     using G = typename Elem<BF16>::G;
-    using Sh = PrefillShape<BF16, DK, NC, CT>;
+    using Sh = PrefillShape<BF16, DK, NC, CT, WIDE>;
     const unsigned units = seg.units ? static_cast<unsigned>(seg.umax) : static_cast<unsigned>(a.N);
     const unsigned per_unit = static_cast<unsigned>(a.v_split) * (seg.units ? 2u : 1u);
     const unsigned grid = units * static_cast<unsigned>(a.H) * per_unit;
-    hipLaunchKernelGGL((prefill_kernel<BF16, DK, NC, CT, SG>), dim3(grid), dim3(Sh::NT), 0,
+    hipLaunchKernelGGL((prefill_kernel<BF16, DK, NC, CT, SG, WIDE>), dim3(grid), dim3(Sh::NT), 0,
                        static_cast<hipStream_t>(a.stream), static_cast<const G*>(a.q),
                        static_cast<const G*>(a.k), static_cast<const G*>(a.v), a.log_alpha, a.beta,
                        a.S0, a.cu_seqlens, a.N, a.H, a.d_v, a.v_split, static_cast<G*>(a.o), a.S_T, seg);
@@ -1115,8 +1170,11 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, const SegView& seg) {
 
 template <bool BF16, int DK, int NC, int CT>
 static hipError_t launch_prefill_sg(const PrefillArgs& a, const SegView& seg) {
-    return a.scalar_gate ? launch_prefill_t<BF16, DK, NC, CT, true>(a, seg)
-                         : launch_prefill_t<BF16, DK, NC, CT, false>(a, seg);
+    if (a.wide_decay)
+        return a.scalar_gate ? launch_prefill_t<BF16, DK, NC, CT, true, true>(a, seg)
+                             : launch_prefill_t<BF16, DK, NC, CT, false, true>(a, seg);
+    return a.scalar_gate ? launch_prefill_t<BF16, DK, NC, CT, true, false>(a, seg)
+                         : launch_prefill_t<BF16, DK, NC, CT, false, false>(a, seg);
 }
 
 template <bool BF16, int DK>

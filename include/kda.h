@@ -31,7 +31,9 @@
  *  - Results are deterministic: the same inputs give the same bits.
  *  - Numerical contract: log_alpha finite and <= 0 with the sum of log_alpha
  *    over any 32 consecutive tokens of a sequence >= -80 per channel (the
- *    chunked prefill evaluates exp(+-that sum) in fp32); beta finite.
+ *    chunked prefill evaluates exp(+-that sum) in fp32); beta finite.  The
+ *    wide-decay option of kda_prefill_ex halves the window to 16 tokens.
+ *    The decode step has no such limit.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -121,6 +123,36 @@ kda_status kda_prefill_split(const void* q, const void* k, const void* v,
                              int32_t d_k, int32_t d_v, kda_dtype dtype, void* o, float* S_T,
                              void* workspace, size_t workspace_bytes, int32_t v_split,
                              void* stream);
+
+/*
+ * kda_prefill_ex -- kda_prefill_split with option flags (0 gives
+ * kda_prefill_split exactly):
+ *
+ *   KDA_PREFILL_SCALAR_GATE  log_alpha is [T_tot, H], one gate per token and
+ *                            head (as gdn_prefill_split, below).
+ *   KDA_PREFILL_WIDE_DECAY   wide-decay variant.  The numerical contract
+ *                            becomes: the sum of log_alpha over any 16
+ *                            consecutive tokens >= -80 per channel (twice
+ *                            the per-token range of the default 32-token
+ *                            window).  A channel whose decay over a 32-token
+ *                            chunk is below about -69 takes its exponents
+ *                            relative to the chunk's middle row, and the
+ *                            state operand of that channel is scaled to
+ *                            match; other channels compute exactly as
+ *                            without the flag, so inputs within the default
+ *                            contract give the same bits either way.  The
+ *                            launch costs a few percent more.
+ *
+ * Unknown flag bits give KDA_ERR_INVALID_ARG.
+ */
+#define KDA_PREFILL_SCALAR_GATE 1u
+#define KDA_PREFILL_WIDE_DECAY 2u
+kda_status kda_prefill_ex(const void* q, const void* k, const void* v,
+                          const float* log_alpha, const float* beta, const float* S0,
+                          const int32_t* cu_seqlens, int32_t N, int64_t T_tot, int32_t H,
+                          int32_t d_k, int32_t d_v, kda_dtype dtype, void* o, float* S_T,
+                          void* workspace, size_t workspace_bytes, int32_t v_split,
+                          uint32_t flags, void* stream);
 
 /* Bytes of workspace kda_prefill needs for these sizes: 0 unless the batch
  * runs segmented (d_k == d_v, T_tot > 4096, N * H < 128); then the segment

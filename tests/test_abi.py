@@ -83,6 +83,18 @@ def test_prefill_entry_point_validates_too():
     assert rc == kda.KDA_ERR_UNSUPPORTED
 
 
+def test_prefill_ex_rejects_unknown_flags():
+    a = dict(q=FAKE, k=FAKE, v=FAKE, log_alpha=FAKE, beta=FAKE, S0=None, cu_seqlens=FAKE, N=1,
+             T_tot=64, H=2, d_k=64, d_v=64, dtype=BF16, o=FAKE, S_T=FAKE, workspace=None,
+             workspace_bytes=0, v_split=0, stream=None)
+    assert kda.kda_prefill_ex(flags=4, **a) == kda.KDA_ERR_INVALID_ARG
+    assert "flags" in kda.kda_last_error()
+    # known flags pass flag validation and fail later, on the bad v_split
+    for f in (kda.KDA_PREFILL_SCALAR_GATE, kda.KDA_PREFILL_WIDE_DECAY, 3):
+        assert kda.kda_prefill_ex(flags=f, **dict(a, v_split=3)) == kda.KDA_ERR_INVALID_ARG
+        assert "v_split" in kda.kda_last_error()
+
+
 def test_gdn_entry_points_validate_the_per_head_gate():
     args = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, S0=None, cu_seqlens=FAKE, N=1, T_tot=64, H=2,
                 d_k=64, d_v=64, dtype=BF16, o=FAKE, S_T=FAKE, workspace=None, workspace_bytes=0,

@@ -89,3 +89,15 @@ def test_gdn_varlen_32k_sampled_heads():
     assert_close(host(o[:, heads]), ref_o[:, heads], "bf16", "o (sampled heads)")
     assert_close(host(ST[:, heads]), ref_S[:, heads], "bf16", "S_T (sampled heads)")
 
+
+def test_gdn_wide_decay():
+    """One gate of -5 per token and head (the decay summed over 16 tokens at
+    the wide-decay limit) through the wide-decay variant."""
+    import torch
+    x = inputs.make_prefill_inputs([400, 17], 2, 128, 128, "bf16", seed=41, s0_std=1.0)
+    la = np.full(x.log_alpha.shape[:2], -5.0, np.float32)
+    ref_o, ref_S = oracle.gdn_prefill(x.q, x.k, x.v, la, x.beta, x.S0, x.cu_seqlens)
+    d = upload(x)
+    o, ST = kda.gdn_prefill_t(**dict(d, log_alpha=torch.from_numpy(la).cuda()), wide_decay=True)
+    assert_close(host(o), ref_o, "bf16", "o")
+    assert_close(host(ST), ref_S, "bf16", "S_T")

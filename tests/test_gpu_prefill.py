@@ -52,21 +52,75 @@ def test_small_cases_every_split(case):
     _run_case(*case, seed=sum(case[0]) + case[2])
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("la_range", [(0.5, 2.5), (2.5, 2.5)], ids=["mixed", "max"])
-def test_strong_decay_at_the_contract_limit(dtype, la_range):
-    """log alpha down to -2.5 per token and channel: the decay summed over 32
-    consecutive tokens reaches the -80 limit of the numerical contract ("max":
-    exactly), so the chunk's exponentials span e^(+-80)."""
-    x = inputs.make_prefill_inputs([700, 33, 1], 2, 128, 128, dtype, seed=11,
+# log alpha ranges: "max32" puts the decay summed over each 32-token chunk at
+# -80 exactly (the default contract's limit); "max16" puts the decay summed
+# over any 16 consecutive tokens at -80 exactly (the wide-decay limit).
+DECAY_RANGES = {"mixed32": (0.5, 2.5), "max32": (2.5, 2.5), "mixed16": (0.0, 5.0), "max16": (5.0, 5.0)}
+
+
+def _strong_decay_case(dk, dtype, la_range, wide):
+    x = inputs.make_prefill_inputs([700, 33, 1], 2, dk, dk, dtype, seed=11,
                                    log_alpha_range=la_range, s0_std=1.0)
     ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens)
     d = upload(x)
-    for split in valid_splits(128):
-        log(f"  strong decay {la_range} {dtype} v_split={split}")
-        o, ST = kda.prefill(**d, v_split=split)
+    for split in valid_splits(dk):
+        log(f"  strong decay {la_range} d={dk} {dtype} wide={wide} v_split={split}")
+        o, ST = kda.prefill(**d, v_split=split, wide_decay=wide)
         assert_close(host(o), ref_o, dtype, "o")
         assert_close(host(ST), ref_S, dtype, "S_T")
+
+
+@pytest.mark.parametrize("dk,dtype", [(128, "bf16"), (128, "f32"), (64, "f32")])
+@pytest.mark.parametrize("name", ["mixed32", "max32"])
+def test_strong_decay_at_the_contract_limit(dk, dtype, name):
+    """log alpha down to -2.5 per token and channel: the chunk's exponentials
+    span e^(+-80) at the default contract's limit.  Covers 32-token chunks in
+    both storage types and the 16-token chunks of fp32 at d = 128."""
+    _strong_decay_case(dk, dtype, DECAY_RANGES[name], False)
+
+
+@pytest.mark.parametrize("dk,dtype", [(128, "bf16"), (128, "f32"), (64, "f32")])
+@pytest.mark.parametrize("name", ["mixed32", "max32", "mixed16", "max16"])
+def test_wide_decay_at_its_limit(dk, dtype, name):
+    """The wide-decay variant down to -5 per token and channel: exponents of
+    the strongly decaying channels are taken from the chunk's middle row, so
+    a chunk's exponentials stay within e^(+-80) up to its limit ("max16")."""
+    _strong_decay_case(dk, dtype, DECAY_RANGES[name], True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_wide_decay_in_some_channels(dtype):
+    """Decay of -5 per token in key channels 0..39 only (the first channel
+    strip and part of the second), weak elsewhere: chunks where some channels
+    take their exponents from the middle row and the others from the chunk
+    start, within one producer strip and across strips."""
+    x = inputs.make_prefill_inputs([300, 45], 2, 128, 128, dtype, seed=12, s0_std=1.0)
+    x.log_alpha[:, :, :40] = -5.0
+    ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens)
+    d = upload(x)
+    for split in valid_splits(128):
+        log(f"  wide decay, channels 0..39 strong, {dtype} v_split={split}")
+        o, ST = kda.prefill(**d, v_split=split, wide_decay=True)
+        assert_close(host(o), ref_o, dtype, "o")
+        assert_close(host(ST), ref_S, dtype, "S_T")
+
+
+@pytest.mark.parametrize("lengths", [[300, 1, 64], [4096 + 500, 77]], ids=["short", "segmented"])
+def test_wide_decay_keeps_the_bits_within_the_default_contract(lengths):
+    """Within the default contract no channel moves its reference, and the
+    wide-decay variant gives exactly the default variant's bits (KDA and
+    GDN, every launch shape)."""
+    import torch
+    x = inputs.make_prefill_inputs(lengths, 2, 128, 128, "bf16", seed=21, s0_std=1.0)
+    d = upload(x)
+    for split in valid_splits(128):
+        o0, S0 = kda.prefill(**d, v_split=split)
+        o1, S1 = kda.prefill(**d, v_split=split, wide_decay=True)
+        assert torch.equal(o0, o1) and torch.equal(S0, S1), f"KDA v_split={split}"
+    la = d["log_alpha"][:, :, 0].contiguous()
+    o0, S0 = kda.gdn_prefill_t(**dict(d, log_alpha=la))
+    o1, S1 = kda.gdn_prefill_t(**dict(d, log_alpha=la), wide_decay=True)
+    assert torch.equal(o0, o1) and torch.equal(S0, S1), "GDN"
 
 
 SEGMENTED = [
