@@ -253,40 +253,33 @@ __global__ __launch_bounds__(ChainShape<DK>::NT) void seg_chain_kernel(const int
 // ---------------------------------------------------------------------------
 // Outputs of later segments: o_t += S_in^T q^_t for every token t of the
 // segment.  One workgroup per (unit, head, kOutTokens tokens); S_in^T is
-// staged once in LDS in the operand type, and each wave takes 16-token tiles
-// of all d_v columns: C layout of o^T, so a lane updates four consecutive
-// columns of one token.  A tile's q^ and o rows are loaded while the tile
-// before it computes; buffer ranges end at the segment's last token (loads
-// past it return zero, stores are dropped), so every load is unconditional.
+// staged once in LDS in the operand type.  Each wave takes 16-token tiles:
+//   1. q^ and o rows are loaded 16 bytes per lane along each row (every
+//      instruction reads whole row segments), one tile ahead;
+//   2. the q^ rows pass through the wave's LDS staging area into MFMA
+//      operand layout (lane: token, k slots);
+//   3. the products give o^T in the C layout; they pass through the same
+//      staging area back to row order, are added to o and stored 16 bytes
+//      per lane along each row.
+// Buffer ranges end at the segment's last token (loads past it return zero,
+// stores are dropped), so every load and store is unconditional.
 // ---------------------------------------------------------------------------
-typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
-template <bool BF16>
-__device__ __forceinline__ typename Elem<BF16>::R4 rbuf_load4(__amdgpu_buffer_rsrc_t r, int voff) {
-    if constexpr (BF16) {
-        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
-        return make_uint2(x[0], x[1]);
-    } else {
-        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
-        return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
-                           __uint_as_float(x[3]));
-    }
-}
-
-template <bool BF16>
-__device__ __forceinline__ void rbuf_store4(__amdgpu_buffer_rsrc_t r, int voff, const float (&x)[4]) {
-    if constexpr (BF16) {
-        bf16x4_t h;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) h[j] = static_cast<__bf16>(x[j]);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, h), r, voff, 0, 0);
-    } else {
-        __builtin_amdgcn_raw_buffer_store_b128(
-            u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])}, r,
-            voff, 0, 0);
-    }
-}
+template <bool BF16, int DK>
+struct OutShape {
+    static constexpr int ES = BF16 ? 2 : 4;
+    static constexpr int RB = DK * ES;           // bytes of one token's head slice (q^ and o)
+    static constexpr int LPR = RB / 16;          // lanes per row at 16 bytes
+    static constexpr int RPI = 64 / LPR;         // rows per load instruction
+    static constexpr int NI = 16 / RPI;          // instructions per 16-row tile
+    static constexpr int OE = 16 / ES;           // elements per 16-byte access
+    static constexpr int LDQ = RB + 16;          // staging row stride (bytes), q^ rows
+    static constexpr int LDA = DK * 4 + 16;      // staging row stride (bytes), fp32 products
+    static constexpr int STAGE = 16 * (LDQ > LDA ? LDQ : LDA);  // bytes per wave
+    static constexpr int LDB = DK + 4;           // rows of S_in^T (elements)
+    static_assert(RB % 64 == 0 && NI >= 1, "row tiling");
+};
 
 template <bool BF16, int DK>
 __global__ __launch_bounds__(kFixThreads) void seg_out_kernel(const int4* __restrict__ units,
@@ -298,16 +291,16 @@ __global__ __launch_bounds__(kFixThreads) void seg_out_kernel(const int4* __rest
     using E = typename T::E;
     using G = typename T::G;
     using F8 = typename T::F8;
-    using R4 = typename T::R4;
+    using Sh = OutShape<BF16, DK>;
     constexpr int DV = DK;  // segmented runs have d_v = d_k
     constexpr int KB = DK / 32;
     constexpr int NCT = DV / 16;
-    constexpr int ES = sizeof(G);
-    constexpr int LDB = DK + 4;  // rows of S_in^T: 8-byte (bf16) / 16-byte (fp32) aligned fragments
+    constexpr int LDB = Sh::LDB, NI = Sh::NI, LPR = Sh::LPR, RPI = Sh::RPI, OE = Sh::OE;
     constexpr int TILES = kSegTokens / kOutTokens;
     constexpr int SQ = DK * DV / 4 / kFixThreads;  // float4 of S_in per thread
     static_assert(SQ >= 1, "state staging");
     __shared__ __attribute__((aligned(16))) E sBt[DV * LDB];
+    __shared__ __attribute__((aligned(16))) unsigned char sStage[kFixThreads / 64][Sh::STAGE];
 
     const int w = blockIdx.x;
     const int u = w / (H * TILES);
@@ -325,6 +318,7 @@ __global__ __launch_bounds__(kFixThreads) void seg_out_kernel(const int4* __rest
     const int wave = tid >> 6;
     const int ln = lane & 15;
     const int lgp = lane >> 4;
+    unsigned char* const stage = sStage[wave];
 
     {
         const float4* Sg = reinterpret_cast<const float4*>(sin_state + (static_cast<size_t>(u) * H + h) * DK * DV);
@@ -344,71 +338,87 @@ __global__ __launch_bounds__(kFixThreads) void seg_out_kernel(const int4* __rest
     __syncthreads();
 
     // Byte ranges: rows tt .. min(tt + 16, t1) - 1 of this head's q^ / o
-    // columns (one token row is H * DK elements; at most 16 rows, so every
+    // slices (one token row is H * DK elements; at most 16 rows, so every
     // offset stays far below 2^31 under the host's H * d <= 2^20).
-    const int rowB = H * DK * ES;
+    const int rowB = H * Sh::RB;
     auto rsrc = [&](const G* base, int tt) __attribute__((always_inline)) {
         const int rows = __builtin_amdgcn_readfirstlane(min(16, t1 - tt));
-        const int bytes = rows > 0 ? (rows - 1) * rowB + DK * ES : 0;
+        const int bytes = rows > 0 ? (rows - 1) * rowB + Sh::RB : 0;
         const G* p = rows > 0 ? base + static_cast<size_t>(tt) * H * DK : base;
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<G*>(p), 0, bytes, 0x00020000);
     };
     const G* const qh = qhat + static_cast<size_t>(h) * DK;
     G* const oh = o + static_cast<size_t>(h) * DV;
-    const int vrow = ln * rowB + 4 * lgp * ES;
+    // this lane's row and 16-byte column block in load instruction j
+    const int lrow = lane / LPR, lcol = (lane % LPR) * 16;
+    auto voff = [&](int j) __attribute__((always_inline)) { return (j * RPI + lrow) * rowB + lcol; };
 
-    R4 qn[KB][2], on[NCT];
+    u32x4_t qn[NI], on[NI];
     auto fetch = [&](int tt) __attribute__((always_inline)) {
         const auto rq = rsrc(qh, tt);
         const auto ro = rsrc(oh, tt);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            qn[kb][0] = rbuf_load4<BF16>(rq, vrow + 32 * kb * ES);
-            qn[kb][1] = rbuf_load4<BF16>(rq, vrow + (32 * kb + 16) * ES);
-        }
+        for (int j = 0; j < NI; ++j) qn[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff(j), 0, 0);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) on[ct] = rbuf_load4<BF16>(ro, vrow + 16 * ct * ES);
+        for (int j = 0; j < NI; ++j) on[j] = __builtin_amdgcn_raw_buffer_load_b128(ro, voff(j), 0, 0);
     };
 
     int tt = t0 + 16 * wave;
     fetch(tt);
     for (; tt < t1; tt += 64) {
-        R4 qc[KB][2], oc[NCT];
+        u32x4_t qc[NI], oc[NI];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            qc[kb][0] = qn[kb][0];
-            qc[kb][1] = qn[kb][1];
+        for (int j = 0; j < NI; ++j) {
+            qc[j] = qn[j];
+            oc[j] = on[j];
         }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) oc[ct] = on[ct];
         fetch(tt + 64);  // the next tile (an empty range past the end)
-        // keep the state fragments' LDS reads inside the loop (hoisted, they
-        // would hold 32 fragments in registers and halve the waves in flight)
-        asm volatile("" ::: "memory");
+        // q^ rows -> staging -> operand fragments (lane: token ln, k slots)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            *reinterpret_cast<u32x4_t*>(stage + (j * RPI + lrow) * Sh::LDQ + lcol) = qc[j];
         F8 b[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            float lo[4], hi[4];
-            T::unpack4(qc[kb][0], lo);
-            T::unpack4(qc[kb][1], hi);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                b[kb][j] = T::to_e(lo[j]);
-                b[kb][4 + j] = T::to_e(hi[j]);
-            }
-        }
-        const auto ro = rsrc(oh, tt);
+        for (int kb = 0; kb < KB; ++kb)
+            b[kb] = lds_frag8<BF16>(reinterpret_cast<const E*>(stage) + 32 * kb, Sh::LDQ / Sh::ES, lane);
+        // o^T tiles: lane holds columns 16 ct + 4 lgp .. + 3 of token ln;
+        // staged as fp32 rows (the q^ rows above are consumed)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
                 acc = mma8<BF16>(acc, lds_frag8<BF16>(sBt + (16 * ct) * LDB + 32 * kb, LDB, lane), b[kb]);
-            float cur[4];
-            T::unpack4(oc[ct], cur);
+            *reinterpret_cast<f32x4_t*>(stage + ln * Sh::LDA + (16 * ct + 4 * lgp) * 4) = acc;
+        }
+        // row order again: o += products, 16 bytes per lane along each row
+        const auto ro = rsrc(oh, tt);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) cur[j] += acc[j];
-            rbuf_store4<BF16>(ro, vrow + 16 * ct * ES, cur);
+        for (int j = 0; j < NI; ++j) {
+            const unsigned char* src = stage + (j * RPI + lrow) * Sh::LDA + (lcol / Sh::ES) * 4;
+            float add[OE];
+#pragma unroll
+            for (int e = 0; e < OE; e += 4) {
+                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + 4 * e);
+                add[e] = v[0];
+                add[e + 1] = v[1];
+                add[e + 2] = v[2];
+                add[e + 3] = v[3];
+            }
+            u32x4_t out;
+            if constexpr (BF16) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const unsigned x = oc[j][e];
+                    const float lo = __uint_as_float(x << 16) + add[2 * e];
+                    const float hi = __uint_as_float(x & 0xFFFF0000u) + add[2 * e + 1];
+                    out[e] = static_cast<unsigned>(f32_to_bf16(lo)) | (static_cast<unsigned>(f32_to_bf16(hi)) << 16);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = __float_as_uint(__uint_as_float(oc[j][e]) + add[e]);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(out, ro, voff(j), 0, 0);
         }
     }
 }
