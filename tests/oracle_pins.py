@@ -317,7 +317,37 @@ def pin_zero_state_and_empty_sequences(lib):
     assert np.all(np.isnan(Sm[0, 0]))
 
 
+def pin_segments_compose(lib):
+    """Linearity in (S0, V) over a split sequence: a later segment run from
+    the zero state gives o0 and D; the same segment with V = 0 and S0 = I
+    gives q^_t = M_t^T q_t as outputs and the transition M as final state;
+    then o_t = o0_t + S_in^T q^_t and S_out = M S_in + D chain the segments
+    back into the one-pass result (the decomposition of the segmented GPU
+    prefill)."""
+    rng = np.random.default_rng(114)
+    d = 5
+    q, k, v, la, beta, S0, cu = _random_case(rng, [23], H=2, dk=d, dv=d)
+    o, ST = oracle.prefill(q, k, v, la, beta, S0, cu, lib=lib)
+    cuts = [0, 6, 15, 23]
+    eye = np.broadcast_to(np.eye(d), (1, 2, d, d)).copy()
+    S_in = None
+    for s in range(len(cuts) - 1):
+        a, b = cuts[s], cuts[s + 1]
+        sl = lambda x: np.ascontiguousarray(x[a:b])
+        seg = np.array([0, b - a], np.int32)
+        if s == 0:
+            o_s, S_in = oracle.prefill(sl(q), sl(k), sl(v), sl(la), sl(beta), S0, seg, lib=lib)
+        else:
+            o0, D = oracle.prefill(sl(q), sl(k), sl(v), sl(la), sl(beta), None, seg, lib=lib)
+            qh, M = oracle.prefill(sl(q), sl(k), np.zeros_like(sl(v)), sl(la), sl(beta), eye, seg, lib=lib)
+            o_s = o0 + np.einsum("thi,hij->thj", qh, S_in[0])
+            S_in = np.einsum("hij,hjk->hik", M[0], S_in[0])[None] + D
+        _close(o_s, o[a:b], f"o of segment {s}")
+    _close(S_in, ST, "S_T")
+
+
 PINS = [
+    pin_segments_compose,
     pin_bruteforce_product,
     pin_deltanet_when_alpha_is_one,
     pin_gated_deltanet_scalar_gate,
