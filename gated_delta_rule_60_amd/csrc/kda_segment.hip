@@ -1,5 +1,5 @@
 // kda_segment.hip -- segmented prefill for long sequences: the plan of
-// segments and the fix-up that chains them.
+// segments and the fix-up passes that chain them.
 //
 // The recurrence of "Kimi Linear：让长上下文大模型真正实用的线性注意力架构",
 // section 三.5, is affine in the entering state: over a segment of tokens,
@@ -9,17 +9,16 @@
 // t.  Running the same recurrence with V = 0 and S_in = I (the identity run)
 // gives M as its final state and q^_t as its outputs.  The prefill kernel
 // runs every segment of every head (and the identity runs) in parallel; the
-// fix-up here walks the segments of each long sequence in order:
+// fix-up here chains the segments of each long sequence:
 //
 //     S_in(1) = final state of segment 0,
-//     O(s) += q^(s) S_in(s),   S_in(s+1) = M(s) S_in(s) + D(s),
-//     S_T = S_in(P).
+//     S_in(s+1) = M(s) S_in(s) + D(s),   S_T = S_in(P)     (state chain, in order)
+//     O(s) += q^(s) S_in(s)                                  (output correction)
 //
-// The columns of S (and of o) are independent, so the fix-up splits them
-// over workgroups.
+// The state chain is sequential over segments and splits the independent
+// columns of S over workgroups; the output correction is parallel over
+// segments, heads and token tiles.
 #include <hip/hip_runtime.h>
-
-#include <type_traits>
 
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
@@ -30,8 +29,8 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanSortMax = 64;  // sequences ordered by length (longest first) up to this many
-constexpr int kFixCols = 32;      // value columns per fix-up workgroup
-constexpr int kFixThreads = 256;
+constexpr int kFixCols = 32;      // value columns per state-chain workgroup
+constexpr int kFixThreads = 256;  // threads per output-correction workgroup
 constexpr int kOutTokens = 512;  // tokens per output fix-up workgroup
 static_assert(kSegTokens % kOutTokens == 0, "output tiles cover a segment");
 
