@@ -25,20 +25,23 @@
 // log alpha = 0 and therefore contribute nothing.
 //
 // Parallel decomposition.  One workgroup per (sequence, head, value slice)
-// walks its sequence chunk by chunk.  Its waves have two roles:
+// walks its sequence chunk by chunk (or per segment of a long sequence, see
+// kda_segment.hip: a later segment from the zero state, or its identity run
+// with V = 0 and S0 = I).  Its waves have two roles:
 //   * consumer waves (NC of them) carry the state.  Each owns CT 16-column
 //     tiles of S for the whole sequence, in fp32 registers (MFMA C layout);
 //     the columns of S evolve independently.  The consumers also share the
 //     S-independent MFMA work of the chunk (the Gram products L and A_qk and
 //     the diagonal-block inverses, one job per wave): the jobs of chunk i+1
 //     are computed alongside the recurrence of chunk i (R, U, O and the next
-//     S of the wave's columns) and published through an LDS counter.  O is
-//     written straight from registers.
+//     S of the wave's columns) and published through an LDS counter.  O^T
+//     quads are staged in the consumer's own rows of the slot's V^T tile.
 //   * producer waves (NP of them) do the vector-ALU part of the prep into
 //     LDS tiles that rotate through three slots: global loads (issued a
 //     chunk ahead), the per-channel cumulative decay (a wave-local prefix
 //     scan: each producer wave owns a strip of key channels for all rows),
-//     the decayed operand tiles and V^T.
+//     the decayed operand tiles and V^T; when refilling a slot they store
+//     the staged O of the chunk that used it, in row order.
 // The roles meet only at monotonic counters in LDS (tiles ready, jobs done,
 // slot released), so the producers' prep of chunks i+1 and i+2 runs at the
 // same time as the consumers' recurrence of chunk i on every SIMD.
@@ -48,6 +51,10 @@
 // different execution units of a SIMD.
 // All MFMA operands are bf16 (or fp32 for f32 inputs); accumulation and the
 // carried state are fp32.
+//
+// Variants (template flags): SG takes one gate per token and head (Gated
+// DeltaNet); WIDE takes the exponents of strongly decaying channels from the
+// chunk's middle row (the wide-decay contract of kda_prefill_ex).
 #include <type_traits>
 
 #include "kda_device.hpp"
