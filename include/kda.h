@@ -21,7 +21,8 @@
  * Conventions shared by every entry point.
  *  - Pointers named "device" are HIP device pointers on the current device;
  *    the caller owns every buffer.  The library allocates no device memory
- *    and keeps no global mutable state apart from a thread-local error text.
+ *    and keeps no global mutable state apart from a thread-local error text
+ *    and a per-device cache of the compute-unit count.
  *  - All tensors are dense, contiguous and row-major with the shapes given.
  *    Floating-point pointers must be 16-byte aligned.
  *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
@@ -45,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 1
+#define KDA_VERSION 2
 
 typedef enum {
     KDA_OK = 0,

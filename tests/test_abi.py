@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.kda_version() == 1
+    assert kda.kda_version() == 2
     for s in (0, 1, 2, 3):
         assert kda.kda_status_string(s).startswith("KDA_")
     assert "unknown" in kda.kda_status_string(99)
