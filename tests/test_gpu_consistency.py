@@ -28,8 +28,8 @@ def test_deterministic_and_split_invariant_bits(dtype):
             assert torch.equal(o, o0) and torch.equal(S, S0), f"v_split={split} rep={rep}"
 
 
-@pytest.mark.parametrize("lengths", [[100, 0, 130, 64], [9000, 100, 0, 4097]],
-                         ids=["short", "segmented"])
+@pytest.mark.parametrize("lengths", [[100, 0, 130, 64], [9000, 100, 0, 4097], [3000, 3000, 10]],
+                         ids=["short", "segmented", "segmented_mode_no_long_sequence"])
 def test_packing_does_not_change_bits(lengths):
     """A sequence gives the same bits alone or in any batch; with a batch
     over 4096 tokens the long sequences run in segments, which depend on the
