@@ -105,6 +105,20 @@ def test_wide_decay_in_some_channels(dtype):
         assert_close(host(ST), ref_S, dtype, "S_T")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_wide_decay_with_segments(dtype):
+    """A long sequence that runs in segments (identity runs and state chain)
+    with gates at the wide-decay limit range, -U(0, 5) per token."""
+    x = inputs.make_prefill_inputs([5000, 100], 2, 128, 128, dtype, seed=23,
+                                   log_alpha_range=(0.0, 5.0), s0_std=1.0)
+    code = kda.KDA_DTYPE_BF16 if dtype == "bf16" else kda.KDA_DTYPE_F32
+    assert kda.kda_prefill_workspace_size(x.N, x.T_tot, 2, 128, 128, code) > 0
+    ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens)
+    o, ST = kda.prefill(**upload(x), wide_decay=True)
+    assert_close(host(o), ref_o, dtype, "o")
+    assert_close(host(ST), ref_S, dtype, "S_T")
+
+
 @pytest.mark.parametrize("lengths", [[300, 1, 64], [4096 + 500, 77]], ids=["short", "segmented"])
 def test_wide_decay_keeps_the_bits_within_the_default_contract(lengths):
     """Within the default contract no channel moves its reference, and the
