@@ -259,6 +259,26 @@ __device__ __forceinline__ typename Elem<BF16>::F4 tile_quad(const void* tile, i
                                                               quad_off<BF16, U>(r, Q));
 }
 
+// Byte offset of quad Q (four consecutive tokens) of row r of a V^T tile.
+// bf16 (32-token rows of eight 8-byte quads): rows are paired into 128-byte
+// blocks m = r / 2, whose 16 quads are permuted by
+//     slot = (8 (r & 1) + Q) ^ h(m),   h(m) = ((m >> 1) & 15) ^ ((m & 1) << 2),
+// so that each of the tile's 8-byte accesses is free of LDS bank conflicts:
+// the producers' V transpose and O read-back (rows 4 l + c of lane l) and the
+// consumers' V reads and O staging (rows r0 + 0..15).  fp32 tiles (16-byte
+// quads) keep the row layout of quad_off.
+template <bool BF16, int U>
+__device__ __forceinline__ int vt_off(int r, int Q) {
+    if constexpr (BF16) {
+        static_assert(U == 4, "V^T rows of 32 bf16 tokens");
+        const int m = r >> 1;
+        const int h = ((m >> 1) & 15) ^ ((m & 1) << 2);
+        return 128 * m + 8 * ((((r & 1) << 3) | Q) ^ h);
+    } else {
+        return quad_off<BF16, U>(r, Q);
+    }
+}
+
 // Transposes a 4x4 block given as four raw row quads into four column quads.
 template <bool BF16>
 __device__ __forceinline__ void transpose4(const typename Elem<BF16>::R4 (&rows)[4],
@@ -713,7 +733,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             for (int rt = 0; rt < NB; ++rt) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    const f32x4_t v4 = lds_load4<BF16>(tile_at<BF16>(tVt(B), quad_off<BF16, UT>(col0(ct) + ln, 4 * rt + lg)));
+                    const f32x4_t v4 = lds_load4<BF16>(tile_at<BF16>(tVt(B), vt_off<BF16, UT>(col0(ct) + ln, 4 * rt + lg)));
                     Rp[ct][rt] = f32x4_t{-v4[0], -v4[1], -v4[2], -v4[3]};
                 }
 #pragma unroll
@@ -789,7 +809,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                 }
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
-                    lds_store4<BF16>(tile_at<BF16>(tVt(B), quad_off<BF16, UT>(col0(ct) + ln, 4 * rt + lg)),
+                    lds_store4<BF16>(tile_at<BF16>(tVt(B), vt_off<BF16, UT>(col0(ct) + ln, 4 * rt + lg)),
                                      acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
             }
         };
@@ -989,7 +1009,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                     R4 cols[4];
                     transpose4<BF16>(rv[x][vv], cols);
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) T::lds_put_raw4(tile_at<BF16>(tVt(S), quad_off<BF16, UT>(c4 + c, r0 / 4)), cols[c]);
+                    for (int c = 0; c < 4; ++c) T::lds_put_raw4(tile_at<BF16>(tVt(S), vt_off<BF16, UT>(c4 + c, r0 / 4)), cols[c]);
                 }
             }
             if (!qok) return;
@@ -1116,7 +1136,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                 const int r0 = ok ? 4 * (idx / (BV / 4)) : 0;
                 R4 q4[4], rows[4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) q4[c] = lds_get_raw4<BF16>(tile_at<BF16>(tVt(S), quad_off<BF16, UT>(c4 + c, r0 / 4)));
+                for (int c = 0; c < 4; ++c) q4[c] = lds_get_raw4<BF16>(tile_at<BF16>(tVt(S), vt_off<BF16, UT>(c4 + c, r0 / 4)));
                 transpose4<BF16>(q4, rows);
                 const int off = ok ? r0 * rowV + c4 * GS : kNoAccess;
 #pragma unroll
