@@ -279,6 +279,36 @@ __device__ __forceinline__ int vt_off(int r, int Q) {
     }
 }
 
+// Byte offset of quad Q (four consecutive tokens) of row r of the Kbar^T
+// tile.  bf16 (32-token rows, one 32-deep block): rows are paired into
+// 128-byte blocks m = r / 2 of eight 16-byte units, and a unit keeps the two
+// quads g and g + 4 that one MFMA operand fragment reads:
+//     unit = (4 (r & 1) + (Q & 3)) ^ h(m),   h(m) = x ^ ((x & 1) << 1), x = (m >> 1) & 7,
+// half (Q >> 2) & 1.  The producers' quad writes (rows i0 + c of eight lanes
+// 4 rows apart) and the consumers' fragment reads (rows r0 + 0..15) are then
+// free of LDS bank conflicts.  fp32 tiles keep the row layout of quad_off.
+template <bool BF16, int U>
+__device__ __forceinline__ int kbt_off(int r, int Q) {
+    if constexpr (BF16) {
+        static_assert(U == 4, "Kbar^T rows of 32 bf16 tokens");
+        const int m = r >> 1, x = (m >> 1) & 7;
+        const int h = x ^ ((x & 1) << 1);
+        return 128 * m + 16 * ((((r & 1) << 2) | (Q & 3)) ^ h) + 8 * ((Q >> 2) & 1);
+    } else {
+        return quad_off<BF16, U>(r, Q);
+    }
+}
+
+// MFMA fragment of lane group g of row r of the Kbar^T tile (one 32-deep block)
+template <bool BF16, int U>
+__device__ __forceinline__ typename Elem<BF16>::F8 kbt_frag8(const void* tile, int r, int g) {
+    if constexpr (BF16) {
+        return *reinterpret_cast<const bf16x8_t*>(static_cast<const unsigned char*>(tile) + kbt_off<BF16, U>(r, g));
+    } else {
+        return tile_frag8<BF16, U>(tile, r, 0, g);
+    }
+}
+
 // Transposes a 4x4 block given as four raw row quads into four column quads.
 template <bool BF16>
 __device__ __forceinline__ void transpose4(const typename Elem<BF16>::R4 (&rows)[4],
@@ -825,7 +855,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                                       Sr[ct][it][3] * g4.w};
 #pragma unroll
                 for (int kb = 0; kb < NB / 2; ++kb) {
-                    const F8 a = tile_frag8<BF16, UT>(tKbT(B), 16 * it + ln, kb, lg);
+                    const F8 a = kbt_frag8<BF16, UT>(tKbT(B), 16 * it + ln, lg);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], a, u_frag8(ct, 2 * kb));
                 }
@@ -1100,7 +1130,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             }
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                lds_store4<BF16>(tile_at<BF16>(tKbT(S), quad_off<BF16, UT>(i0 + c, rg)), kbar[0][c], kbar[1][c], kbar[2][c],
+                lds_store4<BF16>(tile_at<BF16>(tKbT(S), kbt_off<BF16, UT>(i0 + c, rg)), kbar[0][c], kbar[1][c], kbar[2][c],
                                  kbar[3][c]);
         };
 
