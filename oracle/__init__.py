@@ -22,8 +22,8 @@ import numpy as np
 
 from .build import build_oracle, library_path
 
-__all__ = ["prefill", "decode_step", "gdn_prefill", "gdn_decode_step", "build_oracle", "library_path",
-           "load", "bind"]
+__all__ = ["prefill", "decode_step", "gdn_prefill", "gdn_decode_step", "prefill_backward",
+           "gdn_prefill_backward", "build_oracle", "library_path", "load", "bind"]
 
 _LIB = None
 
@@ -56,6 +56,13 @@ def bind(path: str) -> ctypes.CDLL:
     lib.kda_oracle_decode_step.argtypes = [f32p, f32p, f32p, f32p, f32p, f64p,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, u8p, f64p, ctypes.c_int32]
+    if hasattr(lib, "kda_oracle_prefill_backward"):
+        lib.kda_oracle_prefill_backward.restype = ctypes.c_int
+        lib.kda_oracle_prefill_backward.argtypes = [f32p, f32p, f32p, f32p, f32p, f64p, i32p,
+                                                    ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.c_int32, f64p, f64p, u8p,
+                                                    f64p, f64p, f64p, f64p, f64p, f64p,
+                                                    ctypes.c_int32]
     return lib
 
 
@@ -171,3 +178,66 @@ def gdn_decode_step(q, k, v, log_alpha, beta, S: np.ndarray, **kw):
     la = np.asarray(log_alpha, dtype=np.float32)
     la = np.ascontiguousarray(np.broadcast_to(la[:, :, None], la.shape + (q.shape[2],)))
     return decode_step(q, k, v, la, beta, S, **kw)
+
+
+def prefill_backward(q, k, v, log_alpha, beta, S0: Optional[np.ndarray], cu_seqlens, dO,
+                     dS_T: Optional[np.ndarray] = None, pair_mask: Optional[np.ndarray] = None,
+                     nthreads: Optional[int] = None, lib: Optional[ctypes.CDLL] = None):
+    """Gradients of a scalar loss through ``prefill``, given dO = dL/do
+    ([T, H, d_v]) and dS_T = dL/dS_T ([N, H, d_k, d_v], None: zero).
+
+    Returns (dq, dk, dv, dlog_alpha, dbeta, dS0) as float64 arrays shaped like
+    q, k, v, log_alpha, beta and the initial state.  Reverse-mode
+    differentiation of the same token recurrence, last token first."""
+    lib = lib or load()
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    N = int(cu.shape[0] - 1)
+    T = int(cu[-1])
+    q = np.asarray(q)
+    H, dk = int(q.shape[1]), int(q.shape[2])
+    dv = int(np.asarray(v).shape[2])
+    q = _f32(q, (T, H, dk))
+    k = _f32(k, (T, H, dk))
+    v = _f32(v, (T, H, dv))
+    la = _f32(log_alpha, (T, H, dk))
+    b = _f32(beta, (T, H))
+    s0 = None
+    if S0 is not None:
+        s0 = np.ascontiguousarray(np.asarray(S0, dtype=np.float64))
+        if s0.shape != (N, H, dk, dv):
+            raise ValueError(f"S0 shape {s0.shape} != {(N, H, dk, dv)}")
+    do = np.ascontiguousarray(np.asarray(dO, dtype=np.float64))
+    if do.shape != (T, H, dv):
+        raise ValueError(f"dO shape {do.shape} != {(T, H, dv)}")
+    dst = None
+    if dS_T is not None:
+        dst = np.ascontiguousarray(np.asarray(dS_T, dtype=np.float64))
+        if dst.shape != (N, H, dk, dv):
+            raise ValueError(f"dS_T shape {dst.shape} != {(N, H, dk, dv)}")
+    mask = None
+    if pair_mask is not None:
+        mask = np.ascontiguousarray(np.asarray(pair_mask, dtype=np.uint8).reshape(N, H))
+    outs = [np.full(sh, np.nan, dtype=np.float64) for sh in
+            ((T, H, dk), (T, H, dk), (T, H, dv), (T, H, dk), (T, H), (N, H, dk, dv))]
+    f64 = ctypes.c_double
+    rc = lib.kda_oracle_prefill_backward(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                                         _ptr(v, ctypes.c_float), _ptr(la, ctypes.c_float),
+                                         _ptr(b, ctypes.c_float), _ptr(s0, f64),
+                                         _ptr(cu, ctypes.c_int32), N, T, H, dk, dv,
+                                         _ptr(do, f64), _ptr(dst, f64), _ptr(mask, ctypes.c_uint8),
+                                         *[_ptr(x, f64) for x in outs],
+                                         int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_prefill_backward failed with status {rc}")
+    return tuple(outs)
+
+
+def gdn_prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, dO, dS_T=None, **kw):
+    """Backward of ``gdn_prefill``: the per-channel backward with the gate
+    repeated over the channels, its log-gate gradient summed over them (the
+    chain rule of that repetition).  dlog_alpha is [T, H]."""
+    q = np.asarray(q)
+    la = np.asarray(log_alpha, dtype=np.float32)
+    la = np.ascontiguousarray(np.broadcast_to(la[:, :, None], la.shape + (q.shape[2],)))
+    dq, dk, dv, dla, db, dS0 = prefill_backward(q, k, v, la, beta, S0, cu_seqlens, dO, dS_T, **kw)
+    return dq, dk, dv, dla.sum(axis=2), db, dS0

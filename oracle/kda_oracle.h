@@ -52,6 +52,21 @@ int kda_oracle_decode_step(const float* q, const float* k, const float* v,
                            int32_t N, int32_t H, int32_t d_k, int32_t d_v,
                            const uint8_t* pair_mask, double* o, int32_t nthreads);
 
+/* Backward pass of kda_oracle_prefill: gradients of a scalar loss given
+ * dO = dL/do [T_tot, H, d_v] and dS_T = dL/dS_T [N, H, d_k, d_v] (NULL: zero).
+ * Outputs (fp64, same layouts as the matching inputs): dq, dk [T_tot, H, d_k],
+ * dv [T_tot, H, d_v], dlog_alpha [T_tot, H, d_k], dbeta [T_tot, H], and
+ * dS0 [N, H, d_k, d_v], the gradient with respect to the initial state (also
+ * when S0 is NULL, i.e. zero).  Reverse-mode differentiation of the token
+ * recurrence, token by token from the last; see kda_oracle.c. */
+int kda_oracle_prefill_backward(const float* q, const float* k, const float* v,
+                                const float* log_alpha, const float* beta,
+                                const double* S0, const int32_t* cu_seqlens,
+                                int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
+                                const double* dO, const double* dS_T, const uint8_t* pair_mask,
+                                double* dq, double* dk, double* dv, double* dlog_alpha,
+                                double* dbeta, double* dS0, int32_t nthreads);
+
 #ifdef __cplusplus
 }
 #endif

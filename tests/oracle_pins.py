@@ -346,6 +346,77 @@ def pin_segments_compose(lib):
     _close(S_in, ST, "S_T")
 
 
+# --------------------------------------------------------------------------
+# Backward pass: finite differences of the forward, and a closed form
+# --------------------------------------------------------------------------
+def _loss_grad_case(rng, lengths, H, dk, dv):
+    q, k, v, la, beta, S0, cu = _random_case(rng, lengths, H, dk, dv, la_hi=0.5)
+    Ro = rng.standard_normal((int(cu[-1]), H, dv))
+    RS = rng.standard_normal((len(lengths), H, dk, dv))
+    return q, k, v, la, beta, S0, cu, Ro, RS
+
+
+def pin_backward_finite_differences(lib):
+    """Each gradient of L = sum(o * Ro) + sum(S_T * RS) equals the central
+    difference of the (separately pinned) forward.  The fp32 inputs are
+    perturbed by h and the difference is divided by the step actually taken.
+    Lengths include an empty sequence and one longer than the 64-token block
+    the backward recomputes states in."""
+    rng = np.random.default_rng(71)
+    for lengths, H, dk, dv in (([4, 0, 3], 2, 3, 2), ([70], 1, 2, 2)):
+        q, k, v, la, beta, S0, cu, Ro, RS = _loss_grad_case(rng, lengths, H, dk, dv)
+        grads = oracle.prefill_backward(q, k, v, la, beta, S0, cu, Ro, RS, lib=lib)
+        args = [q, k, v, la, beta]
+
+        def loss(a, s0):
+            o, ST = oracle.prefill(*a, s0, cu, lib=lib)
+            return float((o * Ro).sum() + (ST * RS).sum())
+
+        for ai, name in enumerate(("dq", "dk", "dv", "dlog_alpha", "dbeta")):
+            x = args[ai]
+            fd = np.zeros(x.shape)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += np.float32(2.0 ** -10)
+                xm[idx] -= np.float32(2.0 ** -10)
+                ap, am = list(args), list(args)
+                ap[ai], am[ai] = xp, xm
+                fd[idx] = (loss(ap, S0) - loss(am, S0)) / (float(xp[idx]) - float(xm[idx]))
+            _close(grads[ai], fd, f"{name} vs finite differences {lengths}", rtol=2e-5, atol=1e-7)
+        fd = np.zeros(S0.shape)
+        for idx in np.ndindex(S0.shape):
+            sp, sm = S0.copy(), S0.copy()
+            sp[idx] += 1e-6
+            sm[idx] -= 1e-6
+            fd[idx] = (loss(args, sp) - loss(args, sm)) / 2e-6
+        _close(grads[5], fd, f"dS0 vs finite differences {lengths}", rtol=1e-7, atol=1e-8)
+
+
+def pin_backward_frozen_state_closed_form(lib):
+    """beta = 0 and alpha = 1 freeze the state at S0, so o_t = S0^T q_t and the
+    gradient reaching S_t is G_t = dS_T + sum over tau >= t of q_tau do_tau^T.
+    Then dq_t = S0 do_t, dk = dv = 0, dbeta_t = k_t^T G_t (v_t - S0^T k_t),
+    dlog_alpha_t[i] = sum_j G_t[i, j] S0[i, j] and dS0 = G at the first token."""
+    rng = np.random.default_rng(72)
+    q, k, v, la, beta, S0, cu, Ro, RS = _loss_grad_case(rng, [5, 3], 2, 4, 3)
+    beta = np.zeros_like(beta)
+    la = np.zeros_like(la)
+    dq, dk, dv, dla, db, dS0 = oracle.prefill_backward(q, k, v, la, beta, S0, cu, Ro, RS, lib=lib)
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        for h in range(q.shape[1]):
+            S = S0[n, h]
+            G = RS[n, h].copy()
+            for t in range(b - 1, a - 1, -1):
+                G = G + np.outer(q[t, h], Ro[t, h])
+                _close(dq[t, h], S @ Ro[t, h], "dq")
+                _close(db[t, h], k[t, h] @ G @ (v[t, h] - S.T @ k[t, h]), "dbeta")
+                _close(dla[t, h], (G * S).sum(axis=1), "dlog_alpha")
+            _close(dS0[n, h], G, "dS0")
+    _close(dk, np.zeros_like(dk), "dk")
+    _close(dv, np.zeros_like(dv), "dv")
+
+
 PINS = [
     pin_segments_compose,
     pin_bruteforce_product,
@@ -362,6 +433,8 @@ PINS = [
     pin_decode_steps_equal_prefill,
     pin_resume_from_state,
     pin_zero_state_and_empty_sequences,
+    pin_backward_finite_differences,
+    pin_backward_frozen_state_closed_form,
 ]
 
 

@@ -37,6 +37,24 @@ MUTANTS = [
      "for (int64_t t = J->cu[n] + (J->cu[n + 1] > J->cu[n]); t < J->cu[n + 1]; ++t)"),
     ("rank1_update_dropped", "S[(size_t)i * dv + j] += ki * u[j];",
      "S[(size_t)i * dv + j] += 0.0 * ki * u[j];"),
+    # backward pass
+    ("bwd_readout_grad_uses_pre_update_state", "acc += dSp[(size_t)i * dv + j] * dot[j];",
+     "acc += S[(size_t)i * dv + j] * dot[j];"),
+    ("bwd_readout_grad_not_accumulated", "G[(size_t)i * dv + j] += (double)qt[i] * dot[j];",
+     "G[(size_t)i * dv + j] += 0.0 * (double)qt[i] * dot[j];"),
+    ("bwd_beta_grad_uses_scaled_error", "db += de[j] * w[j];", "db += de[j] * bt * w[j];"),
+    ("bwd_key_grad_prediction_term_dropped", "J->dk_[tk + i] = tmp[i] + acc;", "J->dk_[tk + i] = tmp[i];"),
+    ("bwd_decay_grad_uses_decayed_state", "da += g * Sp[(size_t)i * dv + j];",
+     "da += g * S[(size_t)i * dv + j];"),
+    ("bwd_state_grad_not_decayed", "G[(size_t)i * dv + j] = a * g;", "G[(size_t)i * dv + j] = g;"),
+    ("bwd_value_grad_beta_dropped", "J->dv_[tv + j] = bt * de[j];", "J->dv_[tv + j] = de[j];"),
+    ("bwd_prediction_grad_sign", "du[j] = -bt * de[j];", "du[j] = bt * de[j];"),
+    ("bwd_key_grad_transposed_state", "acc += S[(size_t)i * dv + j] * du[j];",
+     "acc += S[((size_t)j * dk + i) % ((size_t)dk * dv)] * du[j];"),
+    ("bwd_states_one_token_late",
+     "memcpy(states + (size_t)(t - tb) * SS, S, sizeof(double) * SS);\n            forward_token(J, t, h, S, u);",
+     "forward_token(J, t, h, S, u);\n            memcpy(states + (size_t)(t - tb) * SS, S, sizeof(double) * SS);"),
+    ("bwd_final_state_grad_ignored", "if (J->dST) memcpy(G,", "if (0) memcpy(G,"),
 ]
 
 _CHILD = r"""
