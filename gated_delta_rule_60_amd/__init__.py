@@ -29,6 +29,8 @@ from ._lib import (  # noqa: F401
     kda_decode_step,
     kda_last_error,
     kda_prefill,
+    kda_prefill_backward,
+    kda_prefill_backward_workspace_size,
     kda_prefill_default_split,
     kda_prefill_ex,
     kda_prefill_split,
@@ -38,6 +40,7 @@ from ._lib import (  # noqa: F401
     library_path,
     load,
     prefill,
+    prefill_backward,
 )
 
 __version__ = "0.1.0"

@@ -45,6 +45,10 @@ SIGNATURES = {
                                          _i32, ctypes.c_int, _vp, _fp, _vp, _sz, _i32, _vp]),
     "gdn_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _i32, _i32, _i32, _i32,
                                        ctypes.c_int, _vp, _vp]),
+    "kda_prefill_backward": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32,
+                                            _i32, ctypes.c_int, _vp, _fp, _fp, _fp, _fp, _fp, _fp, _fp,
+                                            _vp, _sz, _vp]),
+    "kda_prefill_backward_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int]),
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_last_error": (ctypes.c_char_p, []),
     "kda_version": (_i32, []),
@@ -138,6 +142,18 @@ def kda_last_error() -> str:
 
 def kda_version() -> int:
     return int(load().kda_version())
+
+
+def kda_prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, d_o,
+                         d_S_T, d_q, d_k_out, d_v_out, d_log_alpha, d_beta, d_S0, workspace,
+                         workspace_bytes, stream) -> int:
+    return load().kda_prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
+                                       dtype, d_o, d_S_T, d_q, d_k_out, d_v_out, d_log_alpha, d_beta,
+                                       d_S0, workspace, workspace_bytes, stream)
+
+
+def kda_prefill_backward_workspace_size(N, T_tot, H, d_k, d_v, dtype) -> int:
+    return int(load().kda_prefill_backward_workspace_size(N, T_tot, H, d_k, d_v, dtype))
 
 
 def _check(status: int) -> None:
@@ -287,3 +303,50 @@ def gdn_decode_step_t(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
     """One Gated DeltaNet decode step (log_alpha [N, H]); S is updated in
     place.  Returns o [N, H, d_v] in q's dtype."""
     return _decode(q, k, v, log_alpha, beta, S, o, stream, True)
+
+
+def prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T=None, *, workspace=None,
+                     stream=None):
+    """Backward of ``prefill`` on torch tensors: gradients of a loss given
+    d_o = dL/do ([T, H, d_v], dtype of q) and d_S_T = dL/dS_T ([N, H, d_k,
+    d_v] fp32, or None).  Returns fp32 (d_q, d_k, d_v, d_log_alpha, d_beta,
+    d_S0) shaped like q, k, v, log_alpha, beta and the initial state.
+    ``workspace``: optional uint8 device tensor of at least
+    ``kda_prefill_backward_workspace_size(...)`` bytes (allocated if None)."""
+    import torch
+    if not q.is_cuda:
+        raise ValueError("kda prefill backward runs on a GPU device; q is on the CPU")
+    dev = q.device
+    T, H, dk = (int(x) for x in q.shape)
+    dv = int(v.shape[-1])
+    code = _dtype_code(q)
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    N = int(cu_seqlens.shape[0]) - 1
+    _need(q, "q", (T, H, dk), q.dtype, dev)
+    _need(k, "k", (T, H, dk), q.dtype, dev)
+    _need(v, "v", (T, H, dv), q.dtype, dev)
+    _need(log_alpha, "log_alpha", (T, H, dk), torch.float32, dev)
+    _need(beta, "beta", (T, H), torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    _need(d_o, "d_o", (T, H, dv), q.dtype, dev)
+    if S0 is not None:
+        _need(S0, "S0", (N, H, dk, dv), torch.float32, dev)
+    if d_S_T is not None:
+        _need(d_S_T, "d_S_T", (N, H, dk, dv), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    gq, gk, gv = torch.empty((T, H, dk), **f32), torch.empty((T, H, dk), **f32), torch.empty((T, H, dv), **f32)
+    gla, gb, gS0 = torch.empty((T, H, dk), **f32), torch.empty((T, H), **f32), torch.empty((N, H, dk, dv), **f32)
+    ws = kda_prefill_backward_workspace_size(N, T, H, dk, dv, code)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    with torch.cuda.device(dev):
+        _check(kda_prefill_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
+                                    beta.data_ptr(), ptr(S0), cu_seqlens.data_ptr(), N, T, H, dk, dv, code,
+                                    d_o.data_ptr(), ptr(d_S_T), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
+                                    gla.data_ptr(), gb.data_ptr(), gS0.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel(), _stream_handle(stream, dev)))
+    return gq, gk, gv, gla, gb, gS0

@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 _CSRC = os.path.join(_HERE, "csrc")
 
-SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_segment.hip", "kda_decode.hip"]
+SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_segment.hip", "kda_decode.hip", "kda_backward.hip"]
 ARCH = "gfx950"
 
 

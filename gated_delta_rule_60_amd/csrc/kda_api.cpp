@@ -70,6 +70,53 @@ int32_t kda_prefill_default_split(int32_t N, int64_t T_tot, int32_t H, int32_t d
     return kda::default_v_split(N, T_tot, H, d_k, d_v, dtype == KDA_DTYPE_BF16);
 }
 
+size_t kda_prefill_backward_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
+                                           kda_dtype dtype) {
+    if (N < 1 || H < 1 || T_tot < 0 || !supported_dim(d_k) || !supported_dim(d_v) ||
+        (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32))
+        return 0;
+    return kda::prefill_bwd_workspace_bytes(N, T_tot, H, d_k, d_v);
+}
+
+kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const float* log_alpha,
+                                const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
+                                int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                const void* d_o, const float* d_S_T, float* d_q, float* d_k_out,
+                                float* d_v_out, float* d_log_alpha, float* d_beta, float* d_S0,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    if (N < 1 || H < 1 || T_tot < 0)
+        return fail(KDA_ERR_INVALID_ARG, "need N >= 1, H >= 1 and T_tot >= 0");
+    const kda_status ds = check_dims(d_k, d_v, dtype);
+    if (ds != KDA_OK) return ds;
+    if (!cu_seqlens || !d_S0) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens and d_S0 must not be NULL");
+    if (T_tot > 0 && (!q || !k || !v || !log_alpha || !beta || !d_o || !d_q || !d_k_out || !d_v_out ||
+                      !d_log_alpha || !d_beta))
+        return fail(KDA_ERR_INVALID_ARG,
+                    "inputs, d_o and every token gradient must not be NULL when T_tot > 0");
+    if (T_tot > INT32_MAX) return fail(KDA_ERR_INVALID_ARG, "T_tot must fit in int32 (cu_seqlens is int32)");
+    if (static_cast<int64_t>(N) * H * (d_v / 8) > (int64_t{1} << 22))
+        return fail(KDA_ERR_INVALID_ARG, "N * H too large");
+    const void* ptrs[] = {q, k, v, log_alpha, d_o, S0, d_S_T, d_q, d_k_out, d_v_out, d_log_alpha, d_S0};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (d_beta && (reinterpret_cast<uintptr_t>(d_beta) & 3u) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "d_beta must be 4-byte aligned");
+    const size_t ws_need = kda_prefill_backward_workspace_size(N, T_tot, H, d_k, d_v, dtype);
+    if (workspace_bytes < ws_need)
+        return fail(KDA_ERR_INVALID_ARG, "workspace smaller than kda_prefill_backward_workspace_size");
+    if (!workspace) return fail(KDA_ERR_INVALID_ARG, "workspace must not be NULL");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    kda::BackwardArgs a{q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, N, T_tot, H, d_k, d_v,
+                        dtype == KDA_DTYPE_BF16, d_q, d_k_out, d_v_out, d_log_alpha, d_beta, d_S0,
+                        workspace, stream};
+    (void)hipGetLastError();  // report only this launch's status
+    const hipError_t e = kda::launch_prefill_bwd(a);
+    if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
+    return KDA_OK;
+}
+
 }  // extern "C"
 
 namespace {

@@ -1,0 +1,491 @@
+// kda_backward.hip -- backward pass of the KDA prefill on gfx950.
+//
+// Gradients of a scalar loss with respect to q, k, v, log alpha, beta and the
+// initial state, given dL/do for every token and dL/dS_T for the final states.
+// The forward recurrence (the update rule of "Kimi Linear：让长上下文大模型真正实用
+// 的线性注意力架构", section 三.5, with per-channel gates from section 三.1 and
+// the read-out o_t = S_t^T q_t after the update) is, per token,
+//
+//     S' = Diag(a) S_{t-1},  u = S'^T k,  w = v - u,  e = beta w,
+//     S_t = S' + k e^T,      o_t = S_t^T q.
+//
+// Its reverse-mode derivative, with G = dL/dS_t carried from the last token:
+//
+//     dq = S_t do,  G += q do^T,  de = G^T k,  dv = beta de,  dbeta = de . w,
+//     du = -beta de,  dk = G e + S' du,  dS' = G + k du^T,
+//     dlog_alpha_i = a_i sum_j dS'_ij S_{t-1,ij},  G <- Diag(a) dS'.
+//
+// The columns of the state evolve independently of one another (column j
+// sees only v_j), so one wave owns 8 value columns of one (sequence, head)
+// for the whole sequence: every column sum of the recurrence (u and de) is a
+// reduction across the lanes of one wave, with no barrier on the token chain.
+// Row sums over the value columns (dq, dk, dlog_alpha) and dbeta are not on
+// that chain; they are staged in LDS and summed over the workgroup's waves
+// once per 8 tokens.
+//
+// Pass 1 (bwd_forward_kernel) runs the forward recurrence and stores the
+// state entering every 16-token block (fp32 checkpoints) and w_t = v_t - u_t
+// for every token.  Pass 2 (bwd_kernel) walks the blocks from the last,
+// recomputes the states of 8 tokens at a time from the block's checkpoint
+// into registers (steps that need no column sum, since w is stored), and
+// applies the reverse step token by token.
+//
+// Arithmetic is fp32 on the vector ALU: the per-token work is rank-1 updates
+// and matrix-vector products, with no dense contraction to give to MFMA.
+#include <hip/hip_runtime.h>
+
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int kBwdBlock = 16;  // tokens per checkpoint block
+constexpr int kBwdHalf = 8;    // tokens whose entering states are held in registers at once
+constexpr int kBwdCols = 8;    // value columns per wave
+
+// Lane layout of one wave's share (kBwdCols columns, all d_k rows) of a state.
+//   d_k >= 64: lane l holds rows R l .. R l + R - 1 (R = d_k / 64) and all 8 columns.
+//   d_k == 32: lane l holds row l & 31 and columns 4 (l >> 5) .. 4 (l >> 5) + 3.
+template <int DK>
+struct BwdLanes {
+    static_assert(DK == 32 || DK == 64 || DK == 128, "d_k in {32, 64, 128}");
+    static constexpr int R = DK >= 64 ? DK / 64 : 1;
+    static constexpr int CPL = DK >= 64 ? kBwdCols : kBwdCols / 2;
+    __device__ static int row(int lane, int rr) { return DK >= 64 ? R * lane + rr : (lane & 31); }
+    __device__ static int col(int lane) { return DK >= 64 ? 0 : 4 * (lane >> 5); }
+};
+
+template <bool BF16>
+__device__ __forceinline__ float ld(const typename Elem<BF16>::G* p) {
+    if constexpr (BF16) {
+        return bf16_to_f32(*p);
+    } else {
+        return *p;
+    }
+}
+
+// Sum over the rows of each of the lane's columns (the wave holds every row
+// of its 8 columns), returned in every lane: a butterfly that halves the
+// values a lane carries at each exchange, then a gather of the 8 (or 4)
+// column totals.
+template <int DK>
+__device__ __forceinline__ void column_sums(const float (&p)[BwdLanes<DK>::CPL], float (&out)[BwdLanes<DK>::CPL],
+                                            int lane) {
+    if constexpr (DK >= 64) {
+        const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+        float h4[4], h2[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float send = b5 ? p[i] : p[i + 4];
+            h4[i] = (b5 ? p[i + 4] : p[i]) + __shfl_xor(send, 32);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float send = b4 ? h4[i] : h4[i + 2];
+            h2[i] = (b4 ? h4[i + 2] : h4[i]) + __shfl_xor(send, 16);
+        }
+        float s = (b3 ? h2[1] : h2[0]) + __shfl_xor(b3 ? h2[0] : h2[1], 8);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 1);
+        // lane l now holds the total of column 4 b5 + 2 b4 + b3
+#pragma unroll
+        for (int c = 0; c < 8; ++c) out[c] = __shfl(s, (c << 3) | (lane & 7));
+    } else {
+        const bool b4 = lane & 16, b3 = lane & 8;
+        float h2[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float send = b4 ? p[i] : p[i + 2];
+            h2[i] = (b4 ? p[i + 2] : p[i]) + __shfl_xor(send, 16);
+        }
+        float s = (b3 ? h2[1] : h2[0]) + __shfl_xor(b3 ? h2[0] : h2[1], 8);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 1);
+        // lane l holds the total of column 2 b4 + b3 of its half (lane & 32)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) out[c] = __shfl(s, (lane & 32) | (c << 3) | (lane & 7));
+    }
+}
+
+struct BwdArgs {
+    const void *q, *k, *v, *dO;
+    const float *la, *beta, *S0, *dST;
+    const int32_t* cu;
+    int32_t N, H, DV;
+    float *ckpt, *w;
+    float *dq, *dk, *dv, *dla, *dbeta, *dS0;
+};
+
+__device__ __forceinline__ int64_t ckpt_slot(const int32_t* cu, int n, int b) {
+    return static_cast<int64_t>(cu[n] / kBwdBlock) + n + b;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: forward recurrence; checkpoints and w.  Grid: N * H * slices
+// workgroups of NW waves; wave wv of slice s owns columns
+// (s NW + wv) 8 .. + 7.
+// ---------------------------------------------------------------------------
+template <bool BF16, int DK, int NW>
+__global__ void __launch_bounds__(64 * NW) bwd_forward_kernel(BwdArgs a) {
+    using L = BwdLanes<DK>;
+    using G = typename Elem<BF16>::G;
+    constexpr int R = L::R, CPL = L::CPL;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int slices = a.DV / (kBwdCols * NW);
+    const int s = blockIdx.x % slices, pair = blockIdx.x / slices;
+    const int n = pair / a.H, h = pair % a.H;
+    const int H = a.H, DV = a.DV;
+    const int c0 = (s * NW + wv) * kBwdCols + L::col(lane);
+    const int64_t t0 = a.cu[n], t1 = a.cu[n + 1];
+
+    float S[R][CPL];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            S[rr][c] = a.S0 ? a.S0[((static_cast<int64_t>(n) * H + h) * DK + L::row(lane, rr)) * DV + c0 + c] : 0.f;
+
+    const G* gk = static_cast<const G*>(a.k);
+    const G* v = static_cast<const G*>(a.v);
+    for (int64_t t = t0; t < t1; ++t) {
+        if ((t - t0) % kBwdBlock == 0) {
+            float* ck = a.ckpt + (ckpt_slot(a.cu, n, static_cast<int>((t - t0) / kBwdBlock)) * H + h) * DK * DV;
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) ck[static_cast<int64_t>(L::row(lane, rr)) * DV + c0 + c] = S[rr][c];
+        }
+        const int64_t tk = (t * H + h) * DK, tv = (t * H + h) * DV;
+        float al[R], kk[R], up[CPL], u[CPL];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            al[rr] = exp_e(a.la[tk + L::row(lane, rr)]);
+            kk[rr] = ld<BF16>(gk + tk + L::row(lane, rr));
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            float acc = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) {
+                S[rr][c] *= al[rr];
+                acc = __builtin_fmaf(kk[rr], S[rr][c], acc);
+            }
+            up[c] = acc;
+        }
+        column_sums<DK>(up, u, lane);
+        const float bt = a.beta[t * H + h];
+        float wv_[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            wv_[c] = ld<BF16>(v + tv + c0 + c) - u[c];
+            const float e = bt * wv_[c];
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) S[rr][c] = __builtin_fmaf(kk[rr], e, S[rr][c]);
+        }
+        if ((lane & 31) == 0 && (DK == 32 || lane == 0)) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) a.w[tv + c0 + c] = wv_[c];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: reverse walk.  Same grid and column ownership as pass 1.
+// SLICED: more than one workgroup per (sequence, head) (two at d_v = 128);
+// their row sums meet by atomic addition in outputs zeroed beforehand.  With
+// exactly two addends on zero the result does not depend on their order.
+// ---------------------------------------------------------------------------
+template <bool BF16, int DK, int NW>
+struct BwdStage {
+    // [quantity dq, dk, dlog_alpha][token of the half][wave][row], then dbeta [token][wave]
+    static constexpr int kRowFloats = 3 * kBwdHalf * NW * DK;
+    static constexpr int kFloats = kRowFloats + kBwdHalf * NW;
+};
+
+template <bool BF16, int DK, int NW, bool SLICED>
+__global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
+    using L = BwdLanes<DK>;
+    using G = typename Elem<BF16>::G;
+    using St = BwdStage<BF16, DK, NW>;
+    constexpr int R = L::R, CPL = L::CPL;
+    __shared__ float stage[St::kFloats];
+    float* sRow = stage;
+    float* sBeta = stage + St::kRowFloats;
+
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int slices = a.DV / (kBwdCols * NW);
+    const int s = blockIdx.x % slices, pair = blockIdx.x / slices;
+    const int n = pair / a.H, h = pair % a.H;
+    const int H = a.H, DV = a.DV;
+    const int c0 = (s * NW + wv) * kBwdCols + L::col(lane);
+    const int64_t t0 = a.cu[n], t1 = a.cu[n + 1];
+    const int nblk = static_cast<int>((t1 - t0 + kBwdBlock - 1) / kBwdBlock);
+    const G* gq = static_cast<const G*>(a.q);
+    const G* gk = static_cast<const G*>(a.k);
+    const G* gdo = static_cast<const G*>(a.dO);
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
+
+    float Gr[R][CPL];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            Gr[rr][c] = a.dST ? a.dST[sbase + static_cast<int64_t>(L::row(lane, rr)) * DV + c0 + c] : 0.f;
+
+    // one forward step of token t without a column sum (w is stored)
+    auto step = [&](float (&S)[R][CPL], int64_t t) __attribute__((always_inline)) {
+        const int64_t tk = (t * H + h) * DK, tv = (t * H + h) * DV;
+        const float bt = a.beta[t * H + h];
+        float al[R], kk[R];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            al[rr] = exp_e(a.la[tk + L::row(lane, rr)]);
+            kk[rr] = ld<BF16>(gk + tk + L::row(lane, rr));
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const float e = bt * a.w[tv + c0 + c];
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) S[rr][c] = __builtin_fmaf(kk[rr], e, al[rr] * S[rr][c]);
+        }
+    };
+
+    for (int b = nblk - 1; b >= 0; --b) {
+        const int64_t tb = t0 + static_cast<int64_t>(b) * kBwdBlock;
+        const int64_t te = tb + kBwdBlock < t1 ? tb + kBwdBlock : t1;
+        const float* ck = a.ckpt + (ckpt_slot(a.cu, n, b) * H + h) * DK * DV;
+        for (int half = 1; half >= 0; --half) {
+            const int64_t th = tb + half * kBwdHalf;
+            if (th >= te) continue;  // uniform over the workgroup
+            float S[R][CPL];
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) S[rr][c] = ck[static_cast<int64_t>(L::row(lane, rr)) * DV + c0 + c];
+            for (int64_t t = tb; t < th; ++t) step(S, t);
+            float Sp[kBwdHalf][R][CPL];
+#pragma unroll
+            for (int r = 0; r < kBwdHalf; ++r) {
+#pragma unroll
+                for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) Sp[r][rr][c] = S[rr][c];
+                if (th + r < te) step(S, th + r);
+            }
+#pragma unroll
+            for (int r = kBwdHalf - 1; r >= 0; --r) {
+                const int64_t t = th + r;
+                if (t >= te) continue;
+                const int64_t tk = (t * H + h) * DK, tv = (t * H + h) * DV;
+                const float bt = a.beta[t * H + h];
+                float al[R], kk[R], qq[R], dqp[R], dkp[R], dap[R];
+                float wv_[CPL], dov[CPL], dep[CPL], de[CPL];
+#pragma unroll
+                for (int rr = 0; rr < R; ++rr) {
+                    const int row = L::row(lane, rr);
+                    al[rr] = exp_e(a.la[tk + row]);
+                    kk[rr] = ld<BF16>(gk + tk + row);
+                    qq[rr] = ld<BF16>(gq + tk + row);
+                    dqp[rr] = 0.f;
+                    dkp[rr] = 0.f;
+                    dap[rr] = 0.f;
+                }
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    wv_[c] = a.w[tv + c0 + c];
+                    dov[c] = ld<BF16>(gdo + tv + c0 + c);
+                    dep[c] = 0.f;
+                }
+                // read-out and the rank-1 correction: dq = S_t do, G += q do^T, de = G^T k
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const float e = bt * wv_[c];
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr) {
+                        const float st = __builtin_fmaf(kk[rr], e, al[rr] * Sp[r][rr][c]);
+                        dqp[rr] = __builtin_fmaf(st, dov[c], dqp[rr]);
+                        Gr[rr][c] = __builtin_fmaf(qq[rr], dov[c], Gr[rr][c]);
+                        dep[c] = __builtin_fmaf(Gr[rr][c], kk[rr], dep[c]);
+                    }
+                }
+                column_sums<DK>(dep, de, lane);
+                // error, prediction and decay
+                float dbp = 0.f;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    dbp = __builtin_fmaf(de[c], wv_[c], dbp);
+                    const float e = bt * wv_[c];
+                    const float du = -bt * de[c];
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr) {
+                        const float sd = al[rr] * Sp[r][rr][c];
+                        dkp[rr] = __builtin_fmaf(Gr[rr][c], e, __builtin_fmaf(sd, du, dkp[rr]));
+                        const float g = __builtin_fmaf(kk[rr], du, Gr[rr][c]);
+                        dap[rr] = __builtin_fmaf(g, Sp[r][rr][c], dap[rr]);
+                        Gr[rr][c] = al[rr] * g;
+                    }
+                }
+                if (DK >= 64 ? lane == 0 : (lane & 31) == 0) {
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) a.dv[tv + c0 + c] = bt * de[c];
+                }
+                if constexpr (DK == 32) {
+                    // the two column halves of a row meet
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr) {
+                        dqp[rr] += __shfl_xor(dqp[rr], 32);
+                        dkp[rr] += __shfl_xor(dkp[rr], 32);
+                        dap[rr] += __shfl_xor(dap[rr], 32);
+                    }
+                    dbp += __shfl_xor(dbp, 32);
+                }
+                if (DK >= 64 || lane < 32) {
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr) {
+                        const int row = L::row(lane, rr);
+                        sRow[((0 * kBwdHalf + r) * NW + wv) * DK + row] = dqp[rr];
+                        sRow[((1 * kBwdHalf + r) * NW + wv) * DK + row] = dkp[rr];
+                        sRow[((2 * kBwdHalf + r) * NW + wv) * DK + row] = al[rr] * dap[rr];
+                    }
+                }
+                if (lane == 0) sBeta[r * NW + wv] = dbp;
+            }
+            __syncthreads();
+            // sums over the waves, one output element per thread and item
+            for (int it = threadIdx.x; it < 3 * kBwdHalf * DK + kBwdHalf; it += 64 * NW) {
+                if (it < 3 * kBwdHalf * DK) {
+                    const int qn = it / (kBwdHalf * DK), r = (it / DK) % kBwdHalf, row = it % DK;
+                    const int64_t t = th + r;
+                    if (t < te) {
+                        float acc = 0.f;
+                        for (int w2 = 0; w2 < NW; ++w2) acc += sRow[((qn * kBwdHalf + r) * NW + w2) * DK + row];
+                        float* out = qn == 0 ? a.dq : (qn == 1 ? a.dk : a.dla);
+                        float* dst = out + (t * H + h) * DK + row;
+                        if constexpr (SLICED) {
+                            atomicAdd(dst, acc);
+                        } else {
+                            *dst = acc;
+                        }
+                    }
+                } else {
+                    const int r = it - 3 * kBwdHalf * DK;
+                    const int64_t t = th + r;
+                    if (t < te) {
+                        float acc = 0.f;
+                        for (int w2 = 0; w2 < NW; ++w2) acc += sBeta[r * NW + w2];
+                        float* dst = a.dbeta + t * H + h;
+                        if constexpr (SLICED) {
+                            atomicAdd(dst, acc);
+                        } else {
+                            *dst = acc;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) a.dS0[sbase + static_cast<int64_t>(L::row(lane, rr)) * DV + c0 + c] = Gr[rr][c];
+}
+
+__global__ void __launch_bounds__(256) bwd_zero_kernel(float* __restrict__ p, int64_t count) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < count;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        p[i] = 0.f;
+}
+
+// waves per workgroup: 8 columns each, at most 64 columns per workgroup
+inline int bwd_waves(int d_v) { return d_v >= 64 ? 8 : d_v / kBwdCols; }
+
+template <bool BF16, int DK, int NW>
+hipError_t launch_bwd_nw(const BwdArgs& a, int64_t T_tot, hipStream_t st) {
+    const int slices = a.DV / (kBwdCols * NW);
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.N) * a.H * slices);
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_forward_kernel<BF16, DK, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (slices > 1) {
+        // zero the outputs the slices add into: dq, dk, dlog_alpha [T_tot, H, d_k], dbeta [T_tot, H]
+        const int64_t rowN = T_tot * a.H * DK;
+        float* bufs[4] = {a.dq, a.dk, a.dla, a.dbeta};
+        const int64_t counts[4] = {rowN, rowN, rowN, T_tot * a.H};
+        for (int i = 0; i < 4; ++i) {
+            if (counts[i] == 0) continue;
+            const int64_t blocks = (counts[i] + 255) / 256;
+            hipLaunchKernelGGL(bwd_zero_kernel, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)), dim3(256),
+                               0, st, bufs[i], counts[i]);
+        }
+        hipLaunchKernelGGL((bwd_kernel<BF16, DK, NW, true>), dim3(grid), dim3(64 * NW), 0, st, a);
+    } else {
+        hipLaunchKernelGGL((bwd_kernel<BF16, DK, NW, false>), dim3(grid), dim3(64 * NW), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+template <bool BF16, int DK>
+hipError_t launch_bwd_dk(const BwdArgs& a, int64_t T_tot, hipStream_t st) {
+    switch (bwd_waves(a.DV)) {
+        case 4: return launch_bwd_nw<BF16, DK, 4>(a, T_tot, st);
+        case 8: return launch_bwd_nw<BF16, DK, 8>(a, T_tot, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+size_t prefill_bwd_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v) {
+    const int64_t slots = T_tot / kBwdBlock + N + 1;
+    const size_t ck = static_cast<size_t>(slots) * H * d_k * d_v * sizeof(float);
+    const size_t w = static_cast<size_t>(T_tot) * H * d_v * sizeof(float);
+    return ((ck + 255) / 256) * 256 + w;
+}
+
+hipError_t launch_prefill_bwd(const BackwardArgs& b) {
+    BwdArgs a;
+    a.q = b.q;
+    a.k = b.k;
+    a.v = b.v;
+    a.dO = b.dO;
+    a.la = b.log_alpha;
+    a.beta = b.beta;
+    a.S0 = b.S0;
+    a.dST = b.dS_T;
+    a.cu = b.cu_seqlens;
+    a.N = b.N;
+    a.H = b.H;
+    a.DV = b.d_v;
+    const int64_t slots = b.T_tot / kBwdBlock + b.N + 1;
+    const size_t ck = static_cast<size_t>(slots) * b.H * b.d_k * b.d_v * sizeof(float);
+    a.ckpt = static_cast<float*>(b.workspace);
+    a.w = reinterpret_cast<float*>(static_cast<unsigned char*>(b.workspace) + ((ck + 255) / 256) * 256);
+    a.dq = b.dq;
+    a.dk = b.dk;
+    a.dv = b.dv;
+    a.dla = b.dlog_alpha;
+    a.dbeta = b.dbeta;
+    a.dS0 = b.dS0;
+    hipStream_t st = static_cast<hipStream_t>(b.stream);
+    if (b.bf16) {
+        switch (b.d_k) {
+            case 32: return launch_bwd_dk<true, 32>(a, b.T_tot, st);
+            case 64: return launch_bwd_dk<true, 64>(a, b.T_tot, st);
+            case 128: return launch_bwd_dk<true, 128>(a, b.T_tot, st);
+        }
+    } else {
+        switch (b.d_k) {
+            case 32: return launch_bwd_dk<false, 32>(a, b.T_tot, st);
+            case 64: return launch_bwd_dk<false, 64>(a, b.T_tot, st);
+            case 128: return launch_bwd_dk<false, 128>(a, b.T_tot, st);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

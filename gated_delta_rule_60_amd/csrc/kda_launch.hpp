@@ -67,6 +67,25 @@ struct DecodeArgs {
     bool scalar_gate = false;  // log_alpha is [N, H] (one gate per sequence and head)
 };
 
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    const float* S0;    // may be null (zero initial state)
+    const int32_t* cu_seqlens;
+    const void* dO;     // [T_tot, H, d_v], storage type of q/k/v
+    const float* dS_T;  // may be null (no gradient reaches the final states)
+    int32_t N;
+    int64_t T_tot;
+    int32_t H, d_k, d_v;
+    bool bf16;
+    float *dq, *dk, *dv, *dlog_alpha, *dbeta, *dS0;
+    void* workspace;  // at least prefill_bwd_workspace_bytes(...) bytes, 256-byte aligned
+    void* stream;
+};
+
 hipError_t launch_prefill(const PrefillArgs& a);
 
 // Whether a prefill of these sizes runs segmented, and the workspace bytes it
@@ -78,6 +97,10 @@ size_t prefill_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
 hipError_t launch_seg_plan(const PrefillArgs& a, SegView* view);
 hipError_t launch_seg_fixup(const PrefillArgs& a, const SegView& v);
 hipError_t launch_decode(const DecodeArgs& a);
+// Backward pass of the prefill (kda_backward.hip) and the workspace it needs:
+// fp32 state checkpoints every 16 tokens and one residual row per token-head.
+hipError_t launch_prefill_bwd(const BackwardArgs& a);
+size_t prefill_bwd_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v);
 
 // Launch shape kda_prefill picks for these sizes (see kda_prefill.hip).
 int32_t default_v_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16);

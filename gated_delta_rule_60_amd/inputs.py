@@ -28,6 +28,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
+    "make_backward_grads",
     "PrefillInputs",
     "DecodeStepInputs",
     "WORKLOADS",
@@ -205,3 +206,18 @@ def make_workload(name: str) -> PrefillInputs:
         lengths = varlen_lengths(rng, lengths[1], lengths[2], lengths[3])
     return make_prefill_inputs(lengths, w["H"], w["d_k"], w["d_v"], w["dtype"], None,
                                w["log_alpha_range"], w["s0_std"], rng=rng)
+
+
+def make_backward_grads(x: PrefillInputs, seed, with_dS_T: bool = True):
+    """Upstream gradients for a backward pass over the batch ``x``: dL/do
+    [T_tot, H, d_v] (N(0,1), rounded to x's storage dtype) and dL/dS_T
+    [N, H, d_k, d_v] (N(0,1) fp32, or None)."""
+    rng = np.random.default_rng(seed)
+    T, H = int(x.q.shape[0]), int(x.q.shape[1])
+    d_k, d_v = int(x.q.shape[2]), int(x.v.shape[2])
+    N = int(x.cu_seqlens.shape[0] - 1)
+    dO = rng.standard_normal((T, H, d_v), dtype=np.float32)
+    if x.dtype == "bf16":
+        round_to_bf16(dO, out=dO)
+    dST = rng.standard_normal((N, H, d_k, d_v), dtype=np.float32) if with_dS_T else None
+    return dO, dST

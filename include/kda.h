@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 2
+#define KDA_VERSION 3
 
 typedef enum {
     KDA_OK = 0,
@@ -220,6 +220,49 @@ kda_status gdn_decode_step(const void* q, const void* k, const void* v,
                            const float* log_alpha, const float* beta, float* S, int32_t N,
                            int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
                            void* stream);
+
+/*
+ * kda_prefill_backward -- gradients of a scalar loss L through kda_prefill:
+ * given dL/do for every token and dL/dS_T for every final state, it returns
+ * dL/d of q, k, v, log_alpha, beta and the initial state.  It is the
+ * reverse-mode derivative of the recurrence of "Kimi Linear：让长上下文大模型
+ * 真正实用的线性注意力架构" (juejin.cn), section 三.5, per channel (section 三.1),
+ * with the read-out o_t = S_t^T q_t after the update.  The training side of
+ * the page's reading of the layer as online learning needs it.
+ *
+ * Inputs are those of kda_prefill (same layouts, dtype, alignment and
+ * numerical contract):
+ *   q, k, v, log_alpha, beta, S0 (NULL: zero), cu_seqlens, N, T_tot, H, d_k,
+ *   d_v, dtype
+ *   d_o        device [T_tot, H, d_v]     dtype     dL/do
+ *   d_S_T      device [N, H, d_k, d_v]    float32   dL/dS_T; NULL: zero
+ * Outputs, all float32, written in full (overwritten, not accumulated):
+ *   d_q, d_k   device [T_tot, H, d_k]
+ *   d_v        device [T_tot, H, d_v]
+ *   d_log_alpha device [T_tot, H, d_k]
+ *   d_beta     device [T_tot, H]           4-byte aligned
+ *   d_S0       device [N, H, d_k, d_v]     also when S0 is NULL
+ *   workspace  device, at least kda_prefill_backward_workspace_size(...)
+ *              bytes, 256-byte aligned, owned by the caller; its contents on
+ *              entry do not matter and are clobbered.
+ * Outputs must not alias inputs or one another.  Errors as for kda_prefill
+ * (validation before any HIP call).  Asynchronous on `stream`.  Results are
+ * identical from run to run.
+ */
+kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
+                                const float* log_alpha, const float* beta, const float* S0,
+                                const int32_t* cu_seqlens, int32_t N, int64_t T_tot, int32_t H,
+                                int32_t d_k, int32_t d_v, kda_dtype dtype, const void* d_o,
+                                const float* d_S_T, float* d_q, float* d_k_out, float* d_v_out,
+                                float* d_log_alpha, float* d_beta, float* d_S0, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kda_prefill_backward needs: fp32 states at the start of
+ * every 16-token block of every sequence (at most T_tot / 16 + N + 1 blocks
+ * per head) and one fp32 row of d_v per token and head.  0 for unsupported
+ * sizes. */
+size_t kda_prefill_backward_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
+                                           int32_t d_v, kda_dtype dtype);
 
 /* Static text for a status code. */
 const char* kda_status_string(kda_status status);

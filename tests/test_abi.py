@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.kda_version() == 2
+    assert kda.kda_version() == 3
     for s in (0, 1, 2, 3):
         assert kda.kda_status_string(s).startswith("KDA_")
     assert "unknown" in kda.kda_status_string(99)
@@ -159,3 +159,40 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_HERE", str(tmp_path))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def _backward(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, log_alpha=FAKE, beta=FAKE, S0=None, cu_seqlens=FAKE, N=1,
+             T_tot=64, H=2, d_k=64, d_v=64, dtype=BF16, d_o=FAKE, d_S_T=None, d_q=FAKE, d_k_out=FAKE,
+             d_v_out=FAKE, d_log_alpha=FAKE, d_beta=FAKE, d_S0=FAKE, workspace=0x100000,
+             workspace_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return kda.kda_prefill_backward(**a)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(N=0), kda.KDA_ERR_INVALID_ARG, "N >= 1"),
+    (dict(T_tot=-1), kda.KDA_ERR_INVALID_ARG, "T_tot"),
+    (dict(d_k=48), kda.KDA_ERR_UNSUPPORTED, "d_k and d_v"),
+    (dict(dtype=5), kda.KDA_ERR_UNSUPPORTED, "dtype"),
+    (dict(d_S0=None), kda.KDA_ERR_INVALID_ARG, "d_S0"),
+    (dict(d_o=None), kda.KDA_ERR_INVALID_ARG, "d_o"),
+    (dict(d_beta=None), kda.KDA_ERR_INVALID_ARG, "gradient"),
+    (dict(d_q=FAKE + 4), kda.KDA_ERR_INVALID_ARG, "16-byte aligned"),
+    (dict(d_beta=FAKE + 2), kda.KDA_ERR_INVALID_ARG, "4-byte aligned"),
+    (dict(workspace_bytes=16), kda.KDA_ERR_INVALID_ARG, "workspace smaller"),
+    (dict(workspace=None), kda.KDA_ERR_INVALID_ARG, "workspace must not be NULL"),
+    (dict(workspace=0x100010), kda.KDA_ERR_INVALID_ARG, "256-byte aligned"),
+])
+def test_backward_validation(kw, status, needle):
+    assert _backward(**kw) == status
+    assert needle in kda.kda_last_error()
+
+
+def test_backward_workspace_size():
+    # fp32 checkpoints for T/16 + N + 1 blocks per head (256-byte rounded) plus one fp32 row per token-head
+    n, t, h, dk, dv = 3, 1000, 4, 64, 32
+    ck = (t // 16 + n + 1) * h * dk * dv * 4
+    assert kda.kda_prefill_backward_workspace_size(n, t, h, dk, dv, BF16) == (ck + 255) // 256 * 256 + t * h * dv * 4
+    assert kda.kda_prefill_backward_workspace_size(0, t, h, dk, dv, BF16) == 0
+    assert kda.kda_prefill_backward_workspace_size(n, t, h, 48, dv, BF16) == 0
