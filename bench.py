@@ -12,6 +12,8 @@ Prints ONE JSON line.  ``value`` is prefill tokens/s; ``roofline`` is the
 prefill kernel against HBM bandwidth (algorithmic bytes / measured kernel
 time); ``decode`` holds the decode step's microseconds and its own roofline;
 ``gdn`` the same prefill with one gate per token and head (Gated DeltaNet);
+``backward`` the backward pass (kda_prefill_backward) over the same batch
+against the fp32 vector ALU peak;
 ``cpu_baseline`` is the fp64 oracle on a bounded sample of the same
 workload, timed on this host's cores.
 """
@@ -29,6 +31,7 @@ sys.path.insert(0, _ROOT)
 METRIC = "KDA prefill tokens/s (T=32k,H=32,d=128) + decode step µs; % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (published; counts packed fp32 FMA)
 # chunk length of the prefill kernel for bf16 inputs at d_k = 128 (32 tokens;
 # 16 where a 32-token chunk's LDS tiles exceed the 160 KB of one CU)
 CHUNK = 32
@@ -54,6 +57,22 @@ def prefill_flops(T_tot: int, H: int, dk: int, dv: int, C: int = CHUNK) -> int:
 def decode_bytes(N: int, H: int, dk: int, dv: int, esize: int) -> int:
     """State read + write (fp32) plus q, k, v, log_alpha, beta, o per (sequence, head)."""
     return (8 * dk * dv + esize * (2 * dk + dv) + 4 * dk + 4 + esize * dv) * N * H
+
+
+def backward_flops(T_tot: int, H: int, dk: int, dv: int) -> int:
+    """fp32 flops of the reverse-mode token recurrence per state element and
+    token (an FMA counts 2), without recomputation: the forward states
+    (decay 1, prediction 2, update 2) and the reverse step (dq 2, G += q do^T 2,
+    de 2, dk 4, dS' 2, dlog_alpha 2, G <- Diag(a) dS' 1)."""
+    return 20 * dk * dv * T_tot * H
+
+
+def backward_bytes(T_tot: int, N: int, H: int, dk: int, dv: int, esize: int) -> int:
+    """Algorithmic HBM bytes of one backward: read q, k, v, do (esize),
+    log_alpha and beta (fp32); write dq, dk, dv, dlog_alpha, dbeta (fp32) per
+    token-head; read S0 and dS_T, write dS0 (fp32) per (sequence, head)."""
+    per_token_head = esize * (2 * dk + 2 * dv) + 4 * dk + 4 + 4 * (3 * dk + dv) + 4
+    return per_token_head * T_tot * H + 3 * 4 * dk * dv * N * H
 
 
 _CSRC = os.path.join(_ROOT, "gated_delta_rule_60_amd", "csrc")
@@ -161,6 +180,32 @@ def bench_prefill(kda, torch, x, steps: int, warmup: int, v_split: int, scalar_g
     return wall, kernel_ms
 
 
+def bench_backward(kda, torch, x, steps: int, warmup: int):
+    """Event-timed kda_prefill_backward launches over the workload, with
+    seeded upstream gradients dL/do and dL/dS_T; one workspace reused."""
+    from gated_delta_rule_60_amd import inputs
+
+    dev = torch.device("cuda:0")
+    td = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    up = lambda a, dt=torch.float32: torch.from_numpy(a).to(dev).to(dt)
+    dO, dST = inputs.make_backward_grads(x, seed=12)
+    args = (up(x.q, td), up(x.k, td), up(x.v, td), up(x.log_alpha), up(x.beta),
+            None if x.S0 is None else up(x.S0), torch.from_numpy(x.cu_seqlens).to(dev), up(dO, td), up(dST))
+    ws = kda.kda_prefill_backward_workspace_size(x.N, x.T_tot, x.H, x.d_k, x.d_v, 0 if x.dtype == "bf16" else 1)
+    wbuf = torch.empty(ws, dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        kda.prefill_backward(*args, workspace=wbuf)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        kda.prefill_backward(*args, workspace=wbuf)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev], ws
+
+
 def bench_decode(kda, torch, steps: int, warmup: int, n_inputs: int):
     from gated_delta_rule_60_amd import inputs
 
@@ -231,6 +276,8 @@ def main():
                     help="distinct pre-generated decode-step inputs, cycled")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gdn", action="store_true", help="skip the scalar-gate (Gated DeltaNet) prefill line")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass line")
+    ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", type=float, default=0.0,
@@ -316,6 +363,21 @@ def main():
                          "unit": "GB/s", "frac": gb / (g_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "traffic": measured_traffic("prefill_kernel", gwl, ["kda_prefill.hip", "kda_device.hpp"]),
                          "kernel": "kda::prefill_kernel (scalar gate)", "alg_bytes_per_launch": gb},
+        }
+    if not args.no_backward:
+        bms, bws = bench_backward(kda, torch, x, args.backward_steps, 1)
+        b_avg = sum(bms) / len(bms)
+        bfl = backward_flops(x.T_tot, x.H, x.d_k, x.d_v)
+        bby = backward_bytes(x.T_tot, x.N, x.H, x.d_k, x.d_v, esize)
+        out["backward"] = {
+            "workload": args.workload, "what": "kda_prefill_backward: dq, dk, dv, dlog_alpha, dbeta, dS0",
+            "tokens_per_s": x.T_tot / (b_avg * 1e-3), "ms_avg": b_avg, "ms_min": min(bms), "launches": len(bms),
+            "workspace_bytes": bws,
+            "roofline": {"bound": "alu", "achieved": bfl / (b_avg * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": bfl / (b_avg * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
+                         "traffic": None, "kernel": "kda::bwd_forward_kernel + kda::bwd_kernel (one call)",
+                         "alg_flops_per_launch": bfl, "alg_bytes_per_launch": bby,
+                         "hbm_frac": bby / (b_avg * 1e-3) / 1e9 / HBM_PEAK_GBS},
         }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)

@@ -65,13 +65,31 @@ __device__ __forceinline__ float ld(const typename Elem<BF16>::G* p) {
     }
 }
 
+// DPP lane permutations inside a row of 16 lanes, each an xor pairing:
+// row_mirror (lane i <- 15 - i: xor 15), row_half_mirror (xor 7), and
+// quad_perm [1,0,3,2] (xor 1) and [2,3,0,1] (xor 2).
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141, kDppXor1 = 0xB1, kDppXor2 = 0x4E;
+
+// value of v in lane src (wave-uniform result)
+__device__ __forceinline__ float read_lane(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 // Sum over the rows of each of the lane's columns (the wave holds every row
-// of its 8 columns), returned in every lane: a butterfly that halves the
-// values a lane carries at each exchange, then a gather of the 8 (or 4)
-// column totals.
+// of its 8 columns), returned in every lane.  A butterfly halves the values a
+// lane carries at each exchange (partners l ^ 32 and l ^ 16 across rows of
+// lanes, then l ^ 15 inside a row), the three remaining exchanges (xor 1, 2
+// and 7) finish each column's total, and the totals are broadcast to every
+// lane through scalar registers.
 template <int DK>
 __device__ __forceinline__ void column_sums(const float (&p)[BwdLanes<DK>::CPL], float (&out)[BwdLanes<DK>::CPL],
                                             int lane) {
+    float s;
     if constexpr (DK >= 64) {
         const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
         float h4[4], h2[2];
@@ -85,13 +103,7 @@ __device__ __forceinline__ void column_sums(const float (&p)[BwdLanes<DK>::CPL],
             const float send = b4 ? h4[i] : h4[i + 2];
             h2[i] = (b4 ? h4[i + 2] : h4[i]) + __shfl_xor(send, 16);
         }
-        float s = (b3 ? h2[1] : h2[0]) + __shfl_xor(b3 ? h2[0] : h2[1], 8);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 1);
-        // lane l now holds the total of column 4 b5 + 2 b4 + b3
-#pragma unroll
-        for (int c = 0; c < 8; ++c) out[c] = __shfl(s, (c << 3) | (lane & 7));
+        s = (b3 ? h2[1] : h2[0]) + dpp<kDppRowMirror>(b3 ? h2[0] : h2[1]);
     } else {
         const bool b4 = lane & 16, b3 = lane & 8;
         float h2[2];
@@ -100,15 +112,28 @@ __device__ __forceinline__ void column_sums(const float (&p)[BwdLanes<DK>::CPL],
             const float send = b4 ? p[i] : p[i + 2];
             h2[i] = (b4 ? p[i + 2] : p[i]) + __shfl_xor(send, 16);
         }
-        float s = (b3 ? h2[1] : h2[0]) + __shfl_xor(b3 ? h2[0] : h2[1], 8);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 1);
-        // lane l holds the total of column 2 b4 + b3 of its half (lane & 32)
+        s = (b3 ? h2[1] : h2[0]) + dpp<kDppRowMirror>(b3 ? h2[0] : h2[1]);
+    }
+    s += dpp<kDppXor1>(s);
+    s += dpp<kDppXor2>(s);
+    s += dpp<kDppRowHalfMirror>(s);
+    // lane l holds the total of column 4 b5 + 2 b4 + b3 (d_k = 32: 2 b4 + b3 of
+    // its half); the totals are read out of lanes 8 c into scalar registers
+    if constexpr (DK >= 64) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) out[c] = __shfl(s, (lane & 32) | (c << 3) | (lane & 7));
+        for (int c = 0; c < 8; ++c) out[c] = read_lane(s, c << 3);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float lo = read_lane(s, c << 3), hi = read_lane(s, 32 | (c << 3));
+            out[c] = (lane & 32) ? hi : lo;
+        }
     }
 }
+
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// accesses, not for its outstanding global stores.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 struct BwdArgs {
     const void *q, *k, *v, *dO;
@@ -149,78 +174,125 @@ __global__ void __launch_bounds__(64 * NW) bwd_forward_kernel(BwdArgs a) {
             S[rr][c] = a.S0 ? a.S0[((static_cast<int64_t>(n) * H + h) * DK + L::row(lane, rr)) * DV + c0 + c] : 0.f;
 
     const G* gk = static_cast<const G*>(a.k);
-    const G* v = static_cast<const G*>(a.v);
-    for (int64_t t = t0; t < t1; ++t) {
-        if ((t - t0) % kBwdBlock == 0) {
-            float* ck = a.ckpt + (ckpt_slot(a.cu, n, static_cast<int>((t - t0) / kBwdBlock)) * H + h) * DK * DV;
+    const G* gv = static_cast<const G*>(a.v);
+    // Tokens run in groups of 4; the inputs of the next group are
+    // loaded while the current group is computed.
+    constexpr int GT = 4;
+    float cla[GT][R], ckk[GT][R], cvv[GT][CPL], cb[GT];
+    float nla[GT][R], nkk[GT][R], nvv[GT][CPL], nb[GT];
+    auto fetch = [&](int64_t g0) __attribute__((always_inline)) {
 #pragma unroll
-            for (int rr = 0; rr < R; ++rr)
+        for (int j = 0; j < GT; ++j) {
+            if (g0 + j < t1) {
+                const int64_t t = g0 + j, tk = (t * H + h) * DK, tv = (t * H + h) * DV;
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) ck[static_cast<int64_t>(L::row(lane, rr)) * DV + c0 + c] = S[rr][c];
+                for (int rr = 0; rr < R; ++rr) {
+                    nla[j][rr] = a.la[tk + L::row(lane, rr)];
+                    nkk[j][rr] = ld<BF16>(gk + tk + L::row(lane, rr));
+                }
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) nvv[j][c] = ld<BF16>(gv + tv + c0 + c);
+                nb[j] = a.beta[t * H + h];
+            }
         }
-        const int64_t tk = (t * H + h) * DK, tv = (t * H + h) * DV;
-        float al[R], kk[R], up[CPL], u[CPL];
+    };
+    if (t0 < t1) fetch(t0);
+    for (int64_t g0 = t0; g0 < t1; g0 += GT) {
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-            al[rr] = exp_e(a.la[tk + L::row(lane, rr)]);
-            kk[rr] = ld<BF16>(gk + tk + L::row(lane, rr));
-        }
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            float acc = 0.f;
+        for (int j = 0; j < GT; ++j) {
 #pragma unroll
             for (int rr = 0; rr < R; ++rr) {
-                S[rr][c] *= al[rr];
-                acc = __builtin_fmaf(kk[rr], S[rr][c], acc);
+                cla[j][rr] = nla[j][rr];
+                ckk[j][rr] = nkk[j][rr];
             }
-            up[c] = acc;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) cvv[j][c] = nvv[j][c];
+            cb[j] = nb[j];
         }
-        column_sums<DK>(up, u, lane);
-        const float bt = a.beta[t * H + h];
-        float wv_[CPL];
+        if (g0 + GT < t1) fetch(g0 + GT);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            wv_[c] = ld<BF16>(v + tv + c0 + c) - u[c];
-            const float e = bt * wv_[c];
+        for (int j = 0; j < GT; ++j) {
+            const int64_t t = g0 + j;
+            if (t >= t1) break;
+            if ((t - t0) % kBwdBlock == 0) {
+                float* ck = a.ckpt + (ckpt_slot(a.cu, n, static_cast<int>((t - t0) / kBwdBlock)) * H + h) * DK * DV;
 #pragma unroll
-            for (int rr = 0; rr < R; ++rr) S[rr][c] = __builtin_fmaf(kk[rr], e, S[rr][c]);
-        }
-        if ((lane & 31) == 0 && (DK == 32 || lane == 0)) {
+                for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) a.w[tv + c0 + c] = wv_[c];
+                    for (int c = 0; c < CPL; ++c) ck[static_cast<int64_t>(L::row(lane, rr)) * DV + c0 + c] = S[rr][c];
+            }
+            float up[CPL], u[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                float acc = 0.f;
+#pragma unroll
+                for (int rr = 0; rr < R; ++rr) {
+                    S[rr][c] *= exp_e(cla[j][rr]);
+                    acc = __builtin_fmaf(ckk[j][rr], S[rr][c], acc);
+                }
+                up[c] = acc;
+            }
+            column_sums<DK>(up, u, lane);
+            float wv_[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                wv_[c] = cvv[j][c] - u[c];
+                const float e = cb[j] * wv_[c];
+#pragma unroll
+                for (int rr = 0; rr < R; ++rr) S[rr][c] = __builtin_fmaf(ckk[j][rr], e, S[rr][c]);
+            }
+            if ((lane & 31) == 0 && (DK == 32 || lane == 0)) {
+                const int64_t tv = (t * H + h) * DV;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) a.w[tv + c0 + c] = wv_[c];
+            }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2: reverse walk.  Same grid and column ownership as pass 1.
-// SLICED: more than one workgroup per (sequence, head) (two at d_v = 128);
-// their row sums meet by atomic addition in outputs zeroed beforehand.  With
-// exactly two addends on zero the result does not depend on their order.
+// Pass 2: reverse walk.  Grid: N * H * SL workgroups of NW waves; wave wv
+// of slice s owns columns (s NW + wv) 8 .. + 7, as in pass 1.
+// With SL = 2 slices (d_v = 128) the two workgroups of one (sequence, head)
+// meet in their row sums (dq, dk, dlog_alpha, dbeta) by atomic addition
+// into outputs zeroed beforehand: with exactly two addends on zero the
+// result does not depend on their order.
 // ---------------------------------------------------------------------------
 template <bool BF16, int DK, int NW>
 struct BwdStage {
-    // [quantity dq, dk, dlog_alpha][token of the half][wave][row], then dbeta [token][wave]
+    static constexpr int BV = kBwdCols * NW;  // value columns of the workgroup
+    // row sums: [quantity dq, dk, dlog_alpha][token of the half][wave][row], then dbeta [token][wave]
     static constexpr int kRowFloats = 3 * kBwdHalf * NW * DK;
-    static constexpr int kFloats = kRowFloats + kBwdHalf * NW;
+    static constexpr int kBetaFloats = kBwdHalf * NW;
+    // inputs of one block, fp32: alpha = exp(log_alpha), k, q [token][row]; w, do [token][column]; beta
+    static constexpr int kInFloats = 3 * kBwdBlock * DK + 2 * kBwdBlock * BV + kBwdBlock;
+    static constexpr int kFloats = kRowFloats + kBetaFloats + kInFloats;
 };
 
-template <bool BF16, int DK, int NW, bool SLICED>
+template <bool BF16, int DK, int NW, int SL>
 __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
     using L = BwdLanes<DK>;
     using G = typename Elem<BF16>::G;
     using St = BwdStage<BF16, DK, NW>;
     constexpr int R = L::R, CPL = L::CPL;
+    constexpr int BV = St::BV;
     __shared__ float stage[St::kFloats];
     float* sRow = stage;
-    float* sBeta = stage + St::kRowFloats;
+    float* sBeta = sRow + St::kRowFloats;
+    float* sA = sBeta + St::kBetaFloats;
+    float* sK = sA + kBwdBlock * DK;
+    float* sQ = sK + kBwdBlock * DK;
+    float* sW = sQ + kBwdBlock * DK;
+    float* sDO = sW + kBwdBlock * BV;
+    float* sB = sDO + kBwdBlock * BV;
 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int slices = a.DV / (kBwdCols * NW);
-    const int s = blockIdx.x % slices, pair = blockIdx.x / slices;
+    static_assert(SL == 1 || SL == 2, "one or two slices");
+    const int s = blockIdx.x % SL, pair = blockIdx.x / SL;
     const int n = pair / a.H, h = pair % a.H;
     const int H = a.H, DV = a.DV;
     const int c0 = (s * NW + wv) * kBwdCols + L::col(lane);
+    const int cs = c0 - s * BV;  // the lane's first column inside the workgroup's slice
     const int64_t t0 = a.cu[n], t1 = a.cu[n + 1];
     const int nblk = static_cast<int>((t1 - t0 + kBwdBlock - 1) / kBwdBlock);
     const G* gq = static_cast<const G*>(a.q);
@@ -235,19 +307,18 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
         for (int c = 0; c < CPL; ++c)
             Gr[rr][c] = a.dST ? a.dST[sbase + static_cast<int64_t>(L::row(lane, rr)) * DV + c0 + c] : 0.f;
 
-    // one forward step of token t without a column sum (w is stored)
-    auto step = [&](float (&S)[R][CPL], int64_t t) __attribute__((always_inline)) {
-        const int64_t tk = (t * H + h) * DK, tv = (t * H + h) * DV;
-        const float bt = a.beta[t * H + h];
+    // one forward step of row r of the staged block without a column sum (w is stored)
+    auto step = [&](float (&S)[R][CPL], int r) __attribute__((always_inline)) {
+        const float bt = sB[r];
         float al[R], kk[R];
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
-            al[rr] = exp_e(a.la[tk + L::row(lane, rr)]);
-            kk[rr] = ld<BF16>(gk + tk + L::row(lane, rr));
+            al[rr] = sA[r * DK + L::row(lane, rr)];
+            kk[rr] = sK[r * DK + L::row(lane, rr)];
         }
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            const float e = bt * a.w[tv + c0 + c];
+            const float e = bt * sW[r * BV + cs + c];
 #pragma unroll
             for (int rr = 0; rr < R; ++rr) S[rr][c] = __builtin_fmaf(kk[rr], e, al[rr] * S[rr][c]);
         }
@@ -257,6 +328,22 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
         const int64_t tb = t0 + static_cast<int64_t>(b) * kBwdBlock;
         const int64_t te = tb + kBwdBlock < t1 ? tb + kBwdBlock : t1;
         const float* ck = a.ckpt + (ckpt_slot(a.cu, n, b) * H + h) * DK * DV;
+        // stage the block's inputs (every reader of the previous block has
+        // passed the barrier that ends its last half)
+        const int ntok = static_cast<int>(te - tb);
+        for (int i = threadIdx.x; i < ntok * DK; i += 64 * NW) {
+            const int64_t tk = ((tb + i / DK) * H + h) * DK + i % DK;
+            sA[i] = exp_e(a.la[tk]);
+            sK[i] = ld<BF16>(gk + tk);
+            sQ[i] = ld<BF16>(gq + tk);
+        }
+        for (int i = threadIdx.x; i < ntok * BV; i += 64 * NW) {
+            const int64_t tv = ((tb + i / BV) * H + h) * DV + s * BV + i % BV;
+            sW[i] = a.w[tv];
+            sDO[i] = ld<BF16>(gdo + tv);
+        }
+        if (threadIdx.x < ntok) sB[threadIdx.x] = a.beta[(tb + threadIdx.x) * H + h];
+        lds_barrier();
         for (int half = 1; half >= 0; --half) {
             const int64_t th = tb + half * kBwdHalf;
             if (th >= te) continue;  // uniform over the workgroup
@@ -265,7 +352,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
             for (int rr = 0; rr < R; ++rr)
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) S[rr][c] = ck[static_cast<int64_t>(L::row(lane, rr)) * DV + c0 + c];
-            for (int64_t t = tb; t < th; ++t) step(S, t);
+            for (int r = 0; r < half * kBwdHalf; ++r) step(S, r);
             float Sp[kBwdHalf][R][CPL];
 #pragma unroll
             for (int r = 0; r < kBwdHalf; ++r) {
@@ -273,30 +360,31 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
                 for (int rr = 0; rr < R; ++rr)
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) Sp[r][rr][c] = S[rr][c];
-                if (th + r < te) step(S, th + r);
+                if (th + r < te) step(S, half * kBwdHalf + r);
             }
 #pragma unroll
             for (int r = kBwdHalf - 1; r >= 0; --r) {
                 const int64_t t = th + r;
                 if (t >= te) continue;
-                const int64_t tk = (t * H + h) * DK, tv = (t * H + h) * DV;
-                const float bt = a.beta[t * H + h];
+                const int64_t tv = (t * H + h) * DV;
+                const int rb = half * kBwdHalf + r;  // row of the staged block
+                const float bt = sB[rb];
                 float al[R], kk[R], qq[R], dqp[R], dkp[R], dap[R];
                 float wv_[CPL], dov[CPL], dep[CPL], de[CPL];
 #pragma unroll
                 for (int rr = 0; rr < R; ++rr) {
                     const int row = L::row(lane, rr);
-                    al[rr] = exp_e(a.la[tk + row]);
-                    kk[rr] = ld<BF16>(gk + tk + row);
-                    qq[rr] = ld<BF16>(gq + tk + row);
+                    al[rr] = sA[rb * DK + row];
+                    kk[rr] = sK[rb * DK + row];
+                    qq[rr] = sQ[rb * DK + row];
                     dqp[rr] = 0.f;
                     dkp[rr] = 0.f;
                     dap[rr] = 0.f;
                 }
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
-                    wv_[c] = a.w[tv + c0 + c];
-                    dov[c] = ld<BF16>(gdo + tv + c0 + c);
+                    wv_[c] = sW[rb * BV + cs + c];
+                    dov[c] = sDO[rb * BV + cs + c];
                     dep[c] = 0.f;
                 }
                 // read-out and the rank-1 correction: dq = S_t do, G += q do^T, de = G^T k
@@ -353,7 +441,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
                 }
                 if (lane == 0) sBeta[r * NW + wv] = dbp;
             }
-            __syncthreads();
+            lds_barrier();
             // sums over the waves, one output element per thread and item
             for (int it = threadIdx.x; it < 3 * kBwdHalf * DK + kBwdHalf; it += 64 * NW) {
                 if (it < 3 * kBwdHalf * DK) {
@@ -364,7 +452,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
                         for (int w2 = 0; w2 < NW; ++w2) acc += sRow[((qn * kBwdHalf + r) * NW + w2) * DK + row];
                         float* out = qn == 0 ? a.dq : (qn == 1 ? a.dk : a.dla);
                         float* dst = out + (t * H + h) * DK + row;
-                        if constexpr (SLICED) {
+                        if constexpr (SL > 1) {
                             atomicAdd(dst, acc);
                         } else {
                             *dst = acc;
@@ -377,7 +465,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
                         float acc = 0.f;
                         for (int w2 = 0; w2 < NW; ++w2) acc += sBeta[r * NW + w2];
                         float* dst = a.dbeta + t * H + h;
-                        if constexpr (SLICED) {
+                        if constexpr (SL > 1) {
                             atomicAdd(dst, acc);
                         } else {
                             *dst = acc;
@@ -385,7 +473,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
 #pragma unroll
@@ -400,8 +488,14 @@ __global__ void __launch_bounds__(256) bwd_zero_kernel(float* __restrict__ p, in
         p[i] = 0.f;
 }
 
-// waves per workgroup: 8 columns each, at most 64 columns per workgroup
-inline int bwd_waves(int d_v) { return d_v >= 64 ? 8 : d_v / kBwdCols; }
+// waves per workgroup (8 columns each): 8, or 4 at d_v = 32; a workgroup
+// covers at most 64 columns, so d_v = 128 runs two slices per (sequence, head)
+inline int bwd_waves(int d_v) { return d_v >= 64 ? 8 : 4; }
+
+inline unsigned grid_1d(int64_t count) {
+    const int64_t blocks = (count + 255) / 256;
+    return static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
+}
 
 template <bool BF16, int DK, int NW>
 hipError_t launch_bwd_nw(const BwdArgs& a, int64_t T_tot, hipStream_t st) {
@@ -411,20 +505,19 @@ hipError_t launch_bwd_nw(const BwdArgs& a, int64_t T_tot, hipStream_t st) {
     hipLaunchKernelGGL((bwd_forward_kernel<BF16, DK, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (slices > 1) {
+    if (slices == 2) {
         // zero the outputs the slices add into: dq, dk, dlog_alpha [T_tot, H, d_k], dbeta [T_tot, H]
         const int64_t rowN = T_tot * a.H * DK;
         float* bufs[4] = {a.dq, a.dk, a.dla, a.dbeta};
         const int64_t counts[4] = {rowN, rowN, rowN, T_tot * a.H};
-        for (int i = 0; i < 4; ++i) {
-            if (counts[i] == 0) continue;
-            const int64_t blocks = (counts[i] + 255) / 256;
-            hipLaunchKernelGGL(bwd_zero_kernel, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)), dim3(256),
-                               0, st, bufs[i], counts[i]);
-        }
-        hipLaunchKernelGGL((bwd_kernel<BF16, DK, NW, true>), dim3(grid), dim3(64 * NW), 0, st, a);
+        for (int i = 0; i < 4; ++i)
+            if (counts[i] > 0)
+                hipLaunchKernelGGL(bwd_zero_kernel, dim3(grid_1d(counts[i])), dim3(256), 0, st, bufs[i], counts[i]);
+        hipLaunchKernelGGL((bwd_kernel<BF16, DK, NW, 2>), dim3(grid), dim3(64 * NW), 0, st, a);
+    } else if (slices == 1) {
+        hipLaunchKernelGGL((bwd_kernel<BF16, DK, NW, 1>), dim3(grid), dim3(64 * NW), 0, st, a);
     } else {
-        hipLaunchKernelGGL((bwd_kernel<BF16, DK, NW, false>), dim3(grid), dim3(64 * NW), 0, st, a);
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
@@ -438,13 +531,18 @@ hipError_t launch_bwd_dk(const BwdArgs& a, int64_t T_tot, hipStream_t st) {
     }
 }
 
+inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// workspace: checkpoints | w
+inline size_t bwd_ckpt_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v) {
+    const int64_t slots = T_tot / kBwdBlock + N + 1;
+    return round256(static_cast<size_t>(slots) * H * d_k * d_v * sizeof(float));
+}
+
 }  // namespace
 
 size_t prefill_bwd_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v) {
-    const int64_t slots = T_tot / kBwdBlock + N + 1;
-    const size_t ck = static_cast<size_t>(slots) * H * d_k * d_v * sizeof(float);
-    const size_t w = static_cast<size_t>(T_tot) * H * d_v * sizeof(float);
-    return ((ck + 255) / 256) * 256 + w;
+    return bwd_ckpt_bytes(N, T_tot, H, d_k, d_v) + static_cast<size_t>(T_tot) * H * d_v * sizeof(float);
 }
 
 hipError_t launch_prefill_bwd(const BackwardArgs& b) {
@@ -461,10 +559,9 @@ hipError_t launch_prefill_bwd(const BackwardArgs& b) {
     a.N = b.N;
     a.H = b.H;
     a.DV = b.d_v;
-    const int64_t slots = b.T_tot / kBwdBlock + b.N + 1;
-    const size_t ck = static_cast<size_t>(slots) * b.H * b.d_k * b.d_v * sizeof(float);
-    a.ckpt = static_cast<float*>(b.workspace);
-    a.w = reinterpret_cast<float*>(static_cast<unsigned char*>(b.workspace) + ((ck + 255) / 256) * 256);
+    unsigned char* ws = static_cast<unsigned char*>(b.workspace);
+    a.ckpt = reinterpret_cast<float*>(ws);
+    a.w = reinterpret_cast<float*>(ws + bwd_ckpt_bytes(b.N, b.T_tot, b.H, b.d_k, b.d_v));
     a.dq = b.dq;
     a.dk = b.dk;
     a.dv = b.dv;
