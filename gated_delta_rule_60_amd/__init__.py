@@ -23,6 +23,8 @@ from ._lib import (  # noqa: F401
     decode_step,
     gdn_decode_step,
     gdn_decode_step_t,
+    gdn_prefill_backward,
+    gdn_prefill_backward_t,
     gdn_prefill,
     gdn_prefill_split,
     gdn_prefill_t,

@@ -49,6 +49,9 @@ SIGNATURES = {
                                             _i32, ctypes.c_int, _vp, _fp, _fp, _fp, _fp, _fp, _fp, _fp,
                                             _vp, _sz, _vp]),
     "kda_prefill_backward_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int]),
+    "gdn_prefill_backward": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32,
+                                            _i32, ctypes.c_int, _vp, _fp, _fp, _fp, _fp, _fp, _fp, _fp,
+                                            _vp, _sz, _vp]),
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_last_error": (ctypes.c_char_p, []),
     "kda_version": (_i32, []),
@@ -148,6 +151,14 @@ def kda_prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, 
                          d_S_T, d_q, d_k_out, d_v_out, d_log_alpha, d_beta, d_S0, workspace,
                          workspace_bytes, stream) -> int:
     return load().kda_prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
+                                       dtype, d_o, d_S_T, d_q, d_k_out, d_v_out, d_log_alpha, d_beta,
+                                       d_S0, workspace, workspace_bytes, stream)
+
+
+def gdn_prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, d_o,
+                         d_S_T, d_q, d_k_out, d_v_out, d_log_alpha, d_beta, d_S0, workspace,
+                         workspace_bytes, stream) -> int:
+    return load().gdn_prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
                                        dtype, d_o, d_S_T, d_q, d_k_out, d_v_out, d_log_alpha, d_beta,
                                        d_S0, workspace, workspace_bytes, stream)
 
@@ -313,6 +324,17 @@ def prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T=None, 
     d_S0) shaped like q, k, v, log_alpha, beta and the initial state.
     ``workspace``: optional uint8 device tensor of at least
     ``kda_prefill_backward_workspace_size(...)`` bytes (allocated if None)."""
+    return _backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, stream, False)
+
+
+def gdn_prefill_backward_t(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T=None, *, workspace=None,
+                           stream=None):
+    """Backward of ``gdn_prefill_t`` (log_alpha [T, H]); d_log_alpha is [T, H].
+    Arguments and results otherwise as in ``prefill_backward``."""
+    return _backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, stream, True)
+
+
+def _backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, stream, scalar_gate: bool):
     import torch
     if not q.is_cuda:
         raise ValueError("kda prefill backward runs on a GPU device; q is on the CPU")
@@ -326,7 +348,7 @@ def prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T=None, 
     _need(q, "q", (T, H, dk), q.dtype, dev)
     _need(k, "k", (T, H, dk), q.dtype, dev)
     _need(v, "v", (T, H, dv), q.dtype, dev)
-    _need(log_alpha, "log_alpha", (T, H, dk), torch.float32, dev)
+    _need(log_alpha, "log_alpha", (T, H) if scalar_gate else (T, H, dk), torch.float32, dev)
     _need(beta, "beta", (T, H), torch.float32, dev)
     _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
     _need(d_o, "d_o", (T, H, dv), q.dtype, dev)
@@ -336,7 +358,8 @@ def prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T=None, 
         _need(d_S_T, "d_S_T", (N, H, dk, dv), torch.float32, dev)
     f32 = dict(dtype=torch.float32, device=dev)
     gq, gk, gv = torch.empty((T, H, dk), **f32), torch.empty((T, H, dk), **f32), torch.empty((T, H, dv), **f32)
-    gla, gb, gS0 = torch.empty((T, H, dk), **f32), torch.empty((T, H), **f32), torch.empty((N, H, dk, dv), **f32)
+    gla = torch.empty((T, H) if scalar_gate else (T, H, dk), **f32)
+    gb, gS0 = torch.empty((T, H), **f32), torch.empty((N, H, dk, dv), **f32)
     ws = kda_prefill_backward_workspace_size(N, T, H, dk, dv, code)
     if workspace is None:
         workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
@@ -344,8 +367,9 @@ def prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T=None, 
         raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
     ptr = lambda t: t.data_ptr() if t is not None else None
     with torch.cuda.device(dev):
-        _check(kda_prefill_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
-                                    beta.data_ptr(), ptr(S0), cu_seqlens.data_ptr(), N, T, H, dk, dv, code,
+        call = gdn_prefill_backward if scalar_gate else kda_prefill_backward
+        _check(call(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
+                    beta.data_ptr(), ptr(S0), cu_seqlens.data_ptr(), N, T, H, dk, dv, code,
                                     d_o.data_ptr(), ptr(d_S_T), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
                                     gla.data_ptr(), gb.data_ptr(), gS0.data_ptr(), workspace.data_ptr(),
                                     workspace.numel(), _stream_handle(stream, dev)))

@@ -78,12 +78,17 @@ size_t kda_prefill_backward_workspace_size(int32_t N, int64_t T_tot, int32_t H, 
     return kda::prefill_bwd_workspace_bytes(N, T_tot, H, d_k, d_v);
 }
 
-kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const float* log_alpha,
-                                const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
-                                int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
-                                const void* d_o, const float* d_S_T, float* d_q, float* d_k_out,
-                                float* d_v_out, float* d_log_alpha, float* d_beta, float* d_S0,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by both backward entry points; scalar_gate: log_alpha and
+// d_log_alpha are [T_tot, H] (4-byte aligned).
+kda_status backward_impl(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                         const float* S0, const int32_t* cu_seqlens, int32_t N, int64_t T_tot, int32_t H,
+                         int32_t d_k, int32_t d_v, kda_dtype dtype, const void* d_o, const float* d_S_T, float* d_q,
+                         float* d_k_out, float* d_v_out, float* d_log_alpha, float* d_beta, float* d_S0,
+                         void* workspace, size_t workspace_bytes, void* stream, bool scalar_gate) {
     g_last_error.clear();
     if (N < 1 || H < 1 || T_tot < 0)
         return fail(KDA_ERR_INVALID_ARG, "need N >= 1, H >= 1 and T_tot >= 0");
@@ -97,11 +102,15 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
     if (T_tot > INT32_MAX) return fail(KDA_ERR_INVALID_ARG, "T_tot must fit in int32 (cu_seqlens is int32)");
     if (static_cast<int64_t>(N) * H * (d_v / 8) > (int64_t{1} << 22))
         return fail(KDA_ERR_INVALID_ARG, "N * H too large");
-    const void* ptrs[] = {q, k, v, log_alpha, d_o, S0, d_S_T, d_q, d_k_out, d_v_out, d_log_alpha, d_S0};
+    const void* ptrs[] = {q, k, v, scalar_gate ? nullptr : log_alpha, d_o, S0, d_S_T, d_q, d_k_out, d_v_out,
+                          scalar_gate ? nullptr : d_log_alpha, d_S0};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-    if (d_beta && (reinterpret_cast<uintptr_t>(d_beta) & 3u) != 0)
-        return fail(KDA_ERR_INVALID_ARG, "d_beta must be 4-byte aligned");
+    const void* ptrs4[] = {d_beta, scalar_gate ? log_alpha : nullptr, scalar_gate ? d_log_alpha : nullptr};
+    for (const void* p : ptrs4)
+        if (p && (reinterpret_cast<uintptr_t>(p) & 3u) != 0)
+            return fail(KDA_ERR_INVALID_ARG, scalar_gate ? "d_beta, log_alpha and d_log_alpha must be 4-byte aligned"
+                                                         : "d_beta must be 4-byte aligned");
     const size_t ws_need = kda_prefill_backward_workspace_size(N, T_tot, H, d_k, d_v, dtype);
     if (workspace_bytes < ws_need)
         return fail(KDA_ERR_INVALID_ARG, "workspace smaller than kda_prefill_backward_workspace_size");
@@ -110,11 +119,35 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
         return fail(KDA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     kda::BackwardArgs a{q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, N, T_tot, H, d_k, d_v,
                         dtype == KDA_DTYPE_BF16, d_q, d_k_out, d_v_out, d_log_alpha, d_beta, d_S0,
-                        workspace, stream};
+                        workspace, stream, scalar_gate};
     (void)hipGetLastError();  // report only this launch's status
     const hipError_t e = kda::launch_prefill_bwd(a);
     if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const float* log_alpha,
+                                const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
+                                int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                const void* d_o, const float* d_S_T, float* d_q, float* d_k_out,
+                                float* d_v_out, float* d_log_alpha, float* d_beta, float* d_S0,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    return backward_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, d_o, d_S_T, d_q,
+                         d_k_out, d_v_out, d_log_alpha, d_beta, d_S0, workspace, workspace_bytes, stream, false);
+}
+
+kda_status gdn_prefill_backward(const void* q, const void* k, const void* v, const float* log_alpha,
+                                const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
+                                int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                const void* d_o, const float* d_S_T, float* d_q, float* d_k_out,
+                                float* d_v_out, float* d_log_alpha, float* d_beta, float* d_S0,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    return backward_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, d_o, d_S_T, d_q,
+                         d_k_out, d_v_out, d_log_alpha, d_beta, d_S0, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -131,6 +131,18 @@ __device__ __forceinline__ void column_sums(const float (&p)[BwdLanes<DK>::CPL],
     }
 }
 
+// Sum of x over the 64 lanes of the wave, in every lane (partners xor 32, 16,
+// then 15, 1, 2 and 7 inside rows of 16 lanes: together every lane bit).
+__device__ __forceinline__ float wave_sum(float x) {
+    x += __shfl_xor(x, 32);
+    x += __shfl_xor(x, 16);
+    x += dpp<kDppRowMirror>(x);
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    x += dpp<kDppRowHalfMirror>(x);
+    return x;
+}
+
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
 // accesses, not for its outstanding global stores.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -149,11 +161,12 @@ __device__ __forceinline__ int64_t ckpt_slot(const int32_t* cu, int n, int b) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1: forward recurrence; checkpoints and w.  Grid: N * H * slices
+// Pass 1: forward recurrence; checkpoints and w.  SG: one gate per token and
+// head (log_alpha [T_tot, H], Gated DeltaNet), used for every key channel.  Grid: N * H * slices
 // workgroups of NW waves; wave wv of slice s owns columns
 // (s NW + wv) 8 .. + 7.
 // ---------------------------------------------------------------------------
-template <bool BF16, int DK, int NW>
+template <bool BF16, int DK, int NW, bool SG>
 __global__ void __launch_bounds__(64 * NW) bwd_forward_kernel(BwdArgs a) {
     using L = BwdLanes<DK>;
     using G = typename Elem<BF16>::G;
@@ -187,7 +200,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_forward_kernel(BwdArgs a) {
                 const int64_t t = g0 + j, tk = (t * H + h) * DK, tv = (t * H + h) * DV;
 #pragma unroll
                 for (int rr = 0; rr < R; ++rr) {
-                    nla[j][rr] = a.la[tk + L::row(lane, rr)];
+                    nla[j][rr] = SG ? a.la[t * H + h] : a.la[tk + L::row(lane, rr)];
                     nkk[j][rr] = ld<BF16>(gk + tk + L::row(lane, rr));
                 }
 #pragma unroll
@@ -263,13 +276,13 @@ struct BwdStage {
     static constexpr int BV = kBwdCols * NW;  // value columns of the workgroup
     // row sums: [quantity dq, dk, dlog_alpha][token of the half][wave][row], then dbeta [token][wave]
     static constexpr int kRowFloats = 3 * kBwdHalf * NW * DK;
-    static constexpr int kBetaFloats = kBwdHalf * NW;
+    static constexpr int kBetaFloats = kBwdHalf * NW;  // also the per-head gate's [token][wave] sums
     // inputs of one block, fp32: alpha = exp(log_alpha), k, q [token][row]; w, do [token][column]; beta
     static constexpr int kInFloats = 3 * kBwdBlock * DK + 2 * kBwdBlock * BV + kBwdBlock;
-    static constexpr int kFloats = kRowFloats + kBetaFloats + kInFloats;
+    static constexpr int kFloats = kRowFloats + 2 * kBetaFloats + kInFloats;
 };
 
-template <bool BF16, int DK, int NW, int SL>
+template <bool BF16, int DK, int NW, int SL, bool SG>
 __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
     using L = BwdLanes<DK>;
     using G = typename Elem<BF16>::G;
@@ -279,7 +292,8 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
     __shared__ float stage[St::kFloats];
     float* sRow = stage;
     float* sBeta = sRow + St::kRowFloats;
-    float* sA = sBeta + St::kBetaFloats;
+    float* sGate = sBeta + St::kBetaFloats;
+    float* sA = sGate + St::kBetaFloats;
     float* sK = sA + kBwdBlock * DK;
     float* sQ = sK + kBwdBlock * DK;
     float* sW = sQ + kBwdBlock * DK;
@@ -333,7 +347,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
         const int ntok = static_cast<int>(te - tb);
         for (int i = threadIdx.x; i < ntok * DK; i += 64 * NW) {
             const int64_t tk = ((tb + i / DK) * H + h) * DK + i % DK;
-            sA[i] = exp_e(a.la[tk]);
+            sA[i] = exp_e(SG ? a.la[(tb + i / DK) * H + h] : a.la[tk]);
             sK[i] = ld<BF16>(gk + tk);
             sQ[i] = ld<BF16>(gq + tk);
         }
@@ -420,6 +434,14 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) a.dv[tv + c0 + c] = bt * de[c];
                 }
+                if constexpr (SG) {
+                    // the per-head gate: dlog_alpha summed over the key channels too
+                    float gp = 0.f;
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr) gp = __builtin_fmaf(al[rr], dap[rr], gp);
+                    gp = wave_sum(gp);
+                    if (lane == 0) sGate[r * NW + wv] = gp;
+                }
                 if constexpr (DK == 32) {
                     // the two column halves of a row meet
 #pragma unroll
@@ -436,15 +458,17 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
                         const int row = L::row(lane, rr);
                         sRow[((0 * kBwdHalf + r) * NW + wv) * DK + row] = dqp[rr];
                         sRow[((1 * kBwdHalf + r) * NW + wv) * DK + row] = dkp[rr];
-                        sRow[((2 * kBwdHalf + r) * NW + wv) * DK + row] = al[rr] * dap[rr];
+                        if constexpr (!SG) sRow[((2 * kBwdHalf + r) * NW + wv) * DK + row] = al[rr] * dap[rr];
                     }
                 }
                 if (lane == 0) sBeta[r * NW + wv] = dbp;
             }
             lds_barrier();
-            // sums over the waves, one output element per thread and item
-            for (int it = threadIdx.x; it < 3 * kBwdHalf * DK + kBwdHalf; it += 64 * NW) {
-                if (it < 3 * kBwdHalf * DK) {
+            // sums over the waves, one output element per thread and item: row sums
+            // of NQ quantities, then dbeta, then (SG) the per-head gate
+            constexpr int NQ = SG ? 2 : 3;
+            for (int it = threadIdx.x; it < NQ * kBwdHalf * DK + (SG ? 2 : 1) * kBwdHalf; it += 64 * NW) {
+                if (it < NQ * kBwdHalf * DK) {
                     const int qn = it / (kBwdHalf * DK), r = (it / DK) % kBwdHalf, row = it % DK;
                     const int64_t t = th + r;
                     if (t < te) {
@@ -459,12 +483,13 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
                         }
                     }
                 } else {
-                    const int r = it - 3 * kBwdHalf * DK;
+                    const int r2 = it - NQ * kBwdHalf * DK, r = r2 % kBwdHalf;
+                    const bool gate = r2 >= kBwdHalf;  // SG only
                     const int64_t t = th + r;
                     if (t < te) {
                         float acc = 0.f;
-                        for (int w2 = 0; w2 < NW; ++w2) acc += sBeta[r * NW + w2];
-                        float* dst = a.dbeta + t * H + h;
+                        for (int w2 = 0; w2 < NW; ++w2) acc += (gate ? sGate : sBeta)[r * NW + w2];
+                        float* dst = (gate ? a.dla : a.dbeta) + t * H + h;
                         if constexpr (SL > 1) {
                             atomicAdd(dst, acc);
                         } else {
@@ -497,38 +522,44 @@ inline unsigned grid_1d(int64_t count) {
     return static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
 }
 
-template <bool BF16, int DK, int NW>
+template <bool BF16, int DK, int NW, bool SG>
 hipError_t launch_bwd_nw(const BwdArgs& a, int64_t T_tot, hipStream_t st) {
     const int slices = a.DV / (kBwdCols * NW);
     const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.N) * a.H * slices);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_forward_kernel<BF16, DK, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((bwd_forward_kernel<BF16, DK, NW, SG>), dim3(grid), dim3(64 * NW), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (slices == 2) {
-        // zero the outputs the slices add into: dq, dk, dlog_alpha [T_tot, H, d_k], dbeta [T_tot, H]
+        // zero the outputs the slices add into: dq, dk, dlog_alpha [T_tot, H, d_k] ([T_tot, H]
+        // with SG), dbeta [T_tot, H]
         const int64_t rowN = T_tot * a.H * DK;
         float* bufs[4] = {a.dq, a.dk, a.dla, a.dbeta};
-        const int64_t counts[4] = {rowN, rowN, rowN, T_tot * a.H};
+        const int64_t counts[4] = {rowN, rowN, SG ? T_tot * a.H : rowN, T_tot * a.H};
         for (int i = 0; i < 4; ++i)
             if (counts[i] > 0)
                 hipLaunchKernelGGL(bwd_zero_kernel, dim3(grid_1d(counts[i])), dim3(256), 0, st, bufs[i], counts[i]);
-        hipLaunchKernelGGL((bwd_kernel<BF16, DK, NW, 2>), dim3(grid), dim3(64 * NW), 0, st, a);
+        hipLaunchKernelGGL((bwd_kernel<BF16, DK, NW, 2, SG>), dim3(grid), dim3(64 * NW), 0, st, a);
     } else if (slices == 1) {
-        hipLaunchKernelGGL((bwd_kernel<BF16, DK, NW, 1>), dim3(grid), dim3(64 * NW), 0, st, a);
+        hipLaunchKernelGGL((bwd_kernel<BF16, DK, NW, 1, SG>), dim3(grid), dim3(64 * NW), 0, st, a);
     } else {
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <bool BF16, int DK>
-hipError_t launch_bwd_dk(const BwdArgs& a, int64_t T_tot, hipStream_t st) {
+template <bool BF16, int DK, bool SG>
+hipError_t launch_bwd_sg(const BwdArgs& a, int64_t T_tot, hipStream_t st) {
     switch (bwd_waves(a.DV)) {
-        case 4: return launch_bwd_nw<BF16, DK, 4>(a, T_tot, st);
-        case 8: return launch_bwd_nw<BF16, DK, 8>(a, T_tot, st);
+        case 4: return launch_bwd_nw<BF16, DK, 4, SG>(a, T_tot, st);
+        case 8: return launch_bwd_nw<BF16, DK, 8, SG>(a, T_tot, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <bool BF16, int DK>
+hipError_t launch_bwd_dk(const BwdArgs& a, bool scalar_gate, int64_t T_tot, hipStream_t st) {
+    return scalar_gate ? launch_bwd_sg<BF16, DK, true>(a, T_tot, st) : launch_bwd_sg<BF16, DK, false>(a, T_tot, st);
 }
 
 inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -571,15 +602,15 @@ hipError_t launch_prefill_bwd(const BackwardArgs& b) {
     hipStream_t st = static_cast<hipStream_t>(b.stream);
     if (b.bf16) {
         switch (b.d_k) {
-            case 32: return launch_bwd_dk<true, 32>(a, b.T_tot, st);
-            case 64: return launch_bwd_dk<true, 64>(a, b.T_tot, st);
-            case 128: return launch_bwd_dk<true, 128>(a, b.T_tot, st);
+            case 32: return launch_bwd_dk<true, 32>(a, b.scalar_gate, b.T_tot, st);
+            case 64: return launch_bwd_dk<true, 64>(a, b.scalar_gate, b.T_tot, st);
+            case 128: return launch_bwd_dk<true, 128>(a, b.scalar_gate, b.T_tot, st);
         }
     } else {
         switch (b.d_k) {
-            case 32: return launch_bwd_dk<false, 32>(a, b.T_tot, st);
-            case 64: return launch_bwd_dk<false, 64>(a, b.T_tot, st);
-            case 128: return launch_bwd_dk<false, 128>(a, b.T_tot, st);
+            case 32: return launch_bwd_dk<false, 32>(a, b.scalar_gate, b.T_tot, st);
+            case 64: return launch_bwd_dk<false, 64>(a, b.scalar_gate, b.T_tot, st);
+            case 128: return launch_bwd_dk<false, 128>(a, b.scalar_gate, b.T_tot, st);
         }
     }
     return hipErrorInvalidValue;

@@ -84,6 +84,7 @@ struct BackwardArgs {
     float *dq, *dk, *dv, *dlog_alpha, *dbeta, *dS0;
     void* workspace;  // at least prefill_bwd_workspace_bytes(...) bytes, 256-byte aligned
     void* stream;
+    bool scalar_gate = false;  // log_alpha and dlog_alpha are [T_tot, H] (one gate per token and head)
 };
 
 hipError_t launch_prefill(const PrefillArgs& a);

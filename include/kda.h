@@ -257,6 +257,23 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
                                 float* d_log_alpha, float* d_beta, float* d_S0, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * gdn_prefill_backward -- the backward pass of gdn_prefill (one gate per token
+ * and head).  Arguments as for kda_prefill_backward, except that log_alpha
+ * and d_log_alpha are device [T_tot, H] float32, 4-byte aligned;
+ * d_log_alpha[t, h] is the gradient with respect to the one gate, i.e. the
+ * sum over the key channels of the per-channel gradient.  The other
+ * gradients are bit-identical to kda_prefill_backward's with log_alpha
+ * repeated over the d_k channels.  Workspace as for kda_prefill_backward.
+ */
+kda_status gdn_prefill_backward(const void* q, const void* k, const void* v,
+                                const float* log_alpha, const float* beta, const float* S0,
+                                const int32_t* cu_seqlens, int32_t N, int64_t T_tot, int32_t H,
+                                int32_t d_k, int32_t d_v, kda_dtype dtype, const void* d_o,
+                                const float* d_S_T, float* d_q, float* d_k_out, float* d_v_out,
+                                float* d_log_alpha, float* d_beta, float* d_S0, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Workspace bytes kda_prefill_backward needs: fp32 states at the start of
  * every 16-token block of every sequence (at most T_tot / 16 + N + 1 blocks
  * per head) and one fp32 row of d_v per token and head.  0 for unsupported

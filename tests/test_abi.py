@@ -196,3 +196,18 @@ def test_backward_workspace_size():
     assert kda.kda_prefill_backward_workspace_size(n, t, h, dk, dv, BF16) == (ck + 255) // 256 * 256 + t * h * dv * 4
     assert kda.kda_prefill_backward_workspace_size(0, t, h, dk, dv, BF16) == 0
     assert kda.kda_prefill_backward_workspace_size(n, t, h, 48, dv, BF16) == 0
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(log_alpha=FAKE + 2), "4-byte aligned"),
+    (dict(d_log_alpha=FAKE + 2), "4-byte aligned"),
+    (dict(d_q=FAKE + 4), "16-byte aligned"),
+])
+def test_gdn_backward_validation(kw, needle):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, log_alpha=FAKE + 4, beta=FAKE, S0=None, cu_seqlens=FAKE, N=1,
+             T_tot=64, H=2, d_k=64, d_v=64, dtype=BF16, d_o=FAKE, d_S_T=None, d_q=FAKE, d_k_out=FAKE,
+             d_v_out=FAKE, d_log_alpha=FAKE + 4, d_beta=FAKE, d_S0=FAKE, workspace=0x100000,
+             workspace_bytes=1 << 40, stream=None)
+    a.update(kw)
+    assert kda.gdn_prefill_backward(**a) == kda.KDA_ERR_INVALID_ARG
+    assert needle in kda.kda_last_error()

@@ -92,3 +92,20 @@ def test_backward_varlen_32k_sampled_heads():
             assert_close(host(g[:, heads]), r[:, heads], "bf16", name)
         else:
             assert_close(host(g[:, heads]), r[:, heads], "bf16", name)
+
+
+def test_backward_strong_decay_and_resets():
+    """The backward evaluates no decay products, so any finite log alpha
+    works: gates drawn from -U(0, 5), plus tokens with log alpha = -1000 (a
+    reset: alpha underflows to 0 in fp32 and fp64 alike)."""
+    import torch
+    x = inputs.make_prefill_inputs([90, 45], 2, 64, 128, "bf16", seed=77, s0_std=1.0,
+                                   log_alpha_range=(0.0, 5.0))
+    x.log_alpha[[3, 50, 51, 100], :, :] = -1000.0
+    dO, dST = inputs.make_backward_grads(x, seed=78)
+    ref = oracle.prefill_backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens,
+                                  dO.astype(np.float64), dST)
+    got = _run(x, dO, dST)
+    torch.cuda.synchronize()
+    for name, g, r in zip(NAMES, got, ref):
+        assert_close(host(g), r, "bf16", name)

@@ -101,3 +101,31 @@ def test_gdn_wide_decay():
     o, ST = kda.gdn_prefill_t(**dict(d, log_alpha=torch.from_numpy(la).cuda()), wide_decay=True)
     assert_close(host(o), ref_o, "bf16", "o")
     assert_close(host(ST), ref_S, "bf16", "S_T")
+
+
+@pytest.mark.parametrize("case", [([70, 0, 33], 2, 64, 64, "f32"), ([150, 40], 2, 128, 128, "bf16"),
+                                  ([37], 3, 32, 128, "bf16")], ids=lambda c: f"L{'-'.join(map(str, c[0]))}_dk{c[2]}_dv{c[3]}_{c[4]}")
+def test_gdn_backward_matches_oracle_and_kda(case):
+    """gdn_prefill_backward against the oracle's scalar-gate backward; its
+    other gradients carry the same bits as kda_prefill_backward's with the
+    gate repeated over the channels, and its gate gradient is their channel sum."""
+    import torch
+    lengths, H, dk, dv, dtype = case
+    x = inputs.make_prefill_inputs(lengths, H, dk, dv, dtype, seed=sum(lengths) + 11, s0_std=1.0)
+    la = _scalar_gate(x)
+    dO, dST = inputs.make_backward_grads(x, seed=sum(lengths) + 12)
+    ref = oracle.gdn_prefill_backward(x.q, x.k, x.v, la, x.beta, x.S0, x.cu_seqlens, dO.astype(np.float64), dST)
+    d = upload(x)
+    td = d["q"].dtype
+    dO_d, dST_d = torch.from_numpy(dO).cuda().to(td), torch.from_numpy(dST).cuda()
+    la_d = torch.from_numpy(la).cuda()
+    args = lambda g: (d["q"], d["k"], d["v"], g, d["beta"], d["S0"], d["cu_seqlens"], dO_d, dST_d)
+    got = kda.gdn_prefill_backward_t(*args(la_d))
+    full = kda.prefill_backward(*args(la_d[:, :, None].expand(-1, -1, dk).contiguous()))
+    torch.cuda.synchronize()
+    names = ("d_q", "d_k", "d_v", "d_log_alpha", "d_beta", "d_S0")
+    for name, g, r in zip(names, got, ref):
+        assert_close(host(g), r, dtype, name)
+    for i in (0, 1, 2, 4, 5):
+        assert torch.equal(got[i], full[i]), f"{names[i]}: GDN != KDA with the gate repeated"
+    assert_close(host(got[3]), host(full[3]).sum(axis=2), "f32", "d_log_alpha vs channel sum")
