@@ -109,3 +109,30 @@ def test_backward_strong_decay_and_resets():
     torch.cuda.synchronize()
     for name, g, r in zip(NAMES, got, ref):
         assert_close(host(g), r, "bf16", name)
+
+
+def test_backward_all_sequences_empty():
+    """T_tot = 0: no token gradients, and the initial state's gradient is dL/dS_T."""
+    import torch
+    x = inputs.make_prefill_inputs([0, 0, 0], 2, 64, 128, "bf16", seed=3, s0_std=1.0)
+    dO, dST = inputs.make_backward_grads(x, seed=4)
+    got = _run(x, dO, dST)
+    torch.cuda.synchronize()
+    assert all(g.numel() == 0 for g in got[:5])
+    assert torch.equal(got[5], torch.from_numpy(dST).cuda())
+
+
+def test_backward_many_short_sequences():
+    """Forty sequences of 0 to 40 tokens (many not a multiple of 16) in one
+    batch: every sequence's checkpoint blocks land in their own slots."""
+    import torch
+    rng = np.random.default_rng(5)
+    lengths = [int(v) for v in rng.integers(0, 41, size=40)]
+    x = inputs.make_prefill_inputs(lengths, 1, 64, 64, "f32", seed=6, s0_std=1.0)
+    dO, dST = inputs.make_backward_grads(x, seed=7)
+    ref = oracle.prefill_backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens,
+                                  dO.astype(np.float64), dST)
+    got = _run(x, dO, dST)
+    torch.cuda.synchronize()
+    for name, g, r in zip(NAMES, got, ref):
+        assert_close(host(g), r, "f32", name)
