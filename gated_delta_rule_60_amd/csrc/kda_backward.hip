@@ -25,13 +25,15 @@
 //
 // Pass 1 (bwd_forward_kernel) runs the forward recurrence and stores the
 // state entering every 16-token block (fp32 checkpoints) and w_t = v_t - u_t
-// for every token.  Pass 2 (bwd_kernel) walks the blocks from the last,
-// recomputes the states of 8 tokens at a time from the block's checkpoint
-// into registers (steps that need no column sum, since w is stored), and
-// applies the reverse step token by token.
+// for every token.  Pass 2 (bwd_kernel) walks the blocks from the last: it
+// stages a block's inputs in LDS, recomputes the states of 8 tokens at a time
+// from the block's checkpoint into registers (steps that need no column sum,
+// since w is stored), and applies the reverse step token by token.  A
+// compile-time flag (SG) serves one gate per token and head (Gated DeltaNet).
 //
-// Arithmetic is fp32 on the vector ALU: the per-token work is rank-1 updates
-// and matrix-vector products, with no dense contraction to give to MFMA.
+// In this token-by-token form every step is rank-1 updates and
+// matrix-vector products, done in fp32 on the vector ALU.  (The chunk form of
+// the adjoint would turn the state-sized products into MFMA contractions.)
 #include <hip/hip_runtime.h>
 
 #include "kda_device.hpp"
