@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     KDA_ERR_INVALID_ARG,
     KDA_ERR_UNSUPPORTED,
     KDA_OK,
+    KDA_PREFILL_ANY_DECAY,
     KDA_PREFILL_SCALAR_GATE,
     KDA_PREFILL_WIDE_DECAY,
     KDAError,

@@ -21,6 +21,7 @@ KDA_DTYPE_BF16 = 0
 KDA_DTYPE_F32 = 1
 KDA_PREFILL_SCALAR_GATE = 1
 KDA_PREFILL_WIDE_DECAY = 2
+KDA_PREFILL_ANY_DECAY = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -202,7 +203,7 @@ def _stream_handle(stream, device) -> int:
 
 
 def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream,
-             scalar_gate: bool, wide_decay: bool = False):
+             scalar_gate: bool, wide_decay: bool = False, any_decay: bool = False):
     """Chunked prefill on torch tensors; returns (o, S_T).
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
@@ -213,7 +214,8 @@ def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspac
     ``workspace`` (optional): a uint8 device tensor of at least
     ``kda_prefill_workspace_size(...)`` bytes; one is allocated when needed
     and not given.  ``wide_decay`` selects the wide-decay kernel variant
-    (KDA_PREFILL_WIDE_DECAY).
+    (KDA_PREFILL_WIDE_DECAY); ``any_decay`` the token-recurrent kernel with no
+    decay-range contract (KDA_PREFILL_ANY_DECAY).
     """
     import torch
     if not q.is_cuda:
@@ -250,7 +252,8 @@ def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspac
             if workspace.numel() < ws:
                 raise ValueError(f"workspace holds {workspace.numel()} bytes; {ws} are needed")
             wbuf = workspace
-    flags = (KDA_PREFILL_SCALAR_GATE if scalar_gate else 0) | (KDA_PREFILL_WIDE_DECAY if wide_decay else 0)
+    flags = ((KDA_PREFILL_SCALAR_GATE if scalar_gate else 0) | (KDA_PREFILL_WIDE_DECAY if wide_decay else 0)
+             | (KDA_PREFILL_ANY_DECAY if any_decay else 0))
     with torch.cuda.device(dev):
         _check(kda_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
                               beta.data_ptr(), S0.data_ptr() if S0 is not None else None,
@@ -261,19 +264,21 @@ def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspac
 
 
 def prefill(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=None,
-            v_split: int = 0, workspace=None, wide_decay: bool = False, stream=None):
+            v_split: int = 0, workspace=None, wide_decay: bool = False, any_decay: bool = False,
+            stream=None):
     """KDA chunked prefill (per-channel gates, log_alpha [T, H, d_k]) on torch
     tensors; returns (o, S_T).  Arguments as in ``_prefill``."""
     return _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream, False,
-                    wide_decay)
+                    wide_decay, any_decay)
 
 
 def gdn_prefill_t(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=None,
-                  v_split: int = 0, workspace=None, wide_decay: bool = False, stream=None):
+                  v_split: int = 0, workspace=None, wide_decay: bool = False, any_decay: bool = False,
+                  stream=None):
     """Gated DeltaNet chunked prefill (one gate per token and head, log_alpha
     [T, H]) on torch tensors; returns (o, S_T).  Arguments as in ``_prefill``."""
     return _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream, True,
-                    wide_decay)
+                    wide_decay, any_decay)
 
 
 

@@ -155,7 +155,8 @@ kda_status gdn_prefill_backward(const void* q, const void* k, const void* v, con
 namespace {
 
 // Shared by every prefill entry point.  KDA_PREFILL_SCALAR_GATE changes only
-// the shape of log_alpha ([T_tot, H], 4-byte aligned); KDA_PREFILL_WIDE_DECAY
+// the shape of log_alpha ([T_tot, H], 4-byte aligned); KDA_PREFILL_ANY_DECAY
+// selects the token-recurrent kernel; KDA_PREFILL_WIDE_DECAY
 // selects the wide-decay kernel variant.
 kda_status prefill_impl(const void* q, const void* k, const void* v, const float* log_alpha,
                         const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
@@ -163,8 +164,10 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
                         float* S_T, void* workspace, size_t workspace_bytes, int32_t v_split,
                         uint32_t flags, void* stream) {
     g_last_error.clear();
-    if ((flags & ~static_cast<uint32_t>(KDA_PREFILL_SCALAR_GATE | KDA_PREFILL_WIDE_DECAY)) != 0)
+    if ((flags & ~static_cast<uint32_t>(KDA_PREFILL_SCALAR_GATE | KDA_PREFILL_WIDE_DECAY | KDA_PREFILL_ANY_DECAY)) != 0)
         return fail(KDA_ERR_INVALID_ARG, "unknown bits in flags");
+    if ((flags & KDA_PREFILL_WIDE_DECAY) && (flags & KDA_PREFILL_ANY_DECAY))
+        return fail(KDA_ERR_INVALID_ARG, "KDA_PREFILL_WIDE_DECAY and KDA_PREFILL_ANY_DECAY exclude each other");
     const bool scalar_gate = (flags & KDA_PREFILL_SCALAR_GATE) != 0;
     if (N < 1 || H < 1 || T_tot < 0)
         return fail(KDA_ERR_INVALID_ARG, "need N >= 1, H >= 1 and T_tot >= 0");
@@ -201,7 +204,7 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
 
     kda::PrefillArgs a{q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
                        dtype == KDA_DTYPE_BF16, o, S_T, v_split, stream, workspace, scalar_gate,
-                       (flags & KDA_PREFILL_WIDE_DECAY) != 0};
+                       (flags & KDA_PREFILL_WIDE_DECAY) != 0, (flags & KDA_PREFILL_ANY_DECAY) != 0};
     (void)hipGetLastError();  // report only this launch's status
     const hipError_t e = kda::launch_prefill(a);
     if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");

@@ -509,6 +509,118 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
         for (int c = 0; c < CPL; ++c) a.dS0[sbase + static_cast<int64_t>(L::row(lane, rr)) * DV + c0 + c] = Gr[rr][c];
 }
 
+// ---------------------------------------------------------------------------
+// Token-recurrent prefill (KDA_PREFILL_ANY_DECAY): the forward recurrence of
+// pass 1 plus the read-out o_t = S_t^T q_t and the final state.  It forms no
+// decay products across tokens, so any finite log alpha <= 0 works (a token
+// with alpha underflowing to 0 resets the state exactly).  Same grid and
+// column ownership as pass 1.  S_T may alias S0: each lane reads and writes
+// only its own elements.
+// ---------------------------------------------------------------------------
+struct RecArgs {
+    const void *q, *k, *v;
+    const float *la, *beta, *S0;
+    const int32_t* cu;
+    int32_t H, DV;
+    void* o;
+    float* S_T;
+};
+
+template <bool BF16, int DK, int NW, bool SG>
+__global__ void __launch_bounds__(64 * NW) rec_prefill_kernel(RecArgs a) {
+    using L = BwdLanes<DK>;
+    using G = typename Elem<BF16>::G;
+    constexpr int R = L::R, CPL = L::CPL;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int slices = a.DV / (kBwdCols * NW);
+    const int s = blockIdx.x % slices, pair = blockIdx.x / slices;
+    const int n = pair / a.H, h = pair % a.H;
+    const int H = a.H, DV = a.DV;
+    const int c0 = (s * NW + wv) * kBwdCols + L::col(lane);
+    const int64_t t0 = a.cu[n], t1 = a.cu[n + 1];
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV;
+    const G* gq = static_cast<const G*>(a.q);
+    const G* gk = static_cast<const G*>(a.k);
+    const G* gv = static_cast<const G*>(a.v);
+    G* go = static_cast<G*>(a.o);
+
+    float S[R][CPL];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            S[rr][c] = a.S0 ? a.S0[sbase + static_cast<int64_t>(L::row(lane, rr)) * DV + c0 + c] : 0.f;
+
+    // inputs of the next token are loaded while the current one is computed
+    float nla[R], nk[R], nq[R], nv[CPL], nb = 0.f;
+    auto fetch = [&](int64_t t) __attribute__((always_inline)) {
+        const int64_t tk = (t * H + h) * DK, tv = (t * H + h) * DV;
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            nla[rr] = SG ? a.la[t * H + h] : a.la[tk + L::row(lane, rr)];
+            nk[rr] = ld<BF16>(gk + tk + L::row(lane, rr));
+            nq[rr] = ld<BF16>(gq + tk + L::row(lane, rr));
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) nv[c] = ld<BF16>(gv + tv + c0 + c);
+        nb = a.beta[t * H + h];
+    };
+    if (t0 < t1) fetch(t0);
+    for (int64_t t = t0; t < t1; ++t) {
+        float al[R], kk[R], qq[R], vv[CPL];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            al[rr] = exp_e(nla[rr]);
+            kk[rr] = nk[rr];
+            qq[rr] = nq[rr];
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) vv[c] = nv[c];
+        const float bt = nb;
+        if (t + 1 < t1) fetch(t + 1);
+        float up[CPL], u[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            float acc = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) {
+                S[rr][c] *= al[rr];
+                acc = __builtin_fmaf(kk[rr], S[rr][c], acc);
+            }
+            up[c] = acc;
+        }
+        column_sums<DK>(up, u, lane);
+        float op[CPL], ov[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const float e = bt * (vv[c] - u[c]);
+            float acc = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) {
+                S[rr][c] = __builtin_fmaf(kk[rr], e, S[rr][c]);
+                acc = __builtin_fmaf(qq[rr], S[rr][c], acc);
+            }
+            op[c] = acc;
+        }
+        column_sums<DK>(op, ov, lane);
+        if ((lane & 31) == 0 && (DK == 32 || lane == 0)) {
+            const int64_t tv = (t * H + h) * DV;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                if constexpr (BF16) {
+                    go[tv + c0 + c] = f32_to_bf16(ov[c]);
+                } else {
+                    go[tv + c0 + c] = ov[c];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) a.S_T[sbase + static_cast<int64_t>(L::row(lane, rr)) * DV + c0 + c] = S[rr][c];
+}
+
 __global__ void __launch_bounds__(256) bwd_zero_kernel(float* __restrict__ p, int64_t count) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < count;
          i += static_cast<int64_t>(gridDim.x) * 256)
@@ -616,6 +728,44 @@ hipError_t launch_prefill_bwd(const BackwardArgs& b) {
         }
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_recurrent(const PrefillArgs& p) {
+    RecArgs a{p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, p.cu_seqlens, p.H, p.d_v, p.o, p.S_T};
+    const int nw = bwd_waves(p.d_v);
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.N) * p.H * (p.d_v / (kBwdCols * nw)));
+    if (grid == 0) return hipSuccess;
+    hipStream_t st = static_cast<hipStream_t>(p.stream);
+#define KDA_REC_LAUNCH(BF, DKV, NWV, SGV) \
+    hipLaunchKernelGGL((rec_prefill_kernel<BF, DKV, NWV, SGV>), dim3(grid), dim3(64 * NWV), 0, st, a)
+#define KDA_REC_DK(BF, DKV)                                                   \
+    do {                                                                      \
+        if (nw == 8) {                                                        \
+            if (p.scalar_gate) KDA_REC_LAUNCH(BF, DKV, 8, true);              \
+            else KDA_REC_LAUNCH(BF, DKV, 8, false);                           \
+        } else {                                                              \
+            if (p.scalar_gate) KDA_REC_LAUNCH(BF, DKV, 4, true);              \
+            else KDA_REC_LAUNCH(BF, DKV, 4, false);                           \
+        }                                                                     \
+    } while (0)
+    if (p.bf16) {
+        switch (p.d_k) {
+            case 32: KDA_REC_DK(true, 32); break;
+            case 64: KDA_REC_DK(true, 64); break;
+            case 128: KDA_REC_DK(true, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (p.d_k) {
+            case 32: KDA_REC_DK(false, 32); break;
+            case 64: KDA_REC_DK(false, 64); break;
+            case 128: KDA_REC_DK(false, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef KDA_REC_DK
+#undef KDA_REC_LAUNCH
+    return hipGetLastError();
 }
 
 }  // namespace kda

@@ -51,6 +51,7 @@ struct PrefillArgs {
     void* workspace;  // at least prefill_workspace_bytes(...) bytes
     bool scalar_gate = false;  // log_alpha is [T_tot, H] (one gate per token and head)
     bool wide_decay = false;   // exponents of strongly decaying channels from the chunk's middle row
+    bool any_decay = false;    // token-recurrent kernel: any finite log_alpha (kda_backward.hip)
 };
 
 struct DecodeArgs {
@@ -88,6 +89,8 @@ struct BackwardArgs {
 };
 
 hipError_t launch_prefill(const PrefillArgs& a);
+// Token-recurrent prefill for any decay range (kda_backward.hip).
+hipError_t launch_prefill_recurrent(const PrefillArgs& a);
 
 // Whether a prefill of these sizes runs segmented, and the workspace bytes it
 // then needs (0 when it does not).

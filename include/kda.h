@@ -143,11 +143,20 @@ kda_status kda_prefill_split(const void* q, const void* k, const void* v,
  *                            without the flag, so inputs within the default
  *                            contract give the same bits either way.  The
  *                            launch costs a few percent more.
+ *   KDA_PREFILL_ANY_DECAY    no range contract: any finite log_alpha <= 0,
+ *                            including hard resets (a token whose alpha
+ *                            underflows to 0 clears the state exactly).
+ *                            Runs the recurrence token by token in fp32
+ *                            on the vector ALU (no chunk factorization);
+ *                            much slower than the chunked kernel.  v_split
+ *                            and the workspace are not used.  Excludes
+ *                            KDA_PREFILL_WIDE_DECAY.
  *
  * Unknown flag bits give KDA_ERR_INVALID_ARG.
  */
 #define KDA_PREFILL_SCALAR_GATE 1u
 #define KDA_PREFILL_WIDE_DECAY 2u
+#define KDA_PREFILL_ANY_DECAY 4u
 kda_status kda_prefill_ex(const void* q, const void* k, const void* v,
                           const float* log_alpha, const float* beta, const float* S0,
                           const int32_t* cu_seqlens, int32_t N, int64_t T_tot, int32_t H,

@@ -87,10 +87,12 @@ def test_prefill_ex_rejects_unknown_flags():
     a = dict(q=FAKE, k=FAKE, v=FAKE, log_alpha=FAKE, beta=FAKE, S0=None, cu_seqlens=FAKE, N=1,
              T_tot=64, H=2, d_k=64, d_v=64, dtype=BF16, o=FAKE, S_T=FAKE, workspace=None,
              workspace_bytes=0, v_split=0, stream=None)
-    assert kda.kda_prefill_ex(flags=4, **a) == kda.KDA_ERR_INVALID_ARG
-    assert "flags" in kda.kda_last_error()
+    for unknown in (8, 16, 1 << 31):
+        assert kda.kda_prefill_ex(flags=unknown, **a) == kda.KDA_ERR_INVALID_ARG
+        assert "flags" in kda.kda_last_error()
     # known flags pass flag validation and fail later, on the bad v_split
-    for f in (kda.KDA_PREFILL_SCALAR_GATE, kda.KDA_PREFILL_WIDE_DECAY, 3):
+    for f in (kda.KDA_PREFILL_SCALAR_GATE, kda.KDA_PREFILL_WIDE_DECAY, 3, kda.KDA_PREFILL_ANY_DECAY,
+              kda.KDA_PREFILL_ANY_DECAY | kda.KDA_PREFILL_SCALAR_GATE):
         assert kda.kda_prefill_ex(flags=f, **dict(a, v_split=3)) == kda.KDA_ERR_INVALID_ARG
         assert "v_split" in kda.kda_last_error()
 
@@ -211,3 +213,12 @@ def test_gdn_backward_validation(kw, needle):
     a.update(kw)
     assert kda.gdn_prefill_backward(**a) == kda.KDA_ERR_INVALID_ARG
     assert needle in kda.kda_last_error()
+
+
+def test_prefill_any_decay_excludes_wide_decay():
+    a = dict(q=FAKE, k=FAKE, v=FAKE, log_alpha=FAKE, beta=FAKE, S0=None, cu_seqlens=FAKE, N=1,
+             T_tot=64, H=2, d_k=64, d_v=64, dtype=BF16, o=FAKE, S_T=FAKE, workspace=None,
+             workspace_bytes=0, v_split=0,
+             flags=kda.KDA_PREFILL_WIDE_DECAY | kda.KDA_PREFILL_ANY_DECAY, stream=None)
+    assert kda.kda_prefill_ex(**a) == kda.KDA_ERR_INVALID_ARG
+    assert "exclude each other" in kda.kda_last_error()
