@@ -206,7 +206,7 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
                        dtype == KDA_DTYPE_BF16, o, S_T, v_split, stream, workspace, scalar_gate,
                        (flags & KDA_PREFILL_WIDE_DECAY) != 0, (flags & KDA_PREFILL_ANY_DECAY) != 0};
     (void)hipGetLastError();  // report only this launch's status
-    const hipError_t e = kda::launch_prefill(a);
+    const hipError_t e = a.any_decay ? kda::launch_prefill_recurrent(a) : kda::launch_prefill(a);
     if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
     return KDA_OK;
 }

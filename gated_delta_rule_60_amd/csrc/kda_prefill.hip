@@ -1257,7 +1257,6 @@ static hipError_t launch_prefill_dt(const PrefillArgs& a, const SegView& seg) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {
-    if (a.any_decay) return launch_prefill_recurrent(a);
     SegView seg{};
     const bool segmented = prefill_segmented(a.N, a.T_tot, a.H, a.d_k, a.d_v);
     if (segmented) {
