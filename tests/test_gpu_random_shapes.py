@@ -1,0 +1,60 @@
+"""A seeded sweep over shapes and options, each case compared element by
+element with the fp64 oracle: ragged lengths (with empty sequences),
+1-3 heads, every head size pair, both dtypes, every valid v_split, the
+scalar gate and the wide- and any-decay variants, and the backward."""
+import numpy as np
+import pytest
+
+import gated_delta_rule_60_amd as kda
+import oracle
+from gated_delta_rule_60_amd import inputs
+from gpu_util import assert_close, host, log, upload, valid_splits
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(n=60, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.integers(1, 5))
+        lengths = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 300, size=N)]
+        H = int(rng.integers(1, 4))
+        dk = int(rng.choice([32, 64, 128]))
+        dv = int(rng.choice([32, 64, 128]))
+        dtype = "bf16" if rng.random() < 0.6 else "f32"
+        split = int(rng.choice(valid_splits(dv)))
+        mode = str(rng.choice(["kda", "kda", "gdn", "wide", "any"]))
+        out.append((i, lengths, H, dk, dv, dtype, split, mode))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: f"{c[0]}_{c[7]}_L{'-'.join(map(str, c[1]))}_H{c[2]}_dk{c[3]}_dv{c[4]}_{c[5]}_s{c[6]}")
+def test_random_shape_forward_and_backward(case):
+    import torch
+    i, lengths, H, dk, dv, dtype, split, mode = case
+    x = inputs.make_prefill_inputs(lengths, H, dk, dv, dtype, seed=1000 + i, s0_std=1.0 if i % 3 else None,
+                                   log_alpha_range=(0.0, 4.0) if mode in ("wide", "any") else (0.001, 0.1))
+    d = upload(x)
+    log(f"  case {case}")
+    if mode == "gdn":
+        la = np.ascontiguousarray(x.log_alpha[:, :, 0])
+        ref_o, ref_S = oracle.gdn_prefill(x.q, x.k, x.v, la, x.beta, x.S0, x.cu_seqlens)
+        o, ST = kda.gdn_prefill_t(**dict(d, log_alpha=torch.from_numpy(la).cuda()), v_split=split)
+    else:
+        ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens)
+        o, ST = kda.prefill(**d, v_split=split, wide_decay=(mode == "wide"), any_decay=(mode == "any"))
+    torch.cuda.synchronize()
+    assert_close(host(o), ref_o, dtype, "o")
+    assert_close(host(ST), ref_S, dtype, "S_T")
+    if mode in ("kda", "any"):
+        dO, dST = inputs.make_backward_grads(x, seed=2000 + i, with_dS_T=bool(i % 2))
+        refs = oracle.prefill_backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens,
+                                       dO.astype(np.float64), dST)
+        td = d["q"].dtype
+        grads = kda.prefill_backward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
+                                     d["cu_seqlens"], torch.from_numpy(dO).cuda().to(td),
+                                     None if dST is None else torch.from_numpy(dST).cuda())
+        torch.cuda.synchronize()
+        for name, g, r in zip(("d_q", "d_k", "d_v", "d_log_alpha", "d_beta", "d_S0"), grads, refs):
+            assert_close(host(g), r, dtype, name)
