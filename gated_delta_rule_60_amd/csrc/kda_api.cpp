@@ -198,7 +198,7 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
     // Workgroups of the prefill kernel: (sequence or segment, head, value
     // slice[, identity run]); each has at most 1024 work-items.
     const bool segmented = kda::prefill_segmented(N, T_tot, H, d_k, d_v);
-    const int64_t units = segmented ? N + T_tot / kda::kSegTokens : N;
+    const int64_t units = segmented ? N + T_tot / kda::kSegMinTokens : N;
     const int64_t grid = units * H * v_split * (segmented ? 2 : 1);
     if (grid > (int64_t{1} << 22)) return fail(KDA_ERR_INVALID_ARG, "N * H * v_split too large");
 

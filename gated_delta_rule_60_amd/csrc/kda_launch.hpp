@@ -9,15 +9,18 @@
 namespace kda {
 
 // Segmented prefill.  When a batch has too few (sequence, head) pairs to
-// fill the GPU (N * H < kSegMaxPairs), sequences longer than kSegTokens run
-// as segments of kSegTokens tokens (the last one shorter), each segment of
-// each head in its own workgroups, so one long sequence spreads over many
-// CUs.  A segment after the first starts from the zero state, and an
+// fill the GPU (N * H < kSegMaxPairs), a sequence longer than its segment
+// length runs as segments (the last one shorter), each segment of each head
+// in its own workgroups, so one long sequence spreads over many CUs.  The
+// segment length depends on the sequence's own length only: about a quarter
+// of it, a multiple of 512 tokens between kSegMinTokens and kSegTokens
+// (seg_len_for in kda_segment.hip).  A segment after the first starts from the zero state, and an
 // identity run over it (V = 0, S0 = I) gives its transition M and
 // q^_t = M_t^T q_t; fix-up passes then add the true entering state's
 // contribution.  With enough pairs the extra identity work and fix-up
 // traffic cost more than the shorter critical path saves.
-constexpr int kSegTokens = 4096;
+constexpr int kSegTokens = 4096;     // longest segment
+constexpr int kSegMinTokens = 1024;  // shortest segment length a sequence is cut at
 constexpr int kSegMaxPairs = 128;
 
 // The device plan and workspace a segmented launch uses (units == nullptr:

@@ -1271,8 +1271,8 @@ hipError_t launch_prefill(const PrefillArgs& a) {
 
 int32_t default_v_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16) {
     (void)bf16;
-    // Segmented runs: one unit per segment (bounded by N + T_tot / kSegTokens).
-    const int64_t seqs = prefill_segmented(N, T_tot, H, d_k, d_v) ? N + T_tot / kSegTokens : N;
+    // Segmented runs: one unit per segment (bounded by N + T_tot / kSegMinTokens).
+    const int64_t seqs = prefill_segmented(N, T_tot, H, d_k, d_v) ? N + T_tot / kSegMinTokens : N;
     const int64_t units = seqs * H;
     // The chunk period of a workgroup barely depends on how many value
     // columns it carries, so extra workgroups do not shorten a sequence's

@@ -44,7 +44,7 @@ struct SegLayout {
 // Workspace: {count, nlong} | units [umax] | longs [lmax] | q^ | M | D
 SegLayout seg_layout(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16) {
     SegLayout L{};
-    const int64_t full = T_tot / kSegTokens;
+    const int64_t full = T_tot / kSegMinTokens;  // segments beyond one per sequence, at most
     L.umax = static_cast<int>(N + full);
     L.lmax = static_cast<int>(full < N ? (full > 0 ? full : 1) : N);
     const size_t es = bf16 ? 2 : 4;
@@ -57,11 +57,21 @@ SegLayout seg_layout(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d
     return L;
 }
 
+// Segment length of a sequence of len tokens: a quarter of it, rounded up to
+// a multiple of the output tile (512), within [kSegMinTokens, kSegTokens].
+// It depends on len alone, so a sequence is cut the same way in any batch
+// that runs segmented.
+__device__ __forceinline__ int seg_len_for(int len) {
+    const int q = ((len + 3) / 4 + kOutTokens - 1) / kOutTokens * kOutTokens;
+    return q < kSegMinTokens ? kSegMinTokens : (q > kSegTokens ? kSegTokens : q);
+}
+static_assert(kSegMinTokens % kOutTokens == 0 && kSegTokens % kOutTokens == 0, "segments of whole output tiles");
+
 // ---------------------------------------------------------------------------
 // Plan: one workgroup.  Sequences are taken longest first (up to
 // kPlanSortMax of them; natural order beyond), each split into
-// ceil(len / kSegTokens) segments (one for an empty sequence); units list
-// the segments in that order, longs the sequences with two or more.
+// ceil(len / seg_len_for(len)) segments (one for an empty sequence); units
+// list the segments in that order, longs the sequences with two or more.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kPlanThreads) void seg_plan_kernel(const int32_t* __restrict__ cu, int N,
                                                               int4* __restrict__ units,
@@ -93,11 +103,12 @@ __global__ __launch_bounds__(kPlanThreads) void seg_plan_kernel(const int32_t* _
     __syncthreads();
     for (int base = 0; base < N; base += kPlanThreads) {
         const int r = base + tid;
-        int n = 0, len = 0, P = 0;
+        int n = 0, len = 0, P = 0, seg = kSegTokens;
         if (r < N) {
             n = sorted ? sOrder[r] : r;
             len = cu[n + 1] - cu[n];
-            P = len > kSegTokens ? (len + kSegTokens - 1) / kSegTokens : 1;
+            seg = seg_len_for(len);
+            P = len > seg ? (len + seg - 1) / seg : 1;
         }
         // inclusive scans of the segment counts and of the long-sequence flags
         sScanA[tid] = P;
@@ -117,8 +128,8 @@ __global__ __launch_bounds__(kPlanThreads) void seg_plan_kernel(const int32_t* _
             const int t0 = cu[n], t1 = cu[n + 1];
             // (bounds hold for valid offsets; the guards keep malformed ones in the workspace)
             for (int s = 0; s < P && u0 + s < umax; ++s) {
-                const int a = t0 + s * kSegTokens;
-                units[u0 + s] = make_int4(n, s, a, min(t1, a + kSegTokens));
+                const int a = t0 + s * seg;
+                units[u0 + s] = make_int4(n, s, a, min(t1, a + seg));
             }
             if (P >= 2 && l0 < lmax && u0 + P <= umax) longs[l0] = make_int4(n, u0, P, 0);
         }
@@ -425,7 +436,7 @@ __global__ __launch_bounds__(kFixThreads) void seg_out_kernel(const int4* __rest
 }  // namespace
 
 bool prefill_segmented(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v) {
-    return d_k == d_v && T_tot > kSegTokens && static_cast<int64_t>(N) * H < kSegMaxPairs;
+    return d_k == d_v && T_tot > kSegMinTokens && static_cast<int64_t>(N) * H < kSegMaxPairs;
 }
 
 size_t prefill_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16) {

@@ -91,10 +91,11 @@ typedef enum {
  * q, k, v, log_alpha, beta and o may be NULL when T_tot == 0.  No state
  * crosses a sequence boundary.
  *
- * Long sequences.  When d_k == d_v, T_tot > 4096 and N * H < 128 (too few
- * (sequence, head) pairs to fill the GPU), a sequence longer than 4096
- * tokens runs as segments of 4096 tokens (the last one shorter) that are
- * processed in parallel: a later segment starts from the zero state, an
+ * Long sequences.  When d_k == d_v, T_tot > 1024 and N * H < 128 (too few
+ * (sequence, head) pairs to fill the GPU), a sequence longer than its
+ * segment length runs as segments (the last one shorter) that are processed
+ * in parallel.  A sequence of len tokens has segments of about len / 4
+ * tokens, rounded up to a multiple of 512 and kept within [1024, 4096]: a later segment starts from the zero state, an
  * identity run over it (V = 0, S0 = I) gives its transition matrix M and the
  * transformed queries M_t^T q_t, and fix-up passes chain the segments'
  * entering states and add their contribution to the outputs.  The
@@ -165,9 +166,9 @@ kda_status kda_prefill_ex(const void* q, const void* k, const void* v,
                           uint32_t flags, void* stream);
 
 /* Bytes of workspace kda_prefill needs for these sizes: 0 unless the batch
- * runs segmented (d_k == d_v, T_tot > 4096, N * H < 128); then the segment
+ * runs segmented (d_k == d_v, T_tot > 1024, N * H < 128); then the segment
  * plan, the identity runs' outputs ([T_tot, H, d_k] in dtype) and two fp32
- * [d_k, d_v] states per (segment, head) for at most N + T_tot / 4096
+ * [d_k, d_v] states per (segment, head) for at most N + T_tot / 1024
  * segments.  0 for unsupported sizes. */
 size_t kda_prefill_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
                                   int32_t d_v, kda_dtype dtype);

@@ -67,7 +67,7 @@ def _prefill(**kw):
     (dict(v_split=8), kda.KDA_ERR_INVALID_ARG, "v_split"),  # 64 / 8 < 16
     (dict(T_tot=2**31), kda.KDA_ERR_INVALID_ARG, "int32"),
     (dict(T_tot=1, H=2**20 // 64 + 1), kda.KDA_ERR_INVALID_ARG, "2^20"),
-    # a batch that may hold a segmented (> 4096-token) sequence needs a workspace
+    # a batch that may hold a segmented (> 1024-token) sequence needs a workspace
     (dict(T_tot=8192), kda.KDA_ERR_INVALID_ARG, "workspace smaller"),
     (dict(T_tot=8192, workspace_bytes=1 << 40), kda.KDA_ERR_INVALID_ARG, "workspace must not be NULL"),
     (dict(T_tot=8192, workspace=FAKE + 16, workspace_bytes=1 << 40), kda.KDA_ERR_INVALID_ARG, "256-byte"),
@@ -136,14 +136,15 @@ def test_decode_rejects_invalid_arguments(kw, status):
 def test_workspace_and_default_split_queries():
     # no workspace unless a sequence can be long enough to run in segments
     # and the batch has too few (sequence, head) pairs to fill the GPU
-    assert kda.kda_prefill_workspace_size(1, 4096, 32, 128, 128, BF16) == 0
+    assert kda.kda_prefill_workspace_size(1, 1024, 32, 128, 128, BF16) == 0
+    assert kda.kda_prefill_workspace_size(1, 4096, 32, 128, 128, BF16) > 0
     assert kda.kda_prefill_workspace_size(1, 100000, 4, 64, 128, BF16) == 0
     assert kda.kda_prefill_workspace_size(8, 32677, 32, 128, 128, BF16) == 0  # 256 pairs
     assert kda.kda_prefill_workspace_size(3, 32677, 42, 128, 128, BF16) > 0   # 126 pairs
     assert kda.kda_prefill_workspace_size(4, 32677, 32, 128, 128, BF16) == 0  # 128 pairs
     ws = kda.kda_prefill_workspace_size(1, 131072, 32, 128, 128, BF16)
-    # at least the identity runs' outputs and M, D for N + T_tot // 4096 segments
-    segs = 1 + 131072 // 4096
+    # at least the identity runs' outputs and M, D for N + T_tot // 1024 segments
+    segs = 1 + 131072 // 1024
     assert ws >= 131072 * 32 * 128 * 2 + 2 * segs * 32 * 128 * 128 * 4
     assert ws < 2 * (131072 * 32 * 128 * 2 + 2 * segs * 32 * 128 * 128 * 4)
     assert kda.kda_prefill_workspace_size(1, 131072, 32, 128, 128, F32) > ws
