@@ -375,7 +375,9 @@ def main():
             "workspace_bytes": bws,
             "roofline": {"bound": "alu", "achieved": bfl / (b_avg * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": bfl / (b_avg * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
-                         "traffic": None, "kernel": "kda::bwd_forward_kernel + kda::bwd_kernel (one call)",
+                         "traffic": measured_traffic("prefill_backward", args.workload,
+                                                     ["kda_backward.hip", "kda_device.hpp"]),
+                         "kernel": "kda::bwd_forward_kernel + kda::bwd_kernel (one call)",
                          "alg_flops_per_launch": bfl, "alg_bytes_per_launch": bby,
                          "hbm_frac": bby / (b_avg * 1e-3) / 1e9 / HBM_PEAK_GBS},
         }
