@@ -29,11 +29,11 @@ def test_deterministic_and_split_invariant_bits(dtype):
 
 
 @pytest.mark.parametrize("lengths", [[100, 0, 130, 64], [9000, 100, 0, 4097], [3000, 3000, 10]],
-                         ids=["short", "segmented", "segmented_mode_no_long_sequence"])
+                         ids=["short", "segmented", "segmented_mid_lengths"])
 def test_packing_does_not_change_bits(lengths):
-    """A sequence gives the same bits alone or in any batch; with a batch
-    over 4096 tokens the long sequences run in segments, which depend on the
-    sequence's own length only."""
+    """A sequence gives the same bits alone or in any batch; in a small
+    batch past 1024 tokens the long sequences run in segments, whose length
+    depends on the sequence's own length only."""
     import torch
     x = _x(lengths)
     d = upload(x)

@@ -138,7 +138,7 @@ def test_wide_decay_keeps_the_bits_within_the_default_contract(lengths):
 
 
 SEGMENTED = [
-    # lengths (some over 4096 tokens: run as 4096-token segments), H, d_k = d_v, dtype, s0
+    # lengths (batches past 1024 tokens run in segments of 1024-4096 tokens), H, d_k = d_v, dtype, s0
     ([2 * 4096 + 77, 300, 4096, 4097], 2, 128, "bf16", True),
     ([3 * 4096 + 5, 10], 1, 128, "f32", True),
     ([4100, 0, 9000], 2, 64, "bf16", True),
@@ -148,8 +148,8 @@ SEGMENTED = [
 
 @pytest.mark.parametrize("case", SEGMENTED, ids=lambda c: f"L{'-'.join(map(str, c[0]))}_H{c[1]}_d{c[2]}_{c[3]}")
 def test_long_sequences_in_segments(case):
-    """Sequences past 4096 tokens run as parallel segments chained by the
-    fix-up passes: every output and final state against the oracle, and the
+    """Long sequences in small batches run as parallel segments chained by
+    the fix-up passes: every output and final state against the oracle, and the
     same bits for every launch shape."""
     import torch
     lengths, H, d, dtype, s0 = case

@@ -1,7 +1,8 @@
 """A seeded sweep over shapes and options, each case compared element by
 element with the fp64 oracle: ragged lengths (with empty sequences),
 1-3 heads, every head size pair, both dtypes, every valid v_split, the
-scalar gate and the wide- and any-decay variants, and the backward."""
+scalar gate and the wide- and any-decay variants, and the backward; then
+small batches past 1024 tokens, which run in segments."""
 import numpy as np
 import pytest
 
@@ -58,3 +59,47 @@ def test_random_shape_forward_and_backward(case):
         torch.cuda.synchronize()
         for name, g, r in zip(("d_q", "d_k", "d_v", "d_log_alpha", "d_beta", "d_S0"), grads, refs):
             assert_close(host(g), r, dtype, name)
+
+
+def _segment_cases(n=14, seed=4242):
+    """Small batches past 1024 tokens, d_k = d_v: the segmented path. Lengths
+    mix the cut points of the 1024-4096-token segments (one token past a
+    multiple of 512 or 1024) with random lengths and empty sequences."""
+    rng = np.random.default_rng(seed)
+    edges = [1025, 1536, 1537, 2049, 4096, 4097, 6145]
+    out = []
+    for i in range(n):
+        N = int(rng.integers(1, 4))
+        lengths = [int(rng.choice(edges)) if rng.random() < 0.4 else int(rng.integers(0, 7000))
+                   for _ in range(N)]
+        if sum(lengths) <= 1024:
+            lengths[0] += 1025
+        if i % 4 == 3:
+            lengths.insert(int(rng.integers(0, N + 1)), 0)
+        H = int(rng.integers(1, 3))
+        d = int(rng.choice([32, 64, 128]))
+        dtype = "bf16" if rng.random() < 0.6 else "f32"
+        split = int(rng.choice(valid_splits(d)))
+        out.append((i, lengths, H, d, dtype, split))
+    return out
+
+
+@pytest.mark.parametrize("case", _segment_cases(),
+                         ids=lambda c: f"{c[0]}_L{'-'.join(map(str, c[1]))}_H{c[2]}_d{c[3]}_{c[4]}_s{c[5]}")
+def test_random_segmented_batches(case):
+    import torch
+    i, lengths, H, d, dtype, split = case
+    x = inputs.make_prefill_inputs(lengths, H, d, d, dtype, seed=3000 + i, s0_std=1.0 if i % 2 else None)
+    code = kda.KDA_DTYPE_BF16 if dtype == "bf16" else kda.KDA_DTYPE_F32
+    assert kda.kda_prefill_workspace_size(x.N, x.T_tot, H, d, d, code) > 0, "not the segmented path"
+    log(f"  case {case}")
+    ref_o, ref_S = oracle.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens)
+    dd = upload(x)
+    o, ST = kda.prefill(**dd, v_split=split)
+    torch.cuda.synchronize()
+    assert_close(host(o), ref_o, dtype, "o")
+    assert_close(host(ST), ref_S, dtype, "S_T")
+    for n in range(x.N):
+        a, b = x.cu_seqlens[n], x.cu_seqlens[n + 1]
+        if b > a:
+            assert_close(host(o[a:b]), ref_o[a:b], dtype, f"o sequence {n} (len {b - a})")
