@@ -313,9 +313,11 @@ __global__ __launch_bounds__(kFixThreads) void seg_out_kernel(const int4* __rest
     __shared__ __attribute__((aligned(16))) unsigned char sStage[kFixThreads / 64][Sh::STAGE];
 
     const int w = blockIdx.x;
+    // Heads vary fastest: consecutive workgroups go round-robin over the 8
+    // XCDs, so the few working tiles of short segments use every XCD.
     const int u = w / (H * TILES);
-    const int h = (w / TILES) % H;
-    const int tile = w % TILES;
+    const int tile = (w / H) % TILES;
+    const int h = w % H;
     if (u >= counts[0]) return;  // whole workgroup: before any barrier
     const int4 it = units[u];
     if (it.y == 0) return;  // a first segment starts from the true state
