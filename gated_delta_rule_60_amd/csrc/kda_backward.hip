@@ -162,6 +162,24 @@ __device__ __forceinline__ int64_t ckpt_slot(const int32_t* cu, int n, int b) {
     return static_cast<int64_t>(cu[n] / kBwdBlock) + n + b;
 }
 
+// The sequence of rank r when sequences are taken longest first (ties by
+// index): workgroups go out in that order, so the longest chains start
+// first even when not every workgroup fits on the GPU at once. Each wave
+// computes it on its own, at kernel entry with all lanes active; batches of
+// more than 64 sequences keep their order.
+__device__ __forceinline__ int seq_longest_first(const int32_t* cu, int N, int r) {
+    if (N > 64) return r;
+    const int j = threadIdx.x & 63;
+    const int len = j < N ? cu[j + 1] - cu[j] : -1;
+    int rank = 0;
+    for (int m = 0; m < N; ++m) {
+        const int lm = __shfl(len, m);
+        rank += (lm > len || (lm == len && m < j)) ? 1 : 0;
+    }
+    const unsigned long long hit = __ballot(j < N && rank == r);
+    return __ffsll(static_cast<unsigned long long>(hit)) - 1;
+}
+
 // ---------------------------------------------------------------------------
 // Pass 1: forward recurrence; checkpoints and w.  SG: one gate per token and
 // head (log_alpha [T_tot, H], Gated DeltaNet), used for every key channel.  Grid: N * H * slices
@@ -176,7 +194,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_forward_kernel(BwdArgs a) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int slices = a.DV / (kBwdCols * NW);
     const int s = blockIdx.x % slices, pair = blockIdx.x / slices;
-    const int n = pair / a.H, h = pair % a.H;
+    const int n = seq_longest_first(a.cu, a.N, pair / a.H), h = pair % a.H;
     const int H = a.H, DV = a.DV;
     const int c0 = (s * NW + wv) * kBwdCols + L::col(lane);
     const int64_t t0 = a.cu[n], t1 = a.cu[n + 1];
@@ -305,7 +323,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_kernel(BwdArgs a) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     static_assert(SL == 1 || SL == 2, "one or two slices");
     const int s = blockIdx.x % SL, pair = blockIdx.x / SL;
-    const int n = pair / a.H, h = pair % a.H;
+    const int n = seq_longest_first(a.cu, a.N, pair / a.H), h = pair % a.H;
     const int H = a.H, DV = a.DV;
     const int c0 = (s * NW + wv) * kBwdCols + L::col(lane);
     const int cs = c0 - s * BV;  // the lane's first column inside the workgroup's slice
