@@ -392,6 +392,47 @@ def pin_backward_finite_differences(lib):
         _close(grads[5], fd, f"dS0 vs finite differences {lengths}", rtol=1e-7, atol=1e-8)
 
 
+def pin_gdn_backward_finite_differences(lib):
+    """Gated DeltaNet (one forgetting rate per head, page section 三.1): every
+    gradient of L = sum(o * Ro) + sum(S_T * RS) through ``gdn_prefill``
+    equals the central difference of that (separately pinned) forward.  The
+    gate gradient is taken with respect to the one [T, H] log gate, so a
+    gate gradient that averages the channels, or keeps only one of them,
+    fails here.  Two sequences and an empty one, H = 2, d_k != d_v."""
+    rng = np.random.default_rng(73)
+    lengths, H, dk, dv = [4, 0, 3], 2, 3, 2
+    q, k, v, la, beta, S0, cu, Ro, RS = _loss_grad_case(rng, lengths, H, dk, dv)
+    la2 = np.ascontiguousarray(la[:, :, 0])
+    grads = oracle.gdn_prefill_backward(q, k, v, la2, beta, S0, cu, Ro, RS, lib=lib)
+    shapes = [q.shape, k.shape, v.shape, la2.shape, beta.shape, S0.shape]
+    for g, sh, name in zip(grads, shapes, ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0")):
+        assert np.asarray(g).shape == tuple(sh), f"{name}: shape {np.asarray(g).shape} vs {sh}"
+    args = [q, k, v, la2, beta]
+
+    def loss(a, s0):
+        o, ST = oracle.gdn_prefill(*a, s0, cu, lib=lib)
+        return float((o * Ro).sum() + (ST * RS).sum())
+
+    for ai, name in enumerate(("dq", "dk", "dv", "dlog_alpha", "dbeta")):
+        x = args[ai]
+        fd = np.zeros(x.shape)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += np.float32(2.0 ** -10)
+            xm[idx] -= np.float32(2.0 ** -10)
+            ap, am = list(args), list(args)
+            ap[ai], am[ai] = xp, xm
+            fd[idx] = (loss(ap, S0) - loss(am, S0)) / (float(xp[idx]) - float(xm[idx]))
+        _close(grads[ai], fd, f"gdn {name} vs finite differences", rtol=2e-5, atol=1e-7)
+    fd = np.zeros(S0.shape)
+    for idx in np.ndindex(S0.shape):
+        sp, sm = S0.copy(), S0.copy()
+        sp[idx] += 1e-6
+        sm[idx] -= 1e-6
+        fd[idx] = (loss(args, sp) - loss(args, sm)) / 2e-6
+    _close(grads[5], fd, "gdn dS0 vs finite differences", rtol=1e-7, atol=1e-8)
+
+
 def pin_backward_frozen_state_closed_form(lib):
     """beta = 0 and alpha = 1 freeze the state at S0, so o_t = S0^T q_t and the
     gradient reaching S_t is G_t = dS_T + sum over tau >= t of q_tau do_tau^T.
@@ -434,6 +475,7 @@ PINS = [
     pin_resume_from_state,
     pin_zero_state_and_empty_sequences,
     pin_backward_finite_differences,
+    pin_gdn_backward_finite_differences,
     pin_backward_frozen_state_closed_form,
 ]
 

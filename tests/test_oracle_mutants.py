@@ -96,3 +96,52 @@ def test_mutant_is_caught(tmp_path, name, old, new):
         return  # the mutant crashed the pin run: caught
     failed = json.loads(r.stdout.strip().splitlines()[-1])
     assert failed, f"mutant {name} passed every pin"
+
+
+# Mistakes planted in the oracle's Python layer (oracle/__init__.py): the
+# Gated DeltaNet backward sums the per-channel gate gradient over the key
+# channels, the chain rule of repeating one gate per head over them.
+PY_MUTANTS = [
+    ("gdn_gate_grad_mean_over_channels", "dla.sum(axis=2)", "dla.mean(axis=2)"),
+    ("gdn_gate_grad_channel_zero_only", "dla.sum(axis=2)", "dla[:, :, 0]"),
+    ("gdn_gate_grad_last_channel_only", "dla.sum(axis=2)", "dla[:, :, -1]"),
+]
+
+_PY_CHILD = r"""
+import json, sys
+sys.path[:0] = [sys.argv[1], sys.argv[2]]
+import oracle, oracle_pins
+assert oracle.__file__.startswith(sys.argv[1]), oracle.__file__
+lib = oracle.bind(sys.argv[3])
+print(json.dumps(oracle_pins.run_all(lib)))
+"""
+
+
+_PY_CONTROL = ("unmodified_copy", "dla.sum(axis=2)", "dla.sum(axis=2)")
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS + [_PY_CONTROL], ids=[m[0] for m in PY_MUTANTS + [_PY_CONTROL]])
+def test_python_mutant_is_caught(tmp_path, name, old, new):
+    import oracle
+
+    pkg = os.path.join(_ROOT, "oracle")
+    src = open(os.path.join(pkg, "__init__.py")).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found in the oracle"
+    mutated = src.replace(old, new, 1)
+    assert (mutated != src) == (old != new)
+    (tmp_path / "oracle").mkdir()
+    (tmp_path / "oracle" / "__init__.py").write_text(mutated)
+    (tmp_path / "oracle" / "build.py").write_text(open(os.path.join(pkg, "build.py")).read())
+    so = oracle.library_path()
+    if not os.path.exists(so):
+        oracle.build_oracle()
+    r = subprocess.run([sys.executable, "-c", _PY_CHILD, str(tmp_path), os.path.join(_ROOT, "tests"), so],
+                       capture_output=True, text=True, timeout=300)
+    if old == new:  # control: the unmodified copy passes every pin in the child
+        assert r.returncode == 0, r.stderr
+        assert json.loads(r.stdout.strip().splitlines()[-1]) == []
+        return
+    if r.returncode != 0:
+        return  # the mutant crashed the pin run: caught
+    failed = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "pin_gdn_backward_finite_differences" in failed, f"mutant {name} passed the GDN backward pin"
