@@ -36,6 +36,7 @@ from ._lib import (  # noqa: F401
     kda_prefill_backward_workspace_size,
     kda_prefill_default_split,
     kda_prefill_ex,
+    kda_prefill_plan,
     kda_prefill_split,
     kda_prefill_workspace_size,
     kda_status_string,
@@ -44,6 +45,7 @@ from ._lib import (  # noqa: F401
     load,
     prefill,
     prefill_backward,
+    prefill_plan,
 )
 
 __version__ = "0.1.0"

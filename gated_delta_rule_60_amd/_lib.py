@@ -4,7 +4,8 @@ The functions named ``kda_*`` mirror the C ABI one to one and take raw
 device pointers (ints) and a stream handle.  ``prefill`` and ``decode_step``
 are argument-marshalling conveniences over torch tensors: they check shapes
 and dtypes, allocate outputs with torch when none are given, and call the C
-ABI on torch's current stream.  Every arithmetic step runs in the library's
+ABI on the given stream (torch's current stream by default), allocating
+every temporary under that stream.  Every arithmetic step runs in the library's
 HIP kernels; there is no fallback of any kind.
 """
 from __future__ import annotations
@@ -38,6 +39,7 @@ SIGNATURES = {
                                       ctypes.c_int, _vp, _fp, _vp, _sz, _i32, ctypes.c_uint32, _vp]),
     "kda_prefill_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int]),
     "kda_prefill_default_split": (_i32, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int]),
+    "kda_prefill_plan": (ctypes.c_int, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int, _i32, _vp, _vp]),
     "kda_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _i32, _i32, _i32, _i32,
                                        ctypes.c_int, _vp, _vp]),
     "gdn_prefill": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32, _i32,
@@ -114,6 +116,18 @@ def kda_prefill_workspace_size(N, T_tot, H, d_k, d_v, dtype) -> int:
 
 def kda_prefill_default_split(N, T_tot, H, d_k, d_v, dtype) -> int:
     return int(load().kda_prefill_default_split(N, T_tot, H, d_k, d_v, dtype))
+
+
+def kda_prefill_plan(N, T_tot, H, d_k, d_v, dtype, compute_units, v_split, workspace_bytes) -> int:
+    return load().kda_prefill_plan(N, T_tot, H, d_k, d_v, dtype, compute_units, v_split, workspace_bytes)
+
+
+def prefill_plan(N, T_tot, H, d_k, d_v, dtype, compute_units: int = 0):
+    """(v_split, workspace bytes) kda_prefill picks on a device with
+    ``compute_units`` compute units (0: the current device)."""
+    v, ws = ctypes.c_int32(0), ctypes.c_size_t(0)
+    _check(kda_prefill_plan(N, T_tot, H, d_k, d_v, dtype, compute_units, ctypes.byref(v), ctypes.byref(ws)))
+    return int(v.value), int(ws.value)
 
 
 def kda_decode_step(q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype, o, stream) -> int:
@@ -196,10 +210,15 @@ def _need(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _stream_handle(stream, device) -> int:
+def _stream_of(stream, device):
+    """The torch stream a call runs on: ``stream``, or the device's current one.
+
+    The wrappers allocate every temporary (default ``cu_seqlens``, outputs,
+    workspaces) under ``torch.cuda.stream`` of this stream, so the caching
+    allocator ties those blocks to the stream the kernels run on and does
+    not hand them to other work while the kernels may still use them."""
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return int(s.cuda_stream)
+    return stream if stream is not None else torch.cuda.current_stream(device)
 
 
 def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream,
@@ -220,6 +239,16 @@ def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspac
     import torch
     if not q.is_cuda:
         raise ValueError("kda prefill runs on a GPU device; q is on the CPU")
+    dev = q.device
+    st = _stream_of(stream, dev)
+    with torch.cuda.device(dev), torch.cuda.stream(st):
+        return _prefill_on(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, st,
+                           scalar_gate, wide_decay, any_decay)
+
+
+def _prefill_on(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, st,
+                scalar_gate, wide_decay, any_decay):
+    import torch
     dev = q.device
     T, H, dk = (int(x) for x in q.shape)
     dv = int(v.shape[-1])
@@ -254,12 +283,11 @@ def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspac
             wbuf = workspace
     flags = ((KDA_PREFILL_SCALAR_GATE if scalar_gate else 0) | (KDA_PREFILL_WIDE_DECAY if wide_decay else 0)
              | (KDA_PREFILL_ANY_DECAY if any_decay else 0))
-    with torch.cuda.device(dev):
-        _check(kda_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
-                              beta.data_ptr(), S0.data_ptr() if S0 is not None else None,
-                              cu_seqlens.data_ptr(), N, T, H, dk, dv, code, o.data_ptr(),
-                              S_T.data_ptr(), wbuf.data_ptr() if wbuf is not None else None, ws,
-                              int(v_split), flags, _stream_handle(stream, dev)))
+    _check(kda_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
+                          beta.data_ptr(), S0.data_ptr() if S0 is not None else None,
+                          cu_seqlens.data_ptr(), N, T, H, dk, dv, code, o.data_ptr(),
+                          S_T.data_ptr(), wbuf.data_ptr() if wbuf is not None else None, ws,
+                          int(v_split), flags, int(st.cuda_stream)))
     return o, S_T
 
 
@@ -289,6 +317,14 @@ def _decode(q, k, v, log_alpha, beta, S, o, stream, scalar_gate: bool):
     if not q.is_cuda:
         raise ValueError("kda decode runs on a GPU device; q is on the CPU")
     dev = q.device
+    st = _stream_of(stream, dev)
+    with torch.cuda.device(dev), torch.cuda.stream(st):
+        return _decode_on(q, k, v, log_alpha, beta, S, o, st, scalar_gate)
+
+
+def _decode_on(q, k, v, log_alpha, beta, S, o, st, scalar_gate):
+    import torch
+    dev = q.device
     N, H, dk = (int(x) for x in q.shape)
     dv = int(v.shape[-1])
     code = _dtype_code(q)
@@ -302,10 +338,8 @@ def _decode(q, k, v, log_alpha, beta, S, o, stream, scalar_gate: bool):
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     _need(o, "o", (N, H, dv), q.dtype, dev)
     call = gdn_decode_step if scalar_gate else kda_decode_step
-    with torch.cuda.device(dev):
-        _check(call(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
-                               beta.data_ptr(), S.data_ptr(), N, H, dk, dv, code, o.data_ptr(),
-                               _stream_handle(stream, dev)))
+    _check(call(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
+                S.data_ptr(), N, H, dk, dv, code, o.data_ptr(), int(st.cuda_stream)))
     return o
 
 
@@ -344,6 +378,14 @@ def _backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, s
     if not q.is_cuda:
         raise ValueError("kda prefill backward runs on a GPU device; q is on the CPU")
     dev = q.device
+    st = _stream_of(stream, dev)
+    with torch.cuda.device(dev), torch.cuda.stream(st):
+        return _backward_on(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, st, scalar_gate)
+
+
+def _backward_on(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, st, scalar_gate):
+    import torch
+    dev = q.device
     T, H, dk = (int(x) for x in q.shape)
     dv = int(v.shape[-1])
     code = _dtype_code(q)
@@ -371,11 +413,9 @@ def _backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, s
     elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
     ptr = lambda t: t.data_ptr() if t is not None else None
-    with torch.cuda.device(dev):
-        call = gdn_prefill_backward if scalar_gate else kda_prefill_backward
-        _check(call(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
-                    beta.data_ptr(), ptr(S0), cu_seqlens.data_ptr(), N, T, H, dk, dv, code,
-                                    d_o.data_ptr(), ptr(d_S_T), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
-                                    gla.data_ptr(), gb.data_ptr(), gS0.data_ptr(), workspace.data_ptr(),
-                                    workspace.numel(), _stream_handle(stream, dev)))
+    call = gdn_prefill_backward if scalar_gate else kda_prefill_backward
+    _check(call(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(), ptr(S0),
+                cu_seqlens.data_ptr(), N, T, H, dk, dv, code, d_o.data_ptr(), ptr(d_S_T), gq.data_ptr(),
+                gk.data_ptr(), gv.data_ptr(), gla.data_ptr(), gb.data_ptr(), gS0.data_ptr(),
+                workspace.data_ptr(), workspace.numel(), int(st.cuda_stream)))
     return gq, gk, gv, gla, gb, gS0

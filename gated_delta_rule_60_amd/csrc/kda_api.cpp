@@ -4,11 +4,46 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstdio>
 #include <string>
 
 #include "kda_launch.hpp"
+
+namespace kda {
+
+// Compute units of the current device, queried once per device (relaxed
+// atomics: concurrent callers may both query and store the same value).
+hipError_t device_cus(int* cus) {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cus = c;
+            return hipSuccess;
+        }
+    }
+    e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (*cus < 1) *cus = 1;
+    if (dev >= 0 && dev < 64) cached[dev].store(*cus, std::memory_order_relaxed);
+    return hipSuccess;
+}
+
+int device_cus_or_default() {
+    int cus = 0;
+    if (device_cus(&cus) != hipSuccess) {
+        (void)hipGetLastError();  // the failed query must not surface as a later call's error
+        return kDefaultCUs;
+    }
+    return cus;
+}
+
+}  // namespace kda
 
 namespace {
 
@@ -38,6 +73,10 @@ kda_status hip_fail(hipError_t e, const char* what) {
 
 }  // namespace
 
+namespace kda {
+void set_last_error(const char* msg) { g_last_error = msg; }
+}  // namespace kda
+
 extern "C" {
 
 int32_t kda_version(void) { return KDA_VERSION; }
@@ -54,20 +93,38 @@ const char* kda_status_string(kda_status status) {
 
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 
+kda_status kda_prefill_plan(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                            int32_t compute_units, int32_t* v_split, size_t* workspace_bytes) {
+    g_last_error.clear();
+    if (N < 1 || H < 1 || T_tot < 0) return fail(KDA_ERR_INVALID_ARG, "need N >= 1, H >= 1 and T_tot >= 0");
+    if (compute_units < 0) return fail(KDA_ERR_INVALID_ARG, "compute_units must be >= 0");
+    if (!v_split || !workspace_bytes) return fail(KDA_ERR_INVALID_ARG, "v_split and workspace_bytes must not be NULL");
+    const kda_status ds = check_dims(d_k, d_v, dtype);
+    if (ds != KDA_OK) return ds;
+    const int cus = compute_units > 0 ? compute_units : kda::device_cus_or_default();
+    *v_split = kda::default_v_split(N, T_tot, H, d_k, d_v, dtype == KDA_DTYPE_BF16, cus);
+    *workspace_bytes = kda::prefill_workspace_bytes(N, T_tot, H, d_k, d_v, dtype == KDA_DTYPE_BF16, cus);
+    return KDA_OK;
+}
+
 size_t kda_prefill_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
                                   kda_dtype dtype) {
-    if (N < 1 || H < 1 || T_tot < 0 || !supported_dim(d_k) || !supported_dim(d_v) ||
-        (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32))
-        return 0;
-    return kda::prefill_workspace_bytes(N, T_tot, H, d_k, d_v, dtype == KDA_DTYPE_BF16);
+    int32_t split = 0;
+    size_t bytes = 0;
+    const std::string keep = g_last_error;  // a query leaves the last error text alone
+    const kda_status st = kda_prefill_plan(N, T_tot, H, d_k, d_v, dtype, 0, &split, &bytes);
+    g_last_error = keep;
+    return st == KDA_OK ? bytes : 0;
 }
 
 int32_t kda_prefill_default_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
                                   kda_dtype dtype) {
-    if (N < 1 || H < 1 || T_tot < 0 || !supported_dim(d_k) || !supported_dim(d_v) ||
-        (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32))
-        return 0;
-    return kda::default_v_split(N, T_tot, H, d_k, d_v, dtype == KDA_DTYPE_BF16);
+    int32_t split = 0;
+    size_t bytes = 0;
+    const std::string keep = g_last_error;
+    const kda_status st = kda_prefill_plan(N, T_tot, H, d_k, d_v, dtype, 0, &split, &bytes);
+    g_last_error = keep;
+    return st == KDA_OK ? split : 0;
 }
 
 size_t kda_prefill_backward_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
@@ -186,24 +243,26 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
         if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
     if (scalar_gate && log_alpha && (reinterpret_cast<uintptr_t>(log_alpha) & 3u) != 0)
         return fail(KDA_ERR_INVALID_ARG, "log_alpha must be 4-byte aligned");
-    const size_t ws_need = kda_prefill_workspace_size(N, T_tot, H, d_k, d_v, dtype);
+    const bool bf16 = dtype == KDA_DTYPE_BF16;
+    const int cus = kda::device_cus_or_default();
+    const size_t ws_need = kda::prefill_workspace_bytes(N, T_tot, H, d_k, d_v, bf16, cus);
     if (workspace_bytes < ws_need)
         return fail(KDA_ERR_INVALID_ARG, "workspace smaller than kda_prefill_workspace_size");
     if (ws_need > 0 && !workspace) return fail(KDA_ERR_INVALID_ARG, "workspace must not be NULL");
     if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
         return fail(KDA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    if (v_split == 0) v_split = kda::default_v_split(N, T_tot, H, d_k, d_v, dtype == KDA_DTYPE_BF16);
+    if (v_split == 0) v_split = kda::default_v_split(N, T_tot, H, d_k, d_v, bf16, cus);
     if (!(v_split == 1 || v_split == 2 || v_split == 4 || v_split == 8) || d_v / v_split < 16)
         return fail(KDA_ERR_INVALID_ARG, "v_split must be 1, 2, 4 or 8 with d_v / v_split >= 16");
     // Workgroups of the prefill kernel: (sequence or segment, head, value
     // slice[, identity run]); each has at most 1024 work-items.
-    const bool segmented = kda::prefill_segmented(N, T_tot, H, d_k, d_v);
-    const int64_t units = segmented ? N + T_tot / kda::kSegMinTokens : N;
+    const bool segmented = kda::prefill_segmented(N, T_tot, H, d_k, d_v, cus);
+    const int64_t units = segmented ? kda::seg_units_max(N, T_tot) : N;
     const int64_t grid = units * H * v_split * (segmented ? 2 : 1);
     if (grid > (int64_t{1} << 22)) return fail(KDA_ERR_INVALID_ARG, "N * H * v_split too large");
 
     kda::PrefillArgs a{q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
-                       dtype == KDA_DTYPE_BF16, o, S_T, v_split, stream, workspace, scalar_gate,
+                       bf16, o, S_T, v_split, stream, workspace, cus, scalar_gate,
                        (flags & KDA_PREFILL_WIDE_DECAY) != 0, (flags & KDA_PREFILL_ANY_DECAY) != 0};
     (void)hipGetLastError();  // report only this launch's status
     const hipError_t e = a.any_decay ? kda::launch_prefill_recurrent(a) : kda::launch_prefill(a);

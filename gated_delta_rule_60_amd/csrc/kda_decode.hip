@@ -19,7 +19,6 @@
 // 三.1) reads one log alpha per pair and uses it for every channel.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <type_traits>
 
 #include "kda_device.hpp"
@@ -160,28 +159,6 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_step_kernel(
         step(std::integral_constant<int, 1>{}, p + stride);
         load_state(std::integral_constant<int, 1>{}, p + 3 * stride);
     }
-}
-
-// compute units of the current device, queried once per device
-// Compute units of the current device, queried once per device (relaxed
-// atomics: concurrent callers may both query and store the same value).
-static hipError_t device_cus(int* cus) {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) {
-        const int c = cached[dev].load(std::memory_order_relaxed);
-        if (c > 0) {
-            *cus = c;
-            return hipSuccess;
-        }
-    }
-    e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    if (*cus < 1) *cus = 1;
-    if (dev >= 0 && dev < 64) cached[dev].store(*cus, std::memory_order_relaxed);
-    return hipSuccess;
 }
 
 template <bool BF16, int DK, int DV>

@@ -68,6 +68,8 @@ struct Elem<true> {
     }
     // raw global quad -> four LDS operand elements (bit copy)
     __device__ static __forceinline__ void lds_put_raw4(E* p, const R4& r) { *reinterpret_cast<uint2*>(p) = r; }
+    // four quiet-NaN elements, raw
+    __device__ static __forceinline__ R4 nan4() { return make_uint2(0x7FC07FC0u, 0x7FC07FC0u); }
     // four consecutive global elements -> floats
     __device__ static __forceinline__ void load4(const G* p, float (&x)[4]) {
         const uint2 r = *reinterpret_cast<const uint2*>(p);
@@ -105,6 +107,10 @@ struct Elem<false> {
         x[3] = r.w;
     }
     __device__ static __forceinline__ void lds_put_raw4(E* p, const R4& r) { *reinterpret_cast<float4*>(p) = r; }
+    __device__ static __forceinline__ R4 nan4() {
+        const float n = __builtin_nanf("");
+        return make_float4(n, n, n, n);
+    }
     __device__ static __forceinline__ void load4(const G* p, float (&x)[4]) {
         const float4 r = *reinterpret_cast<const float4*>(p);
         x[0] = r.x;

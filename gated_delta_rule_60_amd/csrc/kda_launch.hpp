@@ -9,7 +9,7 @@
 namespace kda {
 
 // Segmented prefill.  When a batch has too few (sequence, head) pairs to
-// fill the GPU (N * H < kSegMaxPairs), a sequence longer than its segment
+// fill the GPU (N * H below half the device's compute units), a sequence longer than its segment
 // length runs as segments (the last one shorter), each segment of each head
 // in its own workgroups, so one long sequence spreads over many CUs.  The
 // segment length depends on the sequence's own length only: about a quarter
@@ -21,7 +21,26 @@ namespace kda {
 // traffic cost more than the shorter critical path saves.
 constexpr int kSegTokens = 4096;     // longest segment
 constexpr int kSegMinTokens = 1024;  // shortest segment length a sequence is cut at
-constexpr int kSegMaxPairs = 128;
+// Compute units assumed when the current device cannot be queried (MI355X).
+constexpr int kDefaultCUs = 256;
+
+// Upper bound on the segments of a batch of N sequences of T_tot tokens in
+// all.  A sequence of len tokens is cut into P <= ceil(len / kSegMinTokens)
+// segments, and P <= 4 unless its segments are kSegTokens long, when
+// P - 1 <= floor(len / kSegTokens); summed over the sequences,
+//     sum P <= N + min(T_tot / kSegMinTokens, 3 N + T_tot / kSegTokens).
+inline int64_t seg_units_max(int32_t N, int64_t T_tot) {
+    const int64_t a = T_tot / kSegMinTokens, b = 3 * static_cast<int64_t>(N) + T_tot / kSegTokens;
+    return N + (a < b ? a : b);
+}
+
+// Sets the text kda_last_error returns on the calling thread.
+void set_last_error(const char* msg);
+
+// Compute units of the current device, queried once per device.
+hipError_t device_cus(int* cus);
+// The same, or kDefaultCUs when no device can be queried (host-side queries).
+int device_cus_or_default();
 
 // The device plan and workspace a segmented launch uses (units == nullptr:
 // whole sequences, one workgroup per (sequence, head, value slice)).
@@ -52,6 +71,7 @@ struct PrefillArgs {
     int32_t v_split;  // 1, 2, 4, 8; d_v / v_split >= 16
     void* stream;
     void* workspace;  // at least prefill_workspace_bytes(...) bytes
+    int cus = kDefaultCUs;     // compute units of the device the launch rules assume
     bool scalar_gate = false;  // log_alpha is [T_tot, H] (one gate per token and head)
     bool wide_decay = false;   // exponents of strongly decaying channels from the chunk's middle row
     bool any_decay = false;    // token-recurrent kernel: any finite log_alpha (kda_backward.hip)
@@ -95,10 +115,11 @@ hipError_t launch_prefill(const PrefillArgs& a);
 // Token-recurrent prefill for any decay range (kda_backward.hip).
 hipError_t launch_prefill_recurrent(const PrefillArgs& a);
 
-// Whether a prefill of these sizes runs segmented, and the workspace bytes it
-// then needs (0 when it does not).
-bool prefill_segmented(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v);
-size_t prefill_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16);
+// Whether a prefill of these sizes runs segmented on a device with `cus`
+// compute units, and the workspace bytes it then needs (0 when it does not).
+bool prefill_segmented(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, int cus);
+size_t prefill_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16,
+                               int cus);
 // Segmented prefill passes around the prefill kernel (kda_segment.hip): the
 // plan (before it) and the state chain plus output correction (after it).
 hipError_t launch_seg_plan(const PrefillArgs& a, SegView* view);
@@ -109,7 +130,8 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill_bwd(const BackwardArgs& a);
 size_t prefill_bwd_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v);
 
-// Launch shape kda_prefill picks for these sizes (see kda_prefill.hip).
-int32_t default_v_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16);
+// Launch shape kda_prefill picks for these sizes on a device with `cus`
+// compute units (see kda_prefill.hip).
+int32_t default_v_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16, int cus);
 
 }  // namespace kda

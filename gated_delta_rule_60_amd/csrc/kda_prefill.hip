@@ -75,7 +75,6 @@ constexpr size_t align16(size_t x) { return (x + 15) & ~static_cast<size_t>(15);
 // this many sequences; larger batches run in natural order.
 constexpr int kSortMax = 64;
 constexpr size_t kLdsBudget = 160 * 1024;
-constexpr int64_t kHalfCUs = 128;  // half of MI355X's 256 compute units
 // Wide-decay variant: a channel whose decay over one chunk is below
 // -kRefSwitchLog2 (log2 units, about e^-69) takes its exponents relative to
 // the chunk's middle row.
@@ -426,9 +425,13 @@ __device__ __forceinline__ void ctr_signal(int* ctr, int lane) {
 //
 // Every wait is bounded: a wait that has not been satisfied after kSpinMax
 // sleeps (far beyond any legitimate hand-off) marks the workgroup as failed
-// in *fault and returns, so the kernel always drains; the consumers then
-// write NaN final states, which no caller can mistake for a result.
+// in *fault and returns, so the kernel always drains.  Once the flag is set,
+// every later wait of the workgroup gives up within kFaultPoll sleeps
+// instead of its own full bound; the consumers then write NaN final states
+// and the producers store NaN outputs from then on, so a failed workgroup
+// cannot return a plausible result.
 constexpr int kSpinMax = 1 << 24;
+constexpr int kFaultPoll = 64;  // sleeps between two reads of the fault flag
 
 __device__ __forceinline__ void ctr_publish(int* ctr, int value, int lane) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -439,7 +442,9 @@ __device__ __forceinline__ void ctr_publish(int* ctr, int value, int lane) {
 __device__ __forceinline__ void ctr_wait(int* ctr, int target, int* fault) {
     int spins = 0;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
-        if (++spins > kSpinMax) {
+        ++spins;
+        if (spins > kSpinMax ||
+            (spins % kFaultPoll == 0 && __hip_atomic_load(fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0)) {
             __hip_atomic_store(fault, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             break;
         }
@@ -1158,6 +1163,9 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             const int c0 = t_beg + j * C;
             const int len = __builtin_amdgcn_readfirstlane(chunk_len(j));
             const auto r = buffer_rsrc(ohp + static_cast<size_t>(c0) * strideV, len * rowV);
+            // after a failed hand-off in this workgroup: NaN rows instead
+            const bool failed =
+                __builtin_amdgcn_readfirstlane(__hip_atomic_load(fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0;
 #pragma unroll
             for (int vv = 0; vv < VPT; ++vv) {
                 const int idx = vlane + 64 * NPS * vv;
@@ -1168,6 +1176,10 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
 #pragma unroll
                 for (int c = 0; c < 4; ++c) q4[c] = lds_get_raw4<BF16>(tile_at<BF16>(tVt(S), vt_off<BF16, UT>(c4 + c, r0 / 4)));
                 transpose4<BF16>(q4, rows);
+                if (failed) {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) rows[rr] = T::nan4();
+                }
                 const int off = ok ? r0 * rowV + c4 * GS : kNoAccess;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) buf_store_raw4<BF16>(r, off, rr * rowV, rows[rr]);
@@ -1258,7 +1270,7 @@ static hipError_t launch_prefill_dt(const PrefillArgs& a, const SegView& seg) {
 
 hipError_t launch_prefill(const PrefillArgs& a) {
     SegView seg{};
-    const bool segmented = prefill_segmented(a.N, a.T_tot, a.H, a.d_k, a.d_v);
+    const bool segmented = prefill_segmented(a.N, a.T_tot, a.H, a.d_k, a.d_v, a.cus);
     if (segmented) {
         if (a.workspace == nullptr) return hipErrorInvalidValue;
         const hipError_t e = launch_seg_plan(a, &seg);
@@ -1269,10 +1281,10 @@ hipError_t launch_prefill(const PrefillArgs& a) {
     return launch_seg_fixup(a, seg);
 }
 
-int32_t default_v_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16) {
+int32_t default_v_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16, int cus) {
     (void)bf16;
-    // Segmented runs: one unit per segment (bounded by N + T_tot / kSegMinTokens).
-    const int64_t seqs = prefill_segmented(N, T_tot, H, d_k, d_v) ? N + T_tot / kSegMinTokens : N;
+    // Segmented runs: one unit per segment (at most seg_units_max of them).
+    const int64_t seqs = prefill_segmented(N, T_tot, H, d_k, d_v, cus) ? seg_units_max(N, T_tot) : N;
     const int64_t units = seqs * H;
     // The chunk period of a workgroup barely depends on how many value
     // columns it carries, so extra workgroups do not shorten a sequence's
@@ -1283,7 +1295,7 @@ int32_t default_v_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_
     // not at full occupancy.  So 128 value columns split in two only when
     // the launch then fills at most half of the CUs; every split gives the
     // same bits.
-    if (d_v == 128 && units * 2 <= kHalfCUs) return 2;
+    if (d_v == 128 && units * 2 <= cus / 2) return 2;
     return 1;
 }
 

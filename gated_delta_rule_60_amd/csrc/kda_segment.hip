@@ -44,7 +44,7 @@ struct SegLayout {
 // Workspace: {count, nlong} | units [umax] | longs [lmax] | q^ | M | D
 SegLayout seg_layout(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16) {
     SegLayout L{};
-    const int64_t full = T_tot / kSegMinTokens;  // segments beyond one per sequence, at most
+    const int64_t full = seg_units_max(N, T_tot) - N;  // segments beyond one per sequence, at most
     L.umax = static_cast<int>(N + full);
     L.lmax = static_cast<int>(full < N ? (full > 0 ? full : 1) : N);
     const size_t es = bf16 ? 2 : 4;
@@ -437,12 +437,16 @@ __global__ __launch_bounds__(kFixThreads) void seg_out_kernel(const int4* __rest
 
 }  // namespace
 
-bool prefill_segmented(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v) {
-    return d_k == d_v && T_tot > kSegMinTokens && static_cast<int64_t>(N) * H < kSegMaxPairs;
+// Segments pay only while the (sequence, head) pairs fill less than half of
+// the compute units: with more, the identity runs' extra work and the
+// fix-up traffic cost more than the shorter critical path saves.
+bool prefill_segmented(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, int cus) {
+    return d_k == d_v && T_tot > kSegMinTokens && 2 * static_cast<int64_t>(N) * H < cus;
 }
 
-size_t prefill_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16) {
-    if (!prefill_segmented(N, T_tot, H, d_k, d_v)) return 0;
+size_t prefill_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16,
+                               int cus) {
+    if (!prefill_segmented(N, T_tot, H, d_k, d_v, cus)) return 0;
     return seg_layout(N, T_tot, H, d_k, d_v, bf16).bytes;
 }
 

@@ -27,8 +27,9 @@
  *    Floating-point pointers must be 16-byte aligned.
  *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *    NULL is the default stream) and never synchronises.  Arguments are
- *    validated on the host before any HIP call; a kernel fault surfaces at
- *    the caller's next synchronisation.
+ *    validated on the host before any kernel is launched (the only HIP
+ *    calls before that are queries of the current device's compute-unit
+ *    count); a kernel fault surfaces at the caller's next synchronisation.
  *  - Results are deterministic: the same inputs give the same bits.
  *  - Numerical contract: log_alpha finite and <= 0 with the sum of log_alpha
  *    over any 32 consecutive tokens of a sequence >= -80 per channel (the
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 3
+#define KDA_VERSION 4
 
 typedef enum {
     KDA_OK = 0,
@@ -91,7 +92,8 @@ typedef enum {
  * q, k, v, log_alpha, beta and o may be NULL when T_tot == 0.  No state
  * crosses a sequence boundary.
  *
- * Long sequences.  When d_k == d_v, T_tot > 1024 and N * H < 128 (too few
+ * Long sequences.  When d_k == d_v, T_tot > 1024 and 2 N H is below the
+ * current device's compute-unit count (256 on MI355X: N H < 128; too few
  * (sequence, head) pairs to fill the GPU), a sequence longer than its
  * segment length runs as segments (the last one shorter) that are processed
  * in parallel.  A sequence of len tokens has segments of about len / 4
@@ -165,18 +167,39 @@ kda_status kda_prefill_ex(const void* q, const void* k, const void* v,
                           void* workspace, size_t workspace_bytes, int32_t v_split,
                           uint32_t flags, void* stream);
 
-/* Bytes of workspace kda_prefill needs for these sizes: 0 unless the batch
- * runs segmented (d_k == d_v, T_tot > 1024, N * H < 128); then the segment
- * plan, the identity runs' outputs ([T_tot, H, d_k] in dtype) and two fp32
- * [d_k, d_v] states per (segment, head) for at most N + T_tot / 1024
- * segments.  0 for unsupported sizes. */
+/* Bytes of workspace kda_prefill needs for these sizes on the current
+ * device: 0 unless the batch runs segmented (d_k == d_v, T_tot > 1024,
+ * 2 N H below the device's compute units); then the segment plan, the
+ * identity runs' outputs ([T_tot, H, d_k] in dtype) and two fp32 [d_k, d_v]
+ * states per (segment, head) for at most
+ * N + min(T_tot / 1024, 3 N + T_tot / 4096) segments (integer division).
+ * 0 for unsupported sizes.  Where no device can be queried the answer is
+ * the one for 256 compute units (MI355X). */
 size_t kda_prefill_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
                                   int32_t d_v, kda_dtype dtype);
 
-/* The v_split kda_prefill would use for these sizes (1, 2, 4 or 8), or 0 if
- * the sizes are not supported. */
+/* The v_split kda_prefill would use for these sizes on the current device
+ * (1, 2, 4 or 8), or 0 if the sizes are not supported; 256 compute units
+ * where no device can be queried. */
 int32_t kda_prefill_default_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
                                   int32_t d_v, kda_dtype dtype);
+
+/*
+ * kda_prefill_plan -- the launch shape and workspace kda_prefill picks for
+ * these sizes on a device with `compute_units` compute units (0: the
+ * current device, or 256 where none can be queried).  Writes *v_split
+ * (1, 2, 4 or 8) and *workspace_bytes (as kda_prefill_workspace_size).
+ * The rules: a batch runs segmented when d_k == d_v, T_tot > 1024 and
+ * 2 N H < compute_units; 128 value columns are split over two workgroups
+ * when the launch's units (sequences, or at most the segment bound above
+ * when segmented) times H times 2 fill at most half of the compute units;
+ * otherwise v_split is 1.  KDA_ERR_INVALID_ARG for N < 1, H < 1, T_tot < 0,
+ * compute_units < 0 or NULL outputs; KDA_ERR_UNSUPPORTED for unsupported
+ * head dimensions or dtypes.  No kernel is launched.
+ */
+kda_status kda_prefill_plan(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
+                            kda_dtype dtype, int32_t compute_units, int32_t* v_split,
+                            size_t* workspace_bytes);
 
 /*
  * kda_decode_step -- one token for each of N independent sequences (the same

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.kda_version() == 3
+    assert kda.kda_version() == 4
     for s in (0, 1, 2, 3):
         assert kda.kda_status_string(s).startswith("KDA_")
     assert "unknown" in kda.kda_status_string(99)
@@ -143,10 +143,12 @@ def test_workspace_and_default_split_queries():
     assert kda.kda_prefill_workspace_size(3, 32677, 42, 128, 128, BF16) > 0   # 126 pairs
     assert kda.kda_prefill_workspace_size(4, 32677, 32, 128, 128, BF16) == 0  # 128 pairs
     ws = kda.kda_prefill_workspace_size(1, 131072, 32, 128, 128, BF16)
-    # at least the identity runs' outputs and M, D for N + T_tot // 1024 segments
-    segs = 1 + 131072 // 1024
-    assert ws >= 131072 * 32 * 128 * 2 + 2 * segs * 32 * 128 * 128 * 4
-    assert ws < 2 * (131072 * 32 * 128 * 2 + 2 * segs * 32 * 128 * 128 * 4)
+    # the identity runs' outputs and M, D for N + min(T_tot // 1024, 3 N + T_tot // 4096)
+    # segments (36 here; 32 are used), plus the plan
+    segs = 1 + min(131072 // 1024, 3 + 131072 // 4096)
+    assert segs == 36
+    body = 131072 * 32 * 128 * 2 + 2 * segs * 32 * 128 * 128 * 4
+    assert body <= ws <= body + 4096
     assert kda.kda_prefill_workspace_size(1, 131072, 32, 128, 128, F32) > ws
     assert kda.kda_prefill_workspace_size(2, 131072, 32, 128, 128, BF16) > ws
     assert kda.kda_prefill_workspace_size(0, 32677, 32, 128, 128, BF16) == 0
@@ -155,6 +157,50 @@ def test_workspace_and_default_split_queries():
         assert s in (1, 2, 4, 8)
     assert kda.kda_prefill_default_split(1, 10, 1, 48, 128, BF16) == 0
     assert kda.kda_prefill_default_split(1, 10, 1, 32, 32, BF16) in (1, 2)
+
+
+def _plan(N, T, H, d, cus, dtype=BF16):
+    return kda.prefill_plan(N, T, H, d, d, dtype, compute_units=cus)
+
+
+def test_prefill_plan_follows_the_compute_unit_count():
+    # 256 compute units (MI355X): segments while 2 N H < 256; 128 columns split in two
+    # while units * H * 2 <= 128, counting segments at their bound when segmented
+    v, ws = _plan(1, 4096, 32, 128, 256)  # 5 units at most: 320 > 128
+    assert (v, ws > 0) == (1, True)
+    assert _plan(8, 32677, 32, 128, 256) == (1, 0)  # 256 pairs fill the device
+    assert _plan(1, 1000, 32, 128, 256) == (2, 0)  # 64 <= 128, too short to segment
+    assert _plan(2, 1000, 16, 128, 256) == (2, 0)
+    assert _plan(4, 32677, 32, 128, 256) == (1, 0)  # 128 pairs: not segmented
+    assert _plan(3, 32677, 42, 128, 256)[1] > 0  # 126 pairs: segmented
+    # 32 compute units: the same sizes cross the rules at an eighth of the pairs
+    assert _plan(1, 4096, 32, 128, 32) == (1, 0)  # 2 * 32 >= 32: one pass
+    v, ws = _plan(1, 4096, 8, 128, 32)  # 16 < 32: segmented
+    assert (v, ws > 0) == (1, True)
+    assert _plan(1, 1000, 4, 128, 32) == (2, 0)  # 8 <= 16
+    assert _plan(1, 1000, 32, 128, 32) == (1, 0)  # 64 > 16
+    # 64 value columns never split; the workspace does not depend on the dtype's split
+    assert _plan(1, 1000, 1, 64, 256) == (1, 0)
+    # compute_units = 0 is the current device (here: none, so 256), as the two queries use
+    for N, T, H in ((1, 4096, 32), (8, 32677, 32), (1, 1000, 32)):
+        v, ws = _plan(N, T, H, 128, 0)
+        assert v == kda.kda_prefill_default_split(N, T, H, 128, 128, BF16)
+        assert ws == kda.kda_prefill_workspace_size(N, T, H, 128, 128, BF16)
+        assert (v, ws) == _plan(N, T, H, 128, 256)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 10, 1, 128, 128, BF16, 256), kda.KDA_ERR_INVALID_ARG),
+    ((1, 10, 1, 128, 128, BF16, -1), kda.KDA_ERR_INVALID_ARG),
+    ((1, 10, 1, 48, 128, BF16, 256), kda.KDA_ERR_UNSUPPORTED),
+    ((1, 10, 1, 128, 128, 9, 256), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_prefill_plan_validation(args, status):
+    import ctypes
+    v, ws = ctypes.c_int32(0), ctypes.c_size_t(0)
+    assert kda.kda_prefill_plan(*args, ctypes.byref(v), ctypes.byref(ws)) == status
+    assert kda.kda_last_error() != ""
+    assert kda.kda_prefill_plan(1, 10, 1, 128, 128, BF16, 256, None, ctypes.byref(ws)) == kda.KDA_ERR_INVALID_ARG
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

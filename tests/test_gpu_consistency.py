@@ -157,3 +157,39 @@ def test_repeated_long_runs_are_bit_identical(split):
     for rep in range(6):
         o, S = kda.prefill(**d, v_split=split)
         assert torch.equal(o, o0) and torch.equal(S, S0), f"v_split={split} rep={rep}"
+
+
+@pytest.mark.parametrize("lengths", [[300, 77], [5000]], ids=["one_pass", "segmented"])
+def test_side_stream_gives_the_same_bits(lengths):
+    """Prefill (one pass, and segmented with its workspace and default
+    cu_seqlens allocated by the binding), backward and decode on a
+    non-current stream give the default stream's bits."""
+    import torch
+    x = _x(lengths)
+    d = upload(x)
+    dO, dST = inputs.make_backward_grads(x, seed=5)
+    gO, gST = torch.from_numpy(dO).cuda().to(torch.bfloat16), torch.from_numpy(dST).cuda()
+    single = len(lengths) == 1
+    pd = dict(d, cu_seqlens=None) if single else d
+    o0, S0 = kda.prefill(**pd)
+    g0 = kda.prefill_backward(**d, d_o=gO, d_S_T=gST)
+    Sd0 = d["S0"].clone()
+    od0 = kda.decode_step(d["q"][:1].expand(x.N, -1, -1).contiguous(), d["k"][:1].expand(x.N, -1, -1).contiguous(),
+                          d["v"][:1].expand(x.N, -1, -1).contiguous(),
+                          d["log_alpha"][:1].expand(x.N, -1, -1).contiguous(),
+                          d["beta"][:1].expand(x.N, -1).contiguous(), Sd0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    dec_in = [t[:1].expand(x.N, *t.shape[1:]).contiguous() for t in (d["q"], d["k"], d["v"], d["log_alpha"])]
+    b1 = d["beta"][:1].expand(x.N, -1).contiguous()
+    for rep in range(3):
+        Sd = d["S0"].clone()  # on the current stream; the side stream waits for it
+        side.wait_stream(torch.cuda.current_stream())
+        o1, S1 = kda.prefill(**pd, stream=side)
+        g1 = kda.prefill_backward(**d, d_o=gO, d_S_T=gST, stream=side)
+        od1 = kda.decode_step(*dec_in, b1, Sd, stream=side)
+        side.synchronize()
+        assert torch.equal(o1, o0) and torch.equal(S1, S0), f"prefill rep {rep}"
+        for a, b in zip(g1, g0):
+            assert torch.equal(a, b), f"backward rep {rep}"
+        assert torch.equal(od1, od0) and torch.equal(Sd, Sd0), f"decode rep {rep}"
