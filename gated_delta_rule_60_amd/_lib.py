@@ -23,6 +23,7 @@ KDA_DTYPE_F32 = 1
 KDA_PREFILL_SCALAR_GATE = 1
 KDA_PREFILL_WIDE_DECAY = 2
 KDA_PREFILL_ANY_DECAY = 4
+KDA_PREFILL_NOALLOC_WORKSPACE_BYTES = 64 << 20  # include/kda.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -55,6 +56,8 @@ SIGNATURES = {
     "gdn_prefill_backward": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32,
                                             _i32, ctypes.c_int, _vp, _fp, _fp, _fp, _fp, _fp, _fp, _fp,
                                             _vp, _sz, _vp]),
+    "kda_prefill_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32, _i32,
+                                           ctypes.c_int, _vp, _fp, _vp]),
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_last_error": (ctypes.c_char_p, []),
     "kda_version": (_i32, []),
@@ -148,6 +151,12 @@ def gdn_prefill_split(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k
 
 def gdn_decode_step(q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype, o, stream) -> int:
     return load().gdn_decode_step(q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype, o, stream)
+
+
+def kda_prefill_noalloc(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, o, S_T,
+                        stream) -> int:
+    return load().kda_prefill_noalloc(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype,
+                                      o, S_T, stream)
 
 
 def kda_status_string(status: int) -> str:

@@ -314,6 +314,34 @@ kda_status gdn_prefill_backward(const void* q, const void* k, const void* v,
 size_t kda_prefill_backward_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
                                            int32_t d_v, kda_dtype dtype);
 
+/*
+ * kda_prefill_noalloc -- kda_prefill for callers that cannot allocate device
+ * memory: code under HIP stream capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Arguments as kda_prefill without the workspace; results
+ * are bit-identical to kda_prefill's.  The segmented path's workspace comes
+ * from a fixed device array of KDA_PREFILL_NOALLOC_WORKSPACE_BYTES bytes
+ * that the library holds on each device it runs on until the process ends
+ * (its address is looked up on the first call made with that device
+ * current).  This call allocates nothing.
+ *
+ * Limit: sizes whose kda_prefill_workspace_size exceeds the fixed workspace
+ * (for example one 128k-token sequence at H = 32, d = 128) return
+ * KDA_ERR_INVALID_ARG before any launch; a batch that runs in one pass
+ * needs no workspace and has no such limit.  The 4096-token sequence at
+ * H = 32, d = 128, bf16 needs about 52 MiB and fits.
+ *
+ * Every call on one device shares that device's array, which keeps the
+ * last call's contents (each call writes every part it reads before
+ * reading it).  Calls that overlap on one device (on different streams, or
+ * from different threads without ordering) race on it: order them.
+ */
+#define KDA_PREFILL_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+kda_status kda_prefill_noalloc(const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, const float* S0,
+                               const int32_t* cu_seqlens, int32_t N, int64_t T_tot, int32_t H,
+                               int32_t d_k, int32_t d_v, kda_dtype dtype, void* o, float* S_T,
+                               void* stream);
+
 /* Static text for a status code. */
 const char* kda_status_string(kda_status status);
 
