@@ -10,10 +10,14 @@ the same run.  Inputs are seeded synthetic data already resident in HBM.
 
 Prints ONE JSON line.  ``value`` is prefill tokens/s; ``roofline`` is the
 prefill kernel against HBM bandwidth (algorithmic bytes / measured kernel
-time); ``decode`` holds the decode step's microseconds and its own roofline;
-``gdn`` the same prefill with one gate per token and head (Gated DeltaNet);
-``backward`` the backward pass (kda_prefill_backward) over the same batch
-against the fp32 vector ALU peak;
+time); ``mfma`` the same launch against the bf16 MFMA peak (algorithmic
+flops, and the busy-cycle counter of the committed profile when it matches
+the kernel source); ``decode`` holds the decode step's microseconds and its
+own roofline; ``configs`` the other prefill workloads (the 256-token fp32
+case, the 4096-token and the 131,072-token sequences), each with its
+median and minimum launch time, roofline and oracle baseline; ``gdn`` the
+same prefill with one gate per token and head (Gated DeltaNet);
+``backward`` the backward pass (kda_prefill_backward) over the same batch;
 ``cpu_baseline`` is the fp64 oracle on a bounded sample of the same
 workload, timed on this host's cores.
 """
@@ -32,9 +36,22 @@ METRIC = "KDA prefill tokens/s (T=32k,H=32,d=128) + decode step µs; % of roofli
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (published; counts packed fp32 FMA)
-# chunk length of the prefill kernel for bf16 inputs at d_k = 128 (32 tokens;
-# 16 where a 32-token chunk's LDS tiles exceed the 160 KB of one CU)
+# Chunk length of the prefill kernel: 32 tokens, 16 for fp32 inputs at
+# d_k = 128 (there a 32-token chunk's LDS tiles exceed the 160 KB of one CU).
 CHUNK = 32
+
+
+def chunk_len(dtype: str, dk: int) -> int:
+    return 16 if dtype == "f32" and dk == 128 else 32
+
+
+# The prefill workloads reported beside the headline one (each is also a
+# parity-test case): name -> what it is.
+SUB_WORKLOADS = {
+    "prefill_t256_h2_d32_f32": "one 256-token sequence, H = 2, d = 32, fp32 (latency-bound)",
+    "prefill_t4096_h32_d128_bf16": "one 4096-token sequence, H = 32, d = 128, bf16 (runs segmented)",
+    "prefill_t131072_h32_d128_bf16": "one 131,072-token sequence, H = 32, d = 128, bf16 (runs segmented)",
+}
 
 
 def prefill_bytes(T_tot: int, N: int, H: int, dk: int, dv: int, esize: int,
@@ -47,11 +64,16 @@ def prefill_bytes(T_tot: int, N: int, H: int, dk: int, dv: int, esize: int,
     return per_token_head * T_tot * H + 2 * 4 * dk * dv * N * H
 
 
-def prefill_flops(T_tot: int, H: int, dk: int, dv: int, C: int = CHUNK) -> int:
+def prefill_flops_per_token_head(dk: int, dv: int, C: int = CHUNK) -> int:
     """Useful MFMA flops of the chunk form per token-head, triangles counted at
     half: Gram products beta K~ K^T and Q~ K^T (2 C d_k), U = T R and A_qk U
-    (2 C d_v), K~ S, Q~ S and Kbar^T U (6 d_k d_v)."""
-    return (2 * C * dk + 2 * C * dv + 6 * dk * dv) * T_tot * H
+    (2 C d_v), K~ S, Q~ S and Kbar^T U (6 d_k d_v).  114,688 at C = 32,
+    d = 128."""
+    return 2 * C * dk + 2 * C * dv + 6 * dk * dv
+
+
+def prefill_flops(T_tot: int, H: int, dk: int, dv: int, C: int = CHUNK) -> int:
+    return prefill_flops_per_token_head(dk, dv, C) * T_tot * H
 
 
 def decode_bytes(N: int, H: int, dk: int, dv: int, esize: int) -> int:
@@ -101,6 +123,28 @@ def measured_traffic(kernel: str, workload: str, sources):
     return int(m_bytes.group(1)) if h.hexdigest() == m_hash.group(1) else None
 
 
+def measured_mfma_busy(kernel: str, workload: str, sources):
+    """MFMA busy fraction of the committed rocprofv3 counter summary of this
+    kernel and workload (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x CUs x
+    4 SIMDs), or None when the kernel sources changed since it was taken."""
+    import hashlib
+    import re
+
+    path = os.path.join(_PROFILES, f"{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_busy = re.search(r"mfma busy fraction: ([0-9.eE+-]+)", text)
+    m_hash = re.search(r"kernel source sha256 \([^)]*\): ([0-9a-f]{64})", text)
+    if not (m_busy and m_hash):
+        return None
+    h = hashlib.sha256()
+    for s in sources:
+        with open(os.path.join(_CSRC, s), "rb") as f:
+            h.update(f.read())
+    return float(m_busy.group(1)) if h.hexdigest() == m_hash.group(1) else None
+
+
 def cpu_baseline(x, seconds: float):
     """Time the fp64 oracle on the benchmark workload, a batch of heads at a
     time (all sequences of each head), until ``seconds`` of wall time have
@@ -111,7 +155,7 @@ def cpu_baseline(x, seconds: float):
 
     threads = oracle.default_threads()
     H = x.H
-    per_batch = max(1, min(H, (2 * threads + x.N - 1) // x.N))
+    per_batch = max(1, min(H, (threads + x.N - 1) // x.N))  # about one (sequence, head) pair per thread
     done, t0 = 0, time.perf_counter()
     while done < H:
         heads = list(range(done, min(H, done + per_batch)))
@@ -138,6 +182,36 @@ def cpu_baseline(x, seconds: float):
                       f"({x.T_tot * done} token-heads) in {dt:.1f} s on {threads} threads; "
                       f"scaled to all heads",
             "cpu": cpu}
+
+
+def decode_cpu_baseline(seconds: float, n_sample: int = 32):
+    """The fp64 oracle's decode step on the first ``n_sample`` of the 256
+    sequences (all 32 heads, d = 128), stepped until ``seconds`` have passed;
+    scaled to microseconds per step for all 256 sequences."""
+    import numpy as np
+
+    import oracle
+    from gated_delta_rule_60_amd import inputs
+
+    w = inputs.WORKLOADS["decode_n256_h32_d128_bf16_x1000"]
+    N, H, dk, dv = w["N"], w["H"], w["d_k"], w["d_v"]
+    threads = oracle.default_threads()
+    S = np.ascontiguousarray(inputs.decode_initial_state(N, H, dk, dv, seed=w["seed"],
+                                                         s0_std=w["s0_std"])[:n_sample].astype(np.float64))
+    steps, dt = 0, 0.0
+    while steps < 40 and dt < seconds:
+        si = inputs.decode_step_inputs(N, H, dk, dv, steps, seed=w["seed"], dtype=w["dtype"],
+                                       log_alpha_range=w["log_alpha_range"])
+        t0 = time.perf_counter()
+        oracle.decode_step(si.q[:n_sample], si.k[:n_sample], si.v[:n_sample], si.log_alpha[:n_sample],
+                           si.beta[:n_sample], S, nthreads=threads)
+        dt += time.perf_counter() - t0
+        steps += 1
+    us = dt / steps * 1e6 * (N / n_sample)
+    return {"value": us, "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle decode step on {n_sample} of {N} sequences x {H} heads, {steps} steps "
+                      f"taking {dt:.1f} s (input generation not counted) on {threads} threads; "
+                      f"scaled to all {N}"}
 
 
 def bench_prefill(kda, torch, x, steps: int, warmup: int, v_split: int, scalar_gate: bool = False):
@@ -178,6 +252,77 @@ def bench_prefill(kda, torch, x, steps: int, warmup: int, v_split: int, scalar_g
     wall = time.perf_counter() - t0
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
     return wall, kernel_ms
+
+
+def bench_prefill_flushed(kda, torch, x, steps: int, warmup: int, flush_bytes: int):
+    """Event-timed kda_prefill launches on one resident input set; before
+    each launch a ``flush_bytes`` buffer is overwritten (outside the timed
+    region) so that no input is left in the 256 MB MALL or the L2s from the
+    previous launch.  Returns the per-launch milliseconds."""
+    dev = torch.device("cuda:0")
+    td = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    up = lambda a, dt=torch.float32: torch.from_numpy(a).to(dev).to(dt)
+    d = dict(q=up(x.q, td), k=up(x.k, td), v=up(x.v, td), log_alpha=up(x.log_alpha), beta=up(x.beta),
+             S0=None if x.S0 is None else up(x.S0), cu_seqlens=torch.from_numpy(x.cu_seqlens).to(dev))
+    d["o"] = torch.empty((x.T_tot, x.H, x.d_v), dtype=td, device=dev)
+    d["S_T"] = torch.empty((x.N, x.H, x.d_k, x.d_v), dtype=torch.float32, device=dev)
+    code = 0 if x.dtype == "bf16" else 1
+    ws = kda.kda_prefill_workspace_size(x.N, x.T_tot, x.H, x.d_k, x.d_v, code)
+    if ws:
+        d["workspace"] = torch.empty(ws, dtype=torch.uint8, device=dev)
+    flush = torch.empty(max(flush_bytes, 4) // 4, dtype=torch.float32, device=dev) if flush_bytes else None
+    for _ in range(warmup):
+        kda.prefill(**d)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(float(i))
+        ev[i][0].record(stream)
+        kda.prefill(**d)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    del d, flush
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def sub_workload_line(kda, torch, name: str, steps: int, warmup: int, cpu_seconds: float):
+    """One reported prefill workload: launch times (median, min), tokens/s,
+    HBM and MFMA rooflines against algorithmic bytes and flops, measured
+    traffic when a matching profile is committed, and the oracle baseline."""
+    from gated_delta_rule_60_amd import inputs
+
+    x = inputs.make_workload(name)
+    esize = 2 if x.dtype == "bf16" else 4
+    nbytes = prefill_bytes(x.T_tot, x.N, x.H, x.d_k, x.d_v, esize)
+    flush = 512 << 20 if nbytes < (1 << 30) else 0
+    ms = sorted(bench_prefill_flushed(kda, torch, x, steps, warmup, flush))
+    med = ms[len(ms) // 2]
+    C = chunk_len(x.dtype, x.d_k)
+    fl = prefill_flops(x.T_tot, x.H, x.d_k, x.d_v, C)
+    code = 0 if x.dtype == "bf16" else 1
+    v_split, ws = kda.prefill_plan(x.N, x.T_tot, x.H, x.d_k, x.d_v, code)
+    peak_mfma = BF16_MFMA_PEAK_TFLOPS if x.dtype == "bf16" else FP32_VALU_PEAK_TFLOPS
+    out = {
+        "what": SUB_WORKLOADS[name], "dtype": x.dtype, "T_tot": x.T_tot, "H": x.H, "d_k": x.d_k, "d_v": x.d_v,
+        "chunk": C, "v_split": v_split, "segmented": ws > 0, "launches": len(ms),
+        "ms_median": med, "ms_min": ms[0], "tokens_per_s": x.T_tot / (med * 1e-3),
+        "timing": "hip events around each kda_prefill call (every kernel of the call); "
+                  + (f"a {flush >> 20} MiB buffer overwritten before each launch" if flush else "no flush needed"),
+        "roofline": {"bound": "hbm", "achieved": nbytes / (med * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("prefill_call", name, ["kda_prefill.hip", "kda_segment.hip",
+                                                                         "kda_device.hpp"]),
+                     "alg_bytes_per_launch": nbytes},
+        "mfma": {"alg_flops_per_launch": fl, "flops_per_token_head": prefill_flops_per_token_head(x.d_k, x.d_v, C),
+                 "achieved_tflops": fl / (med * 1e-3) / 1e12, "peak_tflops": peak_mfma,
+                 "frac": fl / (med * 1e-3) / 1e12 / peak_mfma},
+    }
+    if cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(x, cpu_seconds)
+    del x
+    return out
 
 
 def bench_backward(kda, torch, x, steps: int, warmup: int):
@@ -279,6 +424,10 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass line")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other prefill workloads (256-token fp32, 4096- and 131,072-token sequences)")
+    ap.add_argument("--config-steps", type=int, default=20)
+    ap.add_argument("--config-cpu-seconds", type=float, default=4.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", type=float, default=0.0,
                     help="only run a plain copy of this many GiB (HBM counter calibration)")
@@ -305,8 +454,10 @@ def main():
     wall, kms = bench_prefill(kda, torch, x, args.steps, args.warmup, split)
     ms_per_step = wall * 1e3 / args.steps
     k_avg_ms = sum(kms) / len(kms)
+    k_sorted = sorted(kms)
+    C = chunk_len(x.dtype, x.d_k)
     nbytes = prefill_bytes(x.T_tot, x.N, x.H, x.d_k, x.d_v, esize)
-    nflops = prefill_flops(x.T_tot, x.H, x.d_k, x.d_v)
+    nflops = prefill_flops(x.T_tot, x.H, x.d_k, x.d_v, C)
     achieved = nbytes / (k_avg_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -322,18 +473,24 @@ def main():
         "dtype": x.dtype,
         "data": "synthetic (seeded; inputs resident in HBM)",
         "config": {"workload": args.workload, "sequences": x.N, "T_tot": x.T_tot, "H": x.H,
-                   "d_k": x.d_k, "d_v": x.d_v, "chunk": CHUNK, "v_split": split,
+                   "d_k": x.d_k, "d_v": x.d_v, "chunk": C, "v_split": split,
                    "lengths": [int(b - a) for a, b in zip(x.cu_seqlens[:-1], x.cu_seqlens[1:])]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic("prefill_kernel", args.workload,
                                                  ["kda_prefill.hip", "kda_device.hpp"]),
                      "kernel": "kda::prefill_kernel", "kernel_ms_avg": k_avg_ms,
-                     "kernel_ms_min": min(kms), "alg_bytes_per_launch": nbytes},
-        "mfma": {"alg_flops_per_launch": nflops,
+                     "kernel_ms_median": k_sorted[len(k_sorted) // 2],
+                     "kernel_ms_min": k_sorted[0], "alg_bytes_per_launch": nbytes},
+        "mfma": {"alg_flops_per_launch": nflops, "chunk": C,
+                 "flops_per_token_head": prefill_flops_per_token_head(x.d_k, x.d_v, C),
                  "achieved_tflops": nflops / (k_avg_ms * 1e-3) / 1e12,
                  "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
-                 "frac": nflops / (k_avg_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+                 "frac": nflops / (k_avg_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                 "counter_busy_frac": measured_mfma_busy("prefill_kernel", args.workload,
+                                                         ["kda_prefill.hip", "kda_device.hpp"]),
+                 "counter": "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs), "
+                            "from the committed rocprofv3 summary; null when the kernel changed since"},
     }
     if not args.no_decode:
         d = bench_decode(kda, torch, args.decode_steps, 10, args.decode_inputs)
@@ -351,6 +508,8 @@ def main():
                                                      ["kda_decode.hip", "kda_device.hpp"]),
                          "kernel": "kda::decode_step_kernel", "alg_bytes_per_launch": db},
         }
+        if not args.no_cpu_baseline:
+            out["decode"]["cpu_baseline"] = decode_cpu_baseline(args.config_cpu_seconds)
     if not args.no_gdn:
         _, gms = bench_prefill(kda, torch, x, args.steps, args.warmup, split, scalar_gate=True)
         g_avg_ms = sum(gms) / len(gms)
@@ -383,6 +542,12 @@ def main():
         }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    if not args.no_configs and args.workload == "prefill_varlen8_32k_h32_d128_bf16":
+        del x
+        out["configs"] = {}
+        for name in SUB_WORKLOADS:
+            out["configs"][name] = sub_workload_line(
+                kda, torch, name, args.config_steps, 3, 0.0 if args.no_cpu_baseline else args.config_cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
