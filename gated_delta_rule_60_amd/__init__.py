@@ -33,7 +33,9 @@ from ._lib import (  # noqa: F401
     kda_last_error,
     kda_prefill,
     kda_prefill_backward,
+    kda_prefill_backward_ex,
     kda_prefill_backward_workspace_size,
+    kda_prefill_backward_workspace_size_ex,
     kda_prefill_default_split,
     kda_prefill_ex,
     kda_prefill_plan,

@@ -53,6 +53,11 @@ SIGNATURES = {
                                             _i32, ctypes.c_int, _vp, _fp, _fp, _fp, _fp, _fp, _fp, _fp,
                                             _vp, _sz, _vp]),
     "kda_prefill_backward_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int]),
+    "kda_prefill_backward_ex": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32,
+                                               _i32, ctypes.c_int, _vp, _fp, _fp, _fp, _fp, _fp, _fp, _fp,
+                                               _vp, _sz, ctypes.c_uint32, _vp]),
+    "kda_prefill_backward_workspace_size_ex": (_sz, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int,
+                                                     ctypes.c_uint32]),
     "gdn_prefill_backward": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32,
                                             _i32, ctypes.c_int, _vp, _fp, _fp, _fp, _fp, _fp, _fp, _fp,
                                             _vp, _sz, _vp]),
@@ -189,6 +194,18 @@ def gdn_prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, 
 
 def kda_prefill_backward_workspace_size(N, T_tot, H, d_k, d_v, dtype) -> int:
     return int(load().kda_prefill_backward_workspace_size(N, T_tot, H, d_k, d_v, dtype))
+
+
+def kda_prefill_backward_ex(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, d_o,
+                            d_S_T, d_q, d_k_out, d_v_out, d_log_alpha, d_beta, d_S0, workspace,
+                            workspace_bytes, flags, stream) -> int:
+    return load().kda_prefill_backward_ex(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
+                                          dtype, d_o, d_S_T, d_q, d_k_out, d_v_out, d_log_alpha, d_beta,
+                                          d_S0, workspace, workspace_bytes, flags, stream)
+
+
+def kda_prefill_backward_workspace_size_ex(N, T_tot, H, d_k, d_v, dtype, flags) -> int:
+    return int(load().kda_prefill_backward_workspace_size_ex(N, T_tot, H, d_k, d_v, dtype, flags))
 
 
 def _check(status: int) -> None:
@@ -365,34 +382,38 @@ def gdn_decode_step_t(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
 
 
 def prefill_backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T=None, *, workspace=None,
-                     stream=None):
+                     any_decay: bool = False, stream=None):
     """Backward of ``prefill`` on torch tensors: gradients of a loss given
     d_o = dL/do ([T, H, d_v], dtype of q) and d_S_T = dL/dS_T ([N, H, d_k,
     d_v] fp32, or None).  Returns fp32 (d_q, d_k, d_v, d_log_alpha, d_beta,
     d_S0) shaped like q, k, v, log_alpha, beta and the initial state.
     ``workspace``: optional uint8 device tensor of at least
-    ``kda_prefill_backward_workspace_size(...)`` bytes (allocated if None)."""
-    return _backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, stream, False)
+    ``kda_prefill_backward_workspace_size_ex(...)`` bytes (allocated if None).
+    ``any_decay`` selects the token-recurrent backward (KDA_PREFILL_ANY_DECAY),
+    which has no decay-range contract."""
+    return _backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, stream, False, any_decay)
 
 
 def gdn_prefill_backward_t(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T=None, *, workspace=None,
-                           stream=None):
+                           any_decay: bool = False, stream=None):
     """Backward of ``gdn_prefill_t`` (log_alpha [T, H]); d_log_alpha is [T, H].
     Arguments and results otherwise as in ``prefill_backward``."""
-    return _backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, stream, True)
+    return _backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, stream, True, any_decay)
 
 
-def _backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, stream, scalar_gate: bool):
+def _backward(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, stream, scalar_gate: bool,
+              any_decay: bool = False):
     import torch
     if not q.is_cuda:
         raise ValueError("kda prefill backward runs on a GPU device; q is on the CPU")
     dev = q.device
     st = _stream_of(stream, dev)
     with torch.cuda.device(dev), torch.cuda.stream(st):
-        return _backward_on(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, st, scalar_gate)
+        return _backward_on(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, st, scalar_gate,
+                            any_decay)
 
 
-def _backward_on(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, st, scalar_gate):
+def _backward_on(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace, st, scalar_gate, any_decay):
     import torch
     dev = q.device
     T, H, dk = (int(x) for x in q.shape)
@@ -416,15 +437,16 @@ def _backward_on(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, d_S_T, workspace
     gq, gk, gv = torch.empty((T, H, dk), **f32), torch.empty((T, H, dk), **f32), torch.empty((T, H, dv), **f32)
     gla = torch.empty((T, H) if scalar_gate else (T, H, dk), **f32)
     gb, gS0 = torch.empty((T, H), **f32), torch.empty((N, H, dk, dv), **f32)
-    ws = kda_prefill_backward_workspace_size(N, T, H, dk, dv, code)
+    flags = (KDA_PREFILL_SCALAR_GATE if scalar_gate else 0) | (KDA_PREFILL_ANY_DECAY if any_decay else 0)
+    ws = kda_prefill_backward_workspace_size_ex(N, T, H, dk, dv, code, flags)
     if workspace is None:
         workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
     elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
     ptr = lambda t: t.data_ptr() if t is not None else None
-    call = gdn_prefill_backward if scalar_gate else kda_prefill_backward
-    _check(call(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(), ptr(S0),
-                cu_seqlens.data_ptr(), N, T, H, dk, dv, code, d_o.data_ptr(), ptr(d_S_T), gq.data_ptr(),
-                gk.data_ptr(), gv.data_ptr(), gla.data_ptr(), gb.data_ptr(), gS0.data_ptr(),
-                workspace.data_ptr(), workspace.numel(), int(st.cuda_stream)))
+    _check(kda_prefill_backward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
+                                   ptr(S0), cu_seqlens.data_ptr(), N, T, H, dk, dv, code, d_o.data_ptr(),
+                                   ptr(d_S_T), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(), gla.data_ptr(),
+                                   gb.data_ptr(), gS0.data_ptr(), workspace.data_ptr(), workspace.numel(), flags,
+                                   int(st.cuda_stream)))
     return gq, gk, gv, gla, gb, gS0

@@ -127,12 +127,18 @@ int32_t kda_prefill_default_split(int32_t N, int64_t T_tot, int32_t H, int32_t d
     return st == KDA_OK ? split : 0;
 }
 
-size_t kda_prefill_backward_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
-                                           kda_dtype dtype) {
+size_t kda_prefill_backward_workspace_size_ex(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
+                                              kda_dtype dtype, uint32_t flags) {
     if (N < 1 || H < 1 || T_tot < 0 || !supported_dim(d_k) || !supported_dim(d_v) ||
         (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32))
         return 0;
-    return kda::prefill_bwd_workspace_bytes(N, T_tot, H, d_k, d_v);
+    if (flags & KDA_PREFILL_ANY_DECAY) return kda::prefill_bwd_workspace_bytes(N, T_tot, H, d_k, d_v);
+    return kda::prefill_bwd_chunk_workspace_bytes(N, T_tot, H, d_k, d_v, dtype == KDA_DTYPE_BF16);
+}
+
+size_t kda_prefill_backward_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
+                                           kda_dtype dtype) {
+    return kda_prefill_backward_workspace_size_ex(N, T_tot, H, d_k, d_v, dtype, 0u);
 }
 
 }  // extern "C"
@@ -145,8 +151,12 @@ kda_status backward_impl(const void* q, const void* k, const void* v, const floa
                          const float* S0, const int32_t* cu_seqlens, int32_t N, int64_t T_tot, int32_t H,
                          int32_t d_k, int32_t d_v, kda_dtype dtype, const void* d_o, const float* d_S_T, float* d_q,
                          float* d_k_out, float* d_v_out, float* d_log_alpha, float* d_beta, float* d_S0,
-                         void* workspace, size_t workspace_bytes, void* stream, bool scalar_gate) {
+                         void* workspace, size_t workspace_bytes, void* stream, uint32_t flags) {
     g_last_error.clear();
+    if ((flags & ~static_cast<uint32_t>(KDA_PREFILL_SCALAR_GATE | KDA_PREFILL_ANY_DECAY)) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "unknown or unsupported bits in flags (the backward takes "
+                                         "KDA_PREFILL_SCALAR_GATE and KDA_PREFILL_ANY_DECAY)");
+    const bool scalar_gate = (flags & KDA_PREFILL_SCALAR_GATE) != 0;
     if (N < 1 || H < 1 || T_tot < 0)
         return fail(KDA_ERR_INVALID_ARG, "need N >= 1, H >= 1 and T_tot >= 0");
     const kda_status ds = check_dims(d_k, d_v, dtype);
@@ -159,6 +169,12 @@ kda_status backward_impl(const void* q, const void* k, const void* v, const floa
     if (T_tot > INT32_MAX) return fail(KDA_ERR_INVALID_ARG, "T_tot must fit in int32 (cu_seqlens is int32)");
     if (static_cast<int64_t>(N) * H * (d_v / 8) > (int64_t{1} << 22))
         return fail(KDA_ERR_INVALID_ARG, "N * H too large");
+    if (!(flags & KDA_PREFILL_ANY_DECAY)) {  // the chunked path runs the prefill kernel
+        if (T_tot * H * static_cast<int64_t>(d_k > d_v ? d_k : d_v) > INT32_MAX)
+            return fail(KDA_ERR_INVALID_ARG, "q, k, v, d_o and log_alpha must each hold fewer than 2^31 elements");
+        if (static_cast<int64_t>(H) * (d_k > d_v ? d_k : d_v) > (int64_t{1} << 20))
+            return fail(KDA_ERR_INVALID_ARG, "H * max(d_k, d_v) must not exceed 2^20");
+    }
     const void* ptrs[] = {q, k, v, scalar_gate ? nullptr : log_alpha, d_o, S0, d_S_T, d_q, d_k_out, d_v_out,
                           scalar_gate ? nullptr : d_log_alpha, d_S0};
     for (const void* p : ptrs)
@@ -168,7 +184,7 @@ kda_status backward_impl(const void* q, const void* k, const void* v, const floa
         if (p && (reinterpret_cast<uintptr_t>(p) & 3u) != 0)
             return fail(KDA_ERR_INVALID_ARG, scalar_gate ? "d_beta, log_alpha and d_log_alpha must be 4-byte aligned"
                                                          : "d_beta must be 4-byte aligned");
-    const size_t ws_need = kda_prefill_backward_workspace_size(N, T_tot, H, d_k, d_v, dtype);
+    const size_t ws_need = kda_prefill_backward_workspace_size_ex(N, T_tot, H, d_k, d_v, dtype, flags);
     if (workspace_bytes < ws_need)
         return fail(KDA_ERR_INVALID_ARG, "workspace smaller than kda_prefill_backward_workspace_size");
     if (!workspace) return fail(KDA_ERR_INVALID_ARG, "workspace must not be NULL");
@@ -178,7 +194,7 @@ kda_status backward_impl(const void* q, const void* k, const void* v, const floa
                         dtype == KDA_DTYPE_BF16, d_q, d_k_out, d_v_out, d_log_alpha, d_beta, d_S0,
                         workspace, stream, scalar_gate};
     (void)hipGetLastError();  // report only this launch's status
-    const hipError_t e = kda::launch_prefill_bwd(a);
+    const hipError_t e = (flags & KDA_PREFILL_ANY_DECAY) ? kda::launch_prefill_bwd(a) : kda::launch_prefill_bwd_chunk(a);
     if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
     return KDA_OK;
 }
@@ -194,7 +210,17 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
                                 float* d_v_out, float* d_log_alpha, float* d_beta, float* d_S0,
                                 void* workspace, size_t workspace_bytes, void* stream) {
     return backward_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, d_o, d_S_T, d_q,
-                         d_k_out, d_v_out, d_log_alpha, d_beta, d_S0, workspace, workspace_bytes, stream, false);
+                         d_k_out, d_v_out, d_log_alpha, d_beta, d_S0, workspace, workspace_bytes, stream, 0u);
+}
+
+kda_status kda_prefill_backward_ex(const void* q, const void* k, const void* v, const float* log_alpha,
+                                   const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
+                                   int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                   const void* d_o, const float* d_S_T, float* d_q, float* d_k_out,
+                                   float* d_v_out, float* d_log_alpha, float* d_beta, float* d_S0,
+                                   void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+    return backward_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, d_o, d_S_T, d_q,
+                         d_k_out, d_v_out, d_log_alpha, d_beta, d_S0, workspace, workspace_bytes, stream, flags);
 }
 
 kda_status gdn_prefill_backward(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -204,7 +230,8 @@ kda_status gdn_prefill_backward(const void* q, const void* k, const void* v, con
                                 float* d_v_out, float* d_log_alpha, float* d_beta, float* d_S0,
                                 void* workspace, size_t workspace_bytes, void* stream) {
     return backward_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v, dtype, d_o, d_S_T, d_q,
-                         d_k_out, d_v_out, d_log_alpha, d_beta, d_S0, workspace, workspace_bytes, stream, true);
+                         d_k_out, d_v_out, d_log_alpha, d_beta, d_S0, workspace, workspace_bytes, stream,
+                         KDA_PREFILL_SCALAR_GATE);
 }
 
 }  // extern "C"

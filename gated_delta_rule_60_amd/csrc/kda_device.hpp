@@ -210,4 +210,34 @@ __device__ __forceinline__ f32x4_t mma4(f32x4_t acc, const typename Elem<BF16>::
     }
 }
 
+// ---------------------------------------------------------------------------
+// Raw buffer resource over [base, base + bytes): a load at a byte offset at
+// or past `bytes` returns zero without touching memory, and a store there is
+// dropped.  Per-chunk resources make every load one instruction (a per-lane
+// offset fixed for the whole sequence plus a scalar row offset) and zero the
+// rows past a sequence end.  kNoAccess is a buffer offset beyond every range
+// the kernels build: ranges span at most one chunk's rows of one tensor (C
+// rows of H * max(d_k, d_v) elements, at most 2^27 bytes under the host's
+// limit H * max(d_k, d_v) <= 2^20), and the offset plus a few rows' stride
+// stays below 2^32.
+// ---------------------------------------------------------------------------
+constexpr int kNoAccess = 0x7FFFFF00;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
+                       __uint_as_float(x[3]));
+}
+
+__device__ __forceinline__ float buf_load_f1(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
 }  // namespace kda

@@ -54,6 +54,20 @@ struct SegView {
     int umax;           // units the grid covers
 };
 
+// Checkpoints the forward pass writes for the chunked backward pass (both
+// null for an ordinary prefill).  Per chunk slot (t_beg / C + n + i for
+// chunk i of sequence n, C the prefill's chunk length) and head:
+//   s   [DK / 16][DV / 32][64 lanes][8]  storage type: the state entering the
+//       chunk, as MFMA A-operand fragments with the value columns as the
+//       reduction index (lane l: row 16 it + (l & 15), columns
+//       32 kb + 4 (l >> 4) + {0..3} and 32 kb + 16 + 4 (l >> 4) + {0..3});
+//   w0  [DV / 16][C / 16][64 lanes][4]   storage type: W0 = V - K~ S in the
+//       C layout (lane l: column 16 ct + (l & 15), rows 16 rt + 4 (l >> 4) + {0..3}).
+struct CkptView {
+    void* s;
+    void* w0;
+};
+
 struct PrefillArgs {
     const void* q;
     const void* k;
@@ -112,6 +126,11 @@ struct BackwardArgs {
 };
 
 hipError_t launch_prefill(const PrefillArgs& a);
+// The forward pass with checkpoints instead of outputs (o and S_T are not
+// written): one pass, whole value columns (v_split 1), never segmented.
+hipError_t launch_prefill_ckpt(const PrefillArgs& a, const CkptView& ck);
+// Chunk length of the prefill kernel for these sizes (the checkpoint slot size).
+int prefill_chunk_len(int32_t d_k, bool bf16);
 // Token-recurrent prefill for any decay range (kda_backward.hip).
 hipError_t launch_prefill_recurrent(const PrefillArgs& a);
 
@@ -125,10 +144,17 @@ size_t prefill_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
 hipError_t launch_seg_plan(const PrefillArgs& a, SegView* view);
 hipError_t launch_seg_fixup(const PrefillArgs& a, const SegView& v);
 hipError_t launch_decode(const DecodeArgs& a);
-// Backward pass of the prefill (kda_backward.hip) and the workspace it needs:
-// fp32 state checkpoints every 16 tokens and one residual row per token-head.
+// Token-recurrent backward pass of the prefill (kda_backward.hip), for any
+// decay range, and the workspace it needs: fp32 state checkpoints every 16
+// tokens and one residual row per token-head.
 hipError_t launch_prefill_bwd(const BackwardArgs& a);
 size_t prefill_bwd_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v);
+// Chunked backward pass (kda_bwd_chunk.hip): the forward with checkpoints,
+// then the reverse walk over the chunks; its workspace holds the checkpoints
+// (the entering state and W0 of every chunk, storage type).
+hipError_t launch_prefill_bwd_chunk(const BackwardArgs& a);
+size_t prefill_bwd_chunk_workspace_bytes(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
+                                         bool bf16);
 
 // Launch shape kda_prefill picks for these sizes on a device with `cus`
 // compute units (see kda_prefill.hip).

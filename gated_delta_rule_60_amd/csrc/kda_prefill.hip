@@ -343,34 +343,6 @@ __device__ __forceinline__ typename Elem<BF16>::R4 lds_get_raw4(const typename E
     }
 }
 
-// Raw buffer resource over [base, base + bytes): a load at a byte offset at
-// or past `bytes` returns zero without touching memory.  Per-chunk resources
-// make every load one instruction (a per-lane offset fixed for the whole
-// sequence plus a scalar row offset) and zero the rows past a sequence end.
-// A buffer offset beyond every range this kernel builds: a load returns 0 and
-// a store is dropped, without touching memory.  Ranges span at most one
-// chunk's rows of one tensor (C rows of H * max(d_k, d_v) elements, at most
-// 2^27 bytes under the host's limit H * max(d_k, d_v) <= 2^20), and the
-// offset plus a few rows' stride stays below 2^32.
-constexpr int kNoAccess = 0x7FFFFF00;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
-                       __uint_as_float(x[3]));
-}
-
-__device__ __forceinline__ float buf_load_f1(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-}
-
 // four fp32 values as four consecutive storage elements (bf16: round to
 // nearest even)
 template <bool BF16>
@@ -465,13 +437,13 @@ __device__ __forceinline__ void ctr_wait_each(int* ctrs, int n, int target, int*
 // per-channel computation with the value repeated over the channels.
 // WIDE: wide-decay variant (exponents of strongly decaying channels taken
 // relative to the chunk's middle row, the state operand scaled to match).
-template <bool BF16, int DK, int NC, int CT, bool SG, bool WIDE>
+template <bool BF16, int DK, int NC, int CT, bool SG, bool WIDE, bool CK = false>
 __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void prefill_kernel(
     const typename Elem<BF16>::G* __restrict__ q, const typename Elem<BF16>::G* __restrict__ k,
     const typename Elem<BF16>::G* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, const float* __restrict__ S0, const int32_t* __restrict__ cu,
     int N, int H, int dv, int v_split, typename Elem<BF16>::G* __restrict__ o,
-    float* __restrict__ S_T, SegView seg) {
+    float* __restrict__ S_T, SegView seg, CkptView ck) {
     using Sh = PrefillShape<BF16, DK, NC, CT, WIDE>;
     using T = Elem<BF16>;
     using E = typename T::E;
@@ -742,8 +714,43 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
         f32x4_t Rp[CT][NB], U[CT][NB];
         F4 uf[CT][NB];
 
+        // Checkpoints for the chunked backward pass (CK): per chunk, the
+        // entering state S in the layout of its A operand with the value
+        // columns as the reduction index (each 16 x 16 tile transposed by an
+        // MFMA with the identity, which is exact), and W0 = V - K~ S in the C
+        // layout.  Slot of chunk i: t_beg / C + n + i (distinct over the
+        // sequences of a batch).
+        using Ev = typename Elem<BF16>::E;
+        auto ck_slot = [&](int i) __attribute__((always_inline)) {
+            return static_cast<size_t>(t_beg / C + n + i) * H + h;
+        };
+        auto ck_store_state = [&](int i) __attribute__((always_inline)) {
+            Ev* const base = static_cast<Ev*>(ck.s) + ck_slot(i) * DK * dv;
+            F4 eye;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) eye[j] = T::to_e(4 * lg + j == ln ? 1.f : 0.f);
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const int ctile = (j0 + col0(ct)) >> 4;
+#pragma unroll
+                for (int it = 0; it < DK / 16; ++it) {
+                    // lane (ln, lg): S[16 it + ln][16 ctile + 4 lg .. + 3]
+                    const f32x4_t tr = mma4<BF16>(z, acc_frag4<BF16>(Sr[ct][it]), eye);
+                    const size_t e = (static_cast<size_t>(it * (dv >> 5) + (ctile >> 1)) * 64 + lane) * 8 + 4 * (ctile & 1);
+                    lds_store4<BF16>(base + e, tr[0], tr[1], tr[2], tr[3]);
+                }
+            }
+        };
+        auto ck_store_w0 = [&](int i, int ct, int rt, const f32x4_t& rpv) __attribute__((always_inline)) {
+            Ev* const base = static_cast<Ev*>(ck.w0) + ck_slot(i) * C * dv;
+            const int ctile = (j0 + col0(ct)) >> 4;
+            const size_t e = (static_cast<size_t>(ctile * NB + rt) * 64 + lane) * 4;
+            lds_store4<BF16>(base + e, -rpv[0], -rpv[1], -rpv[2], -rpv[3]);
+        };
+
         // R' = beta (K~ S - V)  (= -R)
-        auto chain_R = [&](int B) __attribute__((always_inline)) {
+        auto chain_R = [&](int B, int ci) __attribute__((always_inline)) {
             if constexpr (WIDE) {
                 // the S operand of K~ S and Q~ S with its rows (key channels)
                 // scaled by 2^ref of the chunk (exactly 1 for a channel with
@@ -776,6 +783,10 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                     const F8 a = tile_frag8<BF16, UK>(tKb(B), 16 * rt + ln, kb, lg);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) Rp[ct][rt] = mma8<BF16>(Rp[ct][rt], a, sf[ct][kb]);
+                }
+                if constexpr (CK) {
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) ck_store_w0(ci, ct, rt, Rp[ct][rt]);
                 }
                 // rows of R' scaled by beta (lane holds rows 16 rt + 4 lg + j)
                 const float4 b4 = *reinterpret_cast<const float4*>(sBeta(B) + 16 * rt + 4 * lg);
@@ -820,6 +831,8 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             // 16 ct + ln: one O^T quad, staged in the wave's own rows of this
             // slot's V^T tile (read above, in chain_R).  The producers store
             // it to global memory, in row order, when they refill the slot.
+            // (The checkpointing variant has no outputs.)
+            if constexpr (CK) return;
 #pragma unroll
             for (int rt = 0; rt < NB; ++rt) {
                 f32x4_t acc[CT];
@@ -911,7 +924,8 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
 #pragma unroll
                     for (int t = 0; t < JPW; ++t) jobs[t] = prep3_compute(Pn, t);
                 }
-                chain_R(P);
+                if constexpr (CK) ck_store_state(i);
+                chain_R(P, i);
                 chain_UO(P, J);
                 chain_S(P);
                 ctr_signal(nFree, lane);
@@ -939,13 +953,15 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                 for (int it = 0; it < DK / 16; ++it) Sr[ct][it] = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
             }
         }
+        if constexpr (!CK) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            const size_t col = static_cast<size_t>(j0 + col0(ct) + ln);
+            for (int ct = 0; ct < CT; ++ct) {
+                const size_t col = static_cast<size_t>(j0 + col0(ct) + ln);
 #pragma unroll
-            for (int it = 0; it < DK / 16; ++it) {
+                for (int it = 0; it < DK / 16; ++it) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sdst[(16 * it + 4 * lg + j) * dv + col] = Sr[ct][it][j];
+                    for (int j = 0; j < 4; ++j) sdst[(16 * it + 4 * lg + j) * dv + col] = Sr[ct][it][j];
+                }
             }
         }
     } else if (wave < NC + NP) {
@@ -1192,7 +1208,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             // it, then store that chunk's O from it
             if (m >= 3) {
                 ctr_wait(nFree, NC * (m - 2), fault);
-                store_o(m - 3, P);
+                if constexpr (!CK) store_o(m - 3, P);
             }
             prep12(X, P);
             ctr_publish(prodDone + pw, m + 1, lane);
@@ -1207,7 +1223,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
         }
         // The last chunks' O stay in slots nobody refills: once every chunk is
         // done, this wave stores those a continued loop would have.
-        if (m - 3 < nchunks) {
+        if (!CK && m - 3 < nchunks) {
             ctr_wait(nFree, NC * nchunks, fault);
             for (; m - 3 < nchunks; m += PP) {
                 if (m >= 3) {
@@ -1224,18 +1240,54 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
 // BV = d_v / v_split: 4 waves x 2 tiles (128), 4 x 1 (64), 2 x 1 (32),
 // 1 x 1 (16); producer waves follow d_k.
 // ---------------------------------------------------------------------------
-template <bool BF16, int DK, int NC, int CT, bool SG, bool WIDE>
-static hipError_t launch_prefill_t(const PrefillArgs& a, const SegView& seg) {
+template <bool BF16, int DK, int NC, int CT, bool SG, bool WIDE, bool CK = false>
+static hipError_t launch_prefill_t(const PrefillArgs& a, const SegView& seg, const CkptView& ck = CkptView{}) {
     using G = typename Elem<BF16>::G;
     using Sh = PrefillShape<BF16, DK, NC, CT, WIDE>;
     const unsigned units = seg.units ? static_cast<unsigned>(seg.umax) : static_cast<unsigned>(a.N);
     const unsigned per_unit = static_cast<unsigned>(a.v_split) * (seg.units ? 2u : 1u);
     const unsigned grid = units * static_cast<unsigned>(a.H) * per_unit;
-    hipLaunchKernelGGL((prefill_kernel<BF16, DK, NC, CT, SG, WIDE>), dim3(grid), dim3(Sh::NT), 0,
+    hipLaunchKernelGGL((prefill_kernel<BF16, DK, NC, CT, SG, WIDE, CK>), dim3(grid), dim3(Sh::NT), 0,
                        static_cast<hipStream_t>(a.stream), static_cast<const G*>(a.q),
                        static_cast<const G*>(a.k), static_cast<const G*>(a.v), a.log_alpha, a.beta,
-                       a.S0, a.cu_seqlens, a.N, a.H, a.d_v, a.v_split, static_cast<G*>(a.o), a.S_T, seg);
+                       a.S0, a.cu_seqlens, a.N, a.H, a.d_v, a.v_split, static_cast<G*>(a.o), a.S_T, seg, ck);
     return hipGetLastError();
+}
+
+template <bool BF16, int DK, int NC, int CT>
+static hipError_t launch_ckpt_sg(const PrefillArgs& a, const CkptView& ck) {
+    return a.scalar_gate ? launch_prefill_t<BF16, DK, NC, CT, true, false, true>(a, SegView{}, ck)
+                         : launch_prefill_t<BF16, DK, NC, CT, false, false, true>(a, SegView{}, ck);
+}
+
+template <bool BF16, int DK>
+static hipError_t launch_ckpt_dk(const PrefillArgs& a, const CkptView& ck) {
+    switch (a.d_v) {  // whole value columns: v_split 1
+        case 128: return launch_ckpt_sg<BF16, DK, 4, 2>(a, ck);
+        case 64: return launch_ckpt_sg<BF16, DK, 4, 1>(a, ck);
+        case 32: return launch_ckpt_sg<BF16, DK, 2, 1>(a, ck);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_prefill_ckpt(const PrefillArgs& a0, const CkptView& ck) {
+    PrefillArgs a = a0;
+    a.v_split = 1;
+    switch (a.d_k) {
+        case 32: return a.bf16 ? launch_ckpt_dk<true, 32>(a, ck) : launch_ckpt_dk<false, 32>(a, ck);
+        case 64: return a.bf16 ? launch_ckpt_dk<true, 64>(a, ck) : launch_ckpt_dk<false, 64>(a, ck);
+        case 128: return a.bf16 ? launch_ckpt_dk<true, 128>(a, ck) : launch_ckpt_dk<false, 128>(a, ck);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+int prefill_chunk_len(int32_t d_k, bool bf16) {
+    switch (d_k) {
+        case 32: return bf16 ? kChunk<true, 32> : kChunk<false, 32>;
+        case 64: return bf16 ? kChunk<true, 64> : kChunk<false, 64>;
+        case 128: return bf16 ? kChunk<true, 128> : kChunk<false, 128>;
+        default: return 0;
+    }
 }
 
 template <bool BF16, int DK, int NC, int CT>

@@ -274,7 +274,6 @@ __global__ __launch_bounds__(ChainShape<DK>::NT) void seg_chain_kernel(const int
 // Buffer ranges end at the segment's last token (loads past it return zero,
 // stores are dropped), so every load and store is unconditional.
 // ---------------------------------------------------------------------------
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 template <bool BF16, int DK>
 struct OutShape {

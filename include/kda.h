@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 4
+#define KDA_VERSION 5
 
 typedef enum {
     KDA_OK = 0,
@@ -263,8 +263,15 @@ kda_status gdn_decode_step(const void* q, const void* k, const void* v,
  * with the read-out o_t = S_t^T q_t after the update.  The training side of
  * the page's reading of the layer as online learning needs it.
  *
- * Inputs are those of kda_prefill (same layouts, dtype, alignment and
- * numerical contract):
+ * It runs chunked, on MFMA: the forward pass once more, storing the state
+ * entering every chunk and W0 = V - K~ S (in the storage type) in the
+ * workspace, then a walk over each sequence's chunks from the last that
+ * carries dL/dS in fp32 and forms every product of the chunk's adjoint as a
+ * matrix product.  Its numerical contract is kda_prefill's (log_alpha summed
+ * over any 32 consecutive tokens >= -80 per channel); kda_prefill_backward_ex
+ * with KDA_PREFILL_ANY_DECAY has none.
+ *
+ * Inputs are those of kda_prefill (same layouts, dtype, alignment and sizes):
  *   q, k, v, log_alpha, beta, S0 (NULL: zero), cu_seqlens, N, T_tot, H, d_k,
  *   d_v, dtype
  *   d_o        device [T_tot, H, d_v]     dtype     dL/do
@@ -279,8 +286,8 @@ kda_status gdn_decode_step(const void* q, const void* k, const void* v,
  *              bytes, 256-byte aligned, owned by the caller; its contents on
  *              entry do not matter and are clobbered.
  * Outputs must not alias inputs or one another.  Errors as for kda_prefill
- * (validation before any HIP call).  Asynchronous on `stream`.  Results are
- * identical from run to run.
+ * (validation before any kernel is launched).  Asynchronous on `stream`.
+ * Results are identical from run to run.
  */
 kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
                                 const float* log_alpha, const float* beta, const float* S0,
@@ -289,6 +296,28 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
                                 const float* d_S_T, float* d_q, float* d_k_out, float* d_v_out,
                                 float* d_log_alpha, float* d_beta, float* d_S0, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * kda_prefill_backward_ex -- kda_prefill_backward with option flags (0 gives
+ * kda_prefill_backward exactly):
+ *   KDA_PREFILL_SCALAR_GATE  one gate per token and head (as
+ *                            gdn_prefill_backward: log_alpha and d_log_alpha
+ *                            are [T_tot, H]).
+ *   KDA_PREFILL_ANY_DECAY    the token-recurrent backward: fp32 on the vector
+ *                            ALU, no range contract (any finite log_alpha
+ *                            <= 0, including hard resets), much slower; its
+ *                            workspace holds fp32 states every 16 tokens and
+ *                            one fp32 row of d_v per token and head.
+ * Other bits give KDA_ERR_INVALID_ARG.  The workspace is sized by
+ * kda_prefill_backward_workspace_size_ex with the same flags.
+ */
+kda_status kda_prefill_backward_ex(const void* q, const void* k, const void* v,
+                                   const float* log_alpha, const float* beta, const float* S0,
+                                   const int32_t* cu_seqlens, int32_t N, int64_t T_tot, int32_t H,
+                                   int32_t d_k, int32_t d_v, kda_dtype dtype, const void* d_o,
+                                   const float* d_S_T, float* d_q, float* d_k_out, float* d_v_out,
+                                   float* d_log_alpha, float* d_beta, float* d_S0, void* workspace,
+                                   size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
  * gdn_prefill_backward -- the backward pass of gdn_prefill (one gate per token
@@ -307,12 +336,19 @@ kda_status gdn_prefill_backward(const void* q, const void* k, const void* v,
                                 float* d_log_alpha, float* d_beta, float* d_S0, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
-/* Workspace bytes kda_prefill_backward needs: fp32 states at the start of
- * every 16-token block of every sequence (at most T_tot / 16 + N + 1 blocks
- * per head) and one fp32 row of d_v per token and head.  0 for unsupported
- * sizes. */
+/* Workspace bytes kda_prefill_backward needs: the state entering every chunk
+ * (d_k x d_v) and W0 of every chunk (C x d_v), in the storage type, for at
+ * most T_tot / C + N + 1 chunks per head, C the prefill's chunk length (32
+ * tokens; 16 for float32 with d_k >= 64).  0 for unsupported sizes. */
 size_t kda_prefill_backward_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
                                            int32_t d_v, kda_dtype dtype);
+
+/* Workspace bytes kda_prefill_backward_ex needs with these flags: as above,
+ * or with KDA_PREFILL_ANY_DECAY fp32 states at the start of every 16-token
+ * block (at most T_tot / 16 + N + 1 blocks per head) and one fp32 row of d_v
+ * per token and head. */
+size_t kda_prefill_backward_workspace_size_ex(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
+                                              int32_t d_v, kda_dtype dtype, uint32_t flags);
 
 /*
  * kda_prefill_noalloc -- kda_prefill for callers that cannot allocate device

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.kda_version() == 4
+    assert kda.kda_version() == 5
     for s in (0, 1, 2, 3):
         assert kda.kda_status_string(s).startswith("KDA_")
     assert "unknown" in kda.kda_status_string(99)
@@ -239,12 +239,38 @@ def test_backward_validation(kw, status, needle):
 
 
 def test_backward_workspace_size():
-    # fp32 checkpoints for T/16 + N + 1 blocks per head (256-byte rounded) plus one fp32 row per token-head
     n, t, h, dk, dv = 3, 1000, 4, 64, 32
+    # chunked (default): the entering state and W0 of at most T/C + N + 1 chunks per
+    # head in the storage type (C = 32; 16 for fp32 with d_k >= 64)
+    for dtype, C, es in ((BF16, 32, 2), (F32, 16, 4)):
+        slots = (t // C + n + 1) * h
+        want = (slots * dk * dv * es + 255) // 256 * 256 + slots * C * dv * es
+        assert kda.kda_prefill_backward_workspace_size(n, t, h, dk, dv, dtype) == want
+        assert kda.kda_prefill_backward_workspace_size_ex(n, t, h, dk, dv, dtype, 0) == want
+        assert kda.kda_prefill_backward_workspace_size_ex(n, t, h, dk, dv, dtype, kda.KDA_PREFILL_SCALAR_GATE) == want
+    assert kda.kda_prefill_backward_workspace_size(n, t, h, 32, dv, F32) == \
+        ((t // 32 + n + 1) * h * 32 * dv * 4 + 255) // 256 * 256 + (t // 32 + n + 1) * h * 32 * dv * 4
+    # token-recurrent: fp32 checkpoints for T/16 + N + 1 blocks per head (256-byte rounded)
+    # plus one fp32 row per token-head
     ck = (t // 16 + n + 1) * h * dk * dv * 4
-    assert kda.kda_prefill_backward_workspace_size(n, t, h, dk, dv, BF16) == (ck + 255) // 256 * 256 + t * h * dv * 4
+    assert kda.kda_prefill_backward_workspace_size_ex(n, t, h, dk, dv, BF16, kda.KDA_PREFILL_ANY_DECAY) == \
+        (ck + 255) // 256 * 256 + t * h * dv * 4
     assert kda.kda_prefill_backward_workspace_size(0, t, h, dk, dv, BF16) == 0
     assert kda.kda_prefill_backward_workspace_size(n, t, h, 48, dv, BF16) == 0
+
+
+def test_backward_ex_rejects_unknown_flags():
+    a = dict(q=FAKE, k=FAKE, v=FAKE, log_alpha=FAKE, beta=FAKE, S0=None, cu_seqlens=FAKE, N=1,
+             T_tot=64, H=2, d_k=64, d_v=64, dtype=BF16, d_o=FAKE, d_S_T=None, d_q=FAKE, d_k_out=FAKE,
+             d_v_out=FAKE, d_log_alpha=FAKE, d_beta=FAKE, d_S0=FAKE, workspace=0x100000,
+             workspace_bytes=1 << 40, stream=None)
+    for bad in (kda.KDA_PREFILL_WIDE_DECAY, 8, 1 << 31):
+        assert kda.kda_prefill_backward_ex(flags=bad, **a) == kda.KDA_ERR_INVALID_ARG
+        assert "flags" in kda.kda_last_error()
+    # known flags pass flag validation and fail later, on the small workspace
+    for f in (0, kda.KDA_PREFILL_ANY_DECAY, kda.KDA_PREFILL_SCALAR_GATE | kda.KDA_PREFILL_ANY_DECAY):
+        assert kda.kda_prefill_backward_ex(flags=f, **dict(a, workspace_bytes=16)) == kda.KDA_ERR_INVALID_ARG
+        assert "workspace smaller" in kda.kda_last_error()
 
 
 @pytest.mark.parametrize("kw,needle", [

@@ -1,7 +1,8 @@
-"""Backward pass of the prefill (kda_prefill_backward) against the fp64
-oracle's reverse-mode recurrence: every gradient, element by element, on
-seeded inputs covering ragged 16-token blocks, empty sequences, both value
-slicings (d_v = 128 runs two workgroups per head) and every head size."""
+"""Backward pass of the prefill against the fp64 oracle's reverse-mode
+recurrence: every gradient, element by element, on seeded inputs covering
+ragged chunks, empty sequences and every head size, for both paths: the
+chunked MFMA backward (kda_prefill_backward) and the token-recurrent one
+(kda_prefill_backward_ex with KDA_PREFILL_ANY_DECAY)."""
 import numpy as np
 import pytest
 
@@ -31,18 +32,22 @@ def _id(c):
     return f"L{'-'.join(map(str, c[0]))}_H{c[1]}_dk{c[2]}_dv{c[3]}_{c[4]}{'' if c[5] else '_noS0'}{'' if c[6] else '_nodST'}"
 
 
-def _run(x, dO, dST):
+PATHS = ["chunked", "recurrent"]
+
+
+def _run(x, dO, dST, path="chunked"):
     import torch
     d = upload(x)
     td = d["q"].dtype
     dO_d = torch.from_numpy(dO).cuda().to(td)
     dST_d = None if dST is None else torch.from_numpy(dST).cuda()
     return kda.prefill_backward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
-                                d["cu_seqlens"], dO_d, dST_d)
+                                d["cu_seqlens"], dO_d, dST_d, any_decay=(path == "recurrent"))
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("case", CASES, ids=_id)
-def test_backward_matches_oracle(case):
+def test_backward_matches_oracle(case, path):
     import torch
     lengths, H, dk, dv, dtype, s0, dst = case
     x = inputs.make_prefill_inputs(lengths, H, dk, dv, dtype, seed=sum(lengths) + dk + 7,
@@ -51,28 +56,46 @@ def test_backward_matches_oracle(case):
     log(f"  oracle backward {lengths} H={H} dk={dk} dv={dv} {dtype}")
     ref = oracle.prefill_backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens,
                                   dO.astype(np.float64), dST)
-    log("  gpu backward")
+    log(f"  gpu backward ({path})")
+    got = _run(x, dO, dST, path)
+    torch.cuda.synchronize()
+    for name, g, r in zip(NAMES, got, ref):
+        assert_close(host(g), r, dtype, name)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_backward_is_deterministic(path):
+    """Same bits on every run (the token-recurrent path adds two slices' row
+    sums atomically onto zero; the chunked path has no atomics)."""
+    import torch
+    x = inputs.make_prefill_inputs([200, 61], 2, 128, 128, "bf16", seed=5, s0_std=1.0)
+    dO, dST = inputs.make_backward_grads(x, seed=6)
+    first = _run(x, dO, dST, path)
+    for rep in range(3):
+        again = _run(x, dO, dST, path)
+        torch.cuda.synchronize()
+        for name, a, b in zip(NAMES, first, again):
+            assert torch.equal(a, b), f"{name} differs on repeat {rep}"
+
+
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 128), ("f32", 32)])
+def test_chunked_backward_at_the_decay_limit(dtype, dk):
+    """The chunked backward's contract is the prefill's: log alpha summed over
+    any 32 consecutive tokens >= -80.  Gates of -2.5 per token reach it."""
+    import torch
+    x = inputs.make_prefill_inputs([150, 47], 2, dk, 128, dtype, seed=91, s0_std=1.0)
+    x.log_alpha[:] = -2.5
+    dO, dST = inputs.make_backward_grads(x, seed=92)
+    ref = oracle.prefill_backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens,
+                                  dO.astype(np.float64), dST)
     got = _run(x, dO, dST)
     torch.cuda.synchronize()
     for name, g, r in zip(NAMES, got, ref):
         assert_close(host(g), r, dtype, name)
 
 
-def test_backward_is_deterministic():
-    """The d_v = 128 shape adds two slices' row sums atomically: still the
-    same bits on every run."""
-    import torch
-    x = inputs.make_prefill_inputs([200, 61], 2, 128, 128, "bf16", seed=5, s0_std=1.0)
-    dO, dST = inputs.make_backward_grads(x, seed=6)
-    first = _run(x, dO, dST)
-    for rep in range(3):
-        again = _run(x, dO, dST)
-        torch.cuda.synchronize()
-        for name, a, b in zip(NAMES, first, again):
-            assert torch.equal(a, b), f"{name} differs on repeat {rep}"
-
-
-def test_backward_varlen_32k_sampled_heads():
+@pytest.mark.parametrize("path", PATHS)
+def test_backward_varlen_32k_sampled_heads(path):
     """The 32k varlen batch (8 sequences, H = 32, d = 128, bf16) in full on the
     GPU; the oracle checks heads 5 and 30 of every sequence."""
     import torch
@@ -84,20 +107,17 @@ def test_backward_varlen_32k_sampled_heads():
     log(f"  oracle backward on heads {heads}")
     ref = oracle.prefill_backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens,
                                   dO.astype(np.float64), dST, pair_mask=mask)
-    log("  gpu backward")
-    got = _run(x, dO, dST)
+    log(f"  gpu backward ({path})")
+    got = _run(x, dO, dST, path)
     torch.cuda.synchronize()
     for name, g, r in zip(NAMES, got, ref):
-        if name == "d_S0":
-            assert_close(host(g[:, heads]), r[:, heads], "bf16", name)
-        else:
-            assert_close(host(g[:, heads]), r[:, heads], "bf16", name)
+        assert_close(host(g[:, heads]), r[:, heads], "bf16", name)
 
 
 def test_backward_strong_decay_and_resets():
-    """The backward evaluates no decay products, so any finite log alpha
-    works: gates drawn from -U(0, 5), plus tokens with log alpha = -1000 (a
-    reset: alpha underflows to 0 in fp32 and fp64 alike)."""
+    """The token-recurrent backward evaluates no decay products, so any finite
+    log alpha works: gates drawn from -U(0, 5), plus tokens with log alpha =
+    -1000 (a reset: alpha underflows to 0 in fp32 and fp64 alike)."""
     import torch
     x = inputs.make_prefill_inputs([90, 45], 2, 64, 128, "bf16", seed=77, s0_std=1.0,
                                    log_alpha_range=(0.0, 5.0))
@@ -105,26 +125,28 @@ def test_backward_strong_decay_and_resets():
     dO, dST = inputs.make_backward_grads(x, seed=78)
     ref = oracle.prefill_backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens,
                                   dO.astype(np.float64), dST)
-    got = _run(x, dO, dST)
+    got = _run(x, dO, dST, "recurrent")
     torch.cuda.synchronize()
     for name, g, r in zip(NAMES, got, ref):
         assert_close(host(g), r, "bf16", name)
 
 
-def test_backward_all_sequences_empty():
+@pytest.mark.parametrize("path", PATHS)
+def test_backward_all_sequences_empty(path):
     """T_tot = 0: no token gradients, and the initial state's gradient is dL/dS_T."""
     import torch
     x = inputs.make_prefill_inputs([0, 0, 0], 2, 64, 128, "bf16", seed=3, s0_std=1.0)
     dO, dST = inputs.make_backward_grads(x, seed=4)
-    got = _run(x, dO, dST)
+    got = _run(x, dO, dST, path)
     torch.cuda.synchronize()
     assert all(g.numel() == 0 for g in got[:5])
     assert torch.equal(got[5], torch.from_numpy(dST).cuda())
 
 
-def test_backward_many_short_sequences():
+@pytest.mark.parametrize("path", PATHS)
+def test_backward_many_short_sequences(path):
     """Forty sequences of 0 to 40 tokens (many not a multiple of 16) in one
-    batch: every sequence's checkpoint blocks land in their own slots."""
+    batch: every sequence's checkpoints land in their own slots."""
     import torch
     rng = np.random.default_rng(5)
     lengths = [int(v) for v in rng.integers(0, 41, size=40)]
@@ -132,7 +154,7 @@ def test_backward_many_short_sequences():
     dO, dST = inputs.make_backward_grads(x, seed=7)
     ref = oracle.prefill_backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.S0, x.cu_seqlens,
                                   dO.astype(np.float64), dST)
-    got = _run(x, dO, dST)
+    got = _run(x, dO, dST, path)
     torch.cuda.synchronize()
     for name, g, r in zip(NAMES, got, ref):
         assert_close(host(g), r, "f32", name)

@@ -103,9 +103,10 @@ def test_gdn_wide_decay():
     assert_close(host(ST), ref_S, "bf16", "S_T")
 
 
+@pytest.mark.parametrize("path", ["chunked", "recurrent"])
 @pytest.mark.parametrize("case", [([70, 0, 33], 2, 64, 64, "f32"), ([150, 40], 2, 128, 128, "bf16"),
                                   ([37], 3, 32, 128, "bf16")], ids=lambda c: f"L{'-'.join(map(str, c[0]))}_dk{c[2]}_dv{c[3]}_{c[4]}")
-def test_gdn_backward_matches_oracle_and_kda(case):
+def test_gdn_backward_matches_oracle_and_kda(case, path):
     """gdn_prefill_backward against the oracle's scalar-gate backward; its
     other gradients carry the same bits as kda_prefill_backward's with the
     gate repeated over the channels, and its gate gradient is their channel sum."""
@@ -120,8 +121,9 @@ def test_gdn_backward_matches_oracle_and_kda(case):
     dO_d, dST_d = torch.from_numpy(dO).cuda().to(td), torch.from_numpy(dST).cuda()
     la_d = torch.from_numpy(la).cuda()
     args = lambda g: (d["q"], d["k"], d["v"], g, d["beta"], d["S0"], d["cu_seqlens"], dO_d, dST_d)
-    got = kda.gdn_prefill_backward_t(*args(la_d))
-    full = kda.prefill_backward(*args(la_d[:, :, None].expand(-1, -1, dk).contiguous()))
+    anyd = path == "recurrent"
+    got = kda.gdn_prefill_backward_t(*args(la_d), any_decay=anyd)
+    full = kda.prefill_backward(*args(la_d[:, :, None].expand(-1, -1, dk).contiguous()), any_decay=anyd)
     torch.cuda.synchronize()
     names = ("d_q", "d_k", "d_v", "d_log_alpha", "d_beta", "d_S0")
     for name, g, r in zip(names, got, ref):

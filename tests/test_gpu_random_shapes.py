@@ -55,7 +55,8 @@ def test_random_shape_forward_and_backward(case):
         td = d["q"].dtype
         grads = kda.prefill_backward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
                                      d["cu_seqlens"], torch.from_numpy(dO).cuda().to(td),
-                                     None if dST is None else torch.from_numpy(dST).cuda())
+                                     None if dST is None else torch.from_numpy(dST).cuda(),
+                                     any_decay=(mode == "any"))
         torch.cuda.synchronize()
         for name, g, r in zip(("d_q", "d_k", "d_v", "d_log_alpha", "d_beta", "d_S0"), grads, refs):
             assert_close(host(g), r, dtype, name)
