@@ -528,17 +528,18 @@ def main():
         b_avg = sum(bms) / len(bms)
         bfl = backward_flops(x.T_tot, x.H, x.d_k, x.d_v)
         bby = backward_bytes(x.T_tot, x.N, x.H, x.d_k, x.d_v, esize)
+        bsrc = ["kda_bwd_chunk.hip", "kda_prefill.hip", "kda_device.hpp"]
         out["backward"] = {
             "workload": args.workload, "what": "kda_prefill_backward: dq, dk, dv, dlog_alpha, dbeta, dS0",
             "tokens_per_s": x.T_tot / (b_avg * 1e-3), "ms_avg": b_avg, "ms_min": min(bms), "launches": len(bms),
             "workspace_bytes": bws,
-            "roofline": {"bound": "alu", "achieved": bfl / (b_avg * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": bfl / (b_avg * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
-                         "traffic": measured_traffic("prefill_backward", args.workload,
-                                                     ["kda_backward.hip", "kda_device.hpp"]),
-                         "kernel": "kda::bwd_forward_kernel + kda::bwd_kernel (one call)",
-                         "alg_flops_per_launch": bfl, "alg_bytes_per_launch": bby,
-                         "hbm_frac": bby / (b_avg * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "roofline": {"bound": "hbm", "achieved": bby / (b_avg * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": bby / (b_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("prefill_backward", args.workload, bsrc),
+                         "kernel": "kda::prefill_kernel (checkpointing) + kda::bwd_chunk_kernel (one call)",
+                         "alg_bytes_per_launch": bby,
+                         "mfma_counter_busy_frac_pass2": measured_mfma_busy("prefill_backward", args.workload, bsrc),
+                         "token_recurrence_flops_per_launch": bfl},
         }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)

@@ -39,14 +39,16 @@
 //      chunk before are issued;
 //   J  chain waves: the C x C products G, L, A and the inverses of the 16 x 16
 //      diagonal blocks of I + L (nilpotent products, as in the forward);
-//   CH chain waves (32 value columns each; D in fp32 registers): U, dU, dR,
-//      dv = beta dR, the carried gradient's update, and U, dR, Dg published
-//      to LDS in row order (each 16 x 16 tile transposed by an MFMA with the
-//      identity);
-//   LA leaf waves: the C x C products dA and dL;
-//   LB leaf waves (32 key channels each, S of those rows in registers): the
-//      products reduced over the value columns and over the chunk's tokens,
-//      then dq, dk, dlog alpha and dbeta.
+//   CH chain waves (32 value columns each; D in fp32 registers): dU, dR,
+//      dv = beta dR, the carried gradient's update, and dR, Dg published to
+//      LDS in row order (each 16 x 16 tile transposed by an MFMA with the
+//      identity); beside it the leaf waves solve U = (I + L)^-1 beta W0,
+//      which only the later stages use;
+//   LA every wave: the C x C products dA and dL;
+//   LB every wave, one 16-channel tile at a time (S of those rows in
+//      registers, loaded at the chunk's start): the products reduced over the
+//      value columns and over the chunk's tokens, then dq, dk, dlog alpha and
+//      dbeta.
 // Every product of two operands is an MFMA (bf16 operands for bf16 inputs,
 // fp32 for fp32 inputs) with fp32 accumulation; the carried gradient is fp32.
 #include <hip/hip_runtime.h>
@@ -107,7 +109,7 @@ struct BcLayout {
     static constexpr size_t SZ_TB = bc_align16(static_cast<size_t>(NB) * 16 * LB * ES);
     static constexpr size_t O_KT = 0;  // K~ rows; U rows from stage CH on
     static constexpr size_t O_KH = O_KT + SZ_CK;
-    static constexpr size_t O_QT = O_KH + SZ_CK;  // Q~ rows; dR rows from stage CH on
+    static constexpr size_t O_QT = O_KH + SZ_CK;  // Q~ rows; -dR rows from stage CH on
     static constexpr size_t O_KTT = O_QT + SZ_CK;  // K~^T
     static constexpr size_t O_QTT = O_KTT + SZ_TK;  // Q~^T
     static constexpr size_t O_KHT = O_QTT + SZ_TK;  // K^^T
@@ -123,12 +125,13 @@ struct BcLayout {
     static constexpr size_t O_BDLT = O_DL + SZ_CC;  // (beta dL)^T  [s][r]
     static constexpr size_t O_TN = O_BDLT + SZ_CC;  // -T_bb        [r][c] per block
     static constexpr size_t O_TT = O_TN + SZ_TB;    // T_bb^T       [r][c] per block
-    static constexpr size_t O_BETA = O_TT + SZ_TB;
+    static constexpr size_t O_G = O_TT + SZ_TB;  // cumulative log2 decay [C][DK] fp32
+    static constexpr size_t O_BETA = O_G + bc_align16(static_cast<size_t>(4) * C * DK);
     static constexpr size_t O_GC = O_BETA + bc_align16(4 * C);
     static constexpr size_t O_DB = O_GC + bc_align16(4 * DK);
     static constexpr size_t O_DBL = O_DB + bc_align16(4 * NC * C);
     static constexpr size_t O_SG = O_DBL + bc_align16(4 * NJOB * C);
-    static constexpr size_t O_SCAN = O_SG + bc_align16(4 * NL * C);
+    static constexpr size_t O_SCAN = O_SG + bc_align16(4 * (DK / 16) * C);
     static constexpr size_t O_SEQ = O_SCAN + static_cast<size_t>(NPS) * 64 * 16;
     static constexpr size_t BYTES = O_SEQ + bc_align16(4 * (kBcSortMax + 1));
     static_assert(BYTES <= 160 * 1024, "LDS budget of one gfx950 workgroup");
@@ -156,15 +159,6 @@ template <int CTRL>
 __device__ __forceinline__ float bc_dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-// Inclusive prefix sum over the 16 lanes of each row (row_shr 1, 2, 4, 8;
-// lanes shifted in from outside the row contribute zero).
-__device__ __forceinline__ float row_prefix(float x) {
-    x += bc_dpp<0x111>(x);
-    x += bc_dpp<0x112>(x);
-    x += bc_dpp<0x114>(x);
-    x += bc_dpp<0x118>(x);
-    return x;
-}
 // Inclusive suffix sum over the 16 lanes of each row (row_shl 1, 2, 4, 8).
 __device__ __forceinline__ float row_suffix(float x) {
     x += bc_dpp<0x101>(x);
@@ -173,12 +167,14 @@ __device__ __forceinline__ float row_suffix(float x) {
     x += bc_dpp<0x108>(x);
     return x;
 }
-// Sum over the 16 lanes of each row, in every lane of the row.
+// Sum over the 16 lanes of each row, the same bits in every lane of the row:
+// DPP butterflies within the row (quad permutations [1,0,3,2] and [2,3,0,1],
+// then the half-row and the row mirror), no trip through LDS.
 __device__ __forceinline__ float row_sum(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
+    x += bc_dpp<0xB1>(x);
+    x += bc_dpp<0x4E>(x);
+    x += bc_dpp<0x141>(x);
+    x += bc_dpp<0x140>(x);
     return x;
 }
 
@@ -239,6 +235,9 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
     constexpr int LK = Ly::LK, LT = Ly::LT, LO = Ly::LO, LS = Ly::LS, LB = Ly::LB;
     constexpr int NRG = Ly::NRG, QW = Ly::QW, NQ = Ly::NQ, NPS = Ly::NPS, DPT = Ly::DPT;
     constexpr int KBK = DK / 32, KBV = DV / 32;
+    constexpr int NW = Ly::NW;
+    constexpr int NCT = DK / 16;                    // 16-channel tiles of stage LB
+    constexpr int TPW = (NCT + NW - 1) / NW;        // stage LB tiles per wave
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Ly::BYTES];
     E* const tKt = reinterpret_cast<E*>(smem + Ly::O_KT);
@@ -261,6 +260,7 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
     E* const tbdLt = reinterpret_cast<E*>(smem + Ly::O_BDLT);
     E* const tTn = reinterpret_cast<E*>(smem + Ly::O_TN);
     E* const tTt = reinterpret_cast<E*>(smem + Ly::O_TT);
+    float* const sG = reinterpret_cast<float*>(smem + Ly::O_G);
     float* const sBeta = reinterpret_cast<float*>(smem + Ly::O_BETA);
     float* const sGC = reinterpret_cast<float*>(smem + Ly::O_GC);
     float* const sDb = reinterpret_cast<float*>(smem + Ly::O_DB);
@@ -304,7 +304,7 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
     // The C x C tiles' blocks above the diagonal are never written: zero once.
     {
         uint4* z = reinterpret_cast<uint4*>(smem + Ly::O_L);
-        constexpr int NZ = static_cast<int>((Ly::O_BETA - Ly::O_L) / 16);
+        constexpr int NZ = static_cast<int>((Ly::O_G - Ly::O_L) / 16);
         for (int i = tid; i < NZ; i += NT) z[i] = make_uint4(0u, 0u, 0u, 0u);
     }
 
@@ -314,9 +314,8 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
 
     // ---- registers ------------------------------------------------------
     f32x4_t dS[2][DK / 16];  // chain: dL/dS entering the chunk after the current one (C layout)
-    F4 w0c[2][NB], w0n[2][NB];  // chain: W0 of the current and the next chunk (C layout)
+    F4 w0c[2][NB];              // W0 of the current chunk, one 32-column block (C layout)
     R4 rdo[DPT][4];             // chain: raw dO rows of the next chunk
-    F8 sfc[2][KBV], sfn[2][KBV];  // leaf: S rows 32 v + 16 ci + ln, value-column fragments
     R4 rk[4], rq[4];              // strip waves: raw k, q of the next chunk
     float4 rla[4];
     float rbeta = 0.f;
@@ -340,9 +339,15 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
     const bool strip_wave = !is_chain && strip < NPS;
     const bool loads_beta = strip_wave && strip == 0 && lane < C;
 
-    auto issue_chain = [&](int m) __attribute__((always_inline)) {
-        const int t0 = t_beg + m * C;
-        const int rows = __builtin_amdgcn_readfirstlane(rows_of(m));
+    // Loads of chunk inputs.  Every load is unconditional: a chunk index below
+    // 0, and waves or lanes without the data, read through empty buffer
+    // ranges (zero, no memory touched).  The compiler's vmcnt waits then count
+    // exactly, and a use of one chunk's data never waits for a later prefetch.
+    auto rows_or0 = [&](int m) __attribute__((always_inline)) { return m >= 0 ? rows_of(m) : 0; };
+    // chain: raw dO rows of chunk m (issued at the end of the chunk after it)
+    auto issue_dO = [&](int m) __attribute__((always_inline)) {
+        const int t0 = t_beg + max(m, 0) * C;
+        const int rows = __builtin_amdgcn_readfirstlane(rows_or0(m));
         const auto rdo_r = buffer_rsrc(doh + static_cast<size_t>(t0) * H * DV, rows * rowV);
 #pragma unroll
         for (int t = 0; t < DPT; ++t) {
@@ -353,47 +358,42 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) rdo[t][rr] = bc_load_raw4<BF16>(rdo_r, off, rr * rowV);
         }
+    };
+    // W0 of chunk m, 32-column block cb (chain: block w for dbeta in stage CH;
+    // leaf: the blocks of stage U)
+    auto load_w0_block = [&](int m, int cb) __attribute__((always_inline)) {
         const E* wb = static_cast<const E*>(a.ckw) + ((slot0 + m) * H + h) * C * DV;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
             for (int rt = 0; rt < NB; ++rt)
-                w0n[ct][rt] = *reinterpret_cast<const F4*>(wb + (static_cast<size_t>((2 * w + ct) * NB + rt) * 64 + lane) * 4);
+                w0c[ct][rt] = *reinterpret_cast<const F4*>(wb + (static_cast<size_t>((2 * cb + ct) * NB + rt) * 64 + lane) * 4);
         }
     };
-    auto issue_leaf = [&](int m) __attribute__((always_inline)) {
-        const int t0 = t_beg + m * C;
-        const int rows = __builtin_amdgcn_readfirstlane(rows_of(m));
-        const E* sb = static_cast<const E*>(a.cks) + ((slot0 + m) * H + h) * DK * DV;
+    auto load_w0 = [&](int m) __attribute__((always_inline)) { load_w0_block(m, is_chain ? w : min(v, DV / 32 - 1)); };
+    // leaf strip waves: k, q, log alpha and beta rows of chunk m (one chunk ahead)
+    auto issue_strip = [&](int m) __attribute__((always_inline)) {
+        const int t0 = t_beg + max(m, 0) * C;
+        const int rows = __builtin_amdgcn_readfirstlane(strip_wave ? rows_or0(m) : 0);
+        const size_t tok = static_cast<size_t>(t0) * H * DK;
+        const auto rk_r = buffer_rsrc(kh + tok, rows * rowK);
+        const auto rq_r = buffer_rsrc(qh + tok, rows * rowK);
+        const auto rl_r = buffer_rsrc(lah + static_cast<size_t>(t0) * strideLA, rows * rowLA);
+        const auto rb_r = buffer_rsrc(bh + static_cast<size_t>(t0) * H, rows * rowB);
+        const int offK = 4 * rg * rowK + i0 * GS;
+        const int offLA = 4 * rg * rowLA + (SG ? 0 : i0 * 4);
+        rbeta = buf_load_f1(rb_r, loads_beta ? lane * rowB : kNoAccess, 0);
 #pragma unroll
-        for (int ci = 0; ci < 2; ++ci) {
-#pragma unroll
-            for (int kb = 0; kb < KBV; ++kb)
-                sfn[ci][kb] = *reinterpret_cast<const F8*>(
-                    sb + (static_cast<size_t>((2 * v + ci) * KBV + kb) * 64 + lane) * 8);
-        }
-        if (strip_wave) {
-            const size_t tok = static_cast<size_t>(t0) * H * DK;
-            const auto rk_r = buffer_rsrc(kh + tok, rows * rowK);
-            const auto rq_r = buffer_rsrc(qh + tok, rows * rowK);
-            const auto rl_r = buffer_rsrc(lah + static_cast<size_t>(t0) * strideLA, rows * rowLA);
-            const auto rb_r = buffer_rsrc(bh + static_cast<size_t>(t0) * H, rows * rowB);
-            const int offK = 4 * rg * rowK + i0 * GS;
-            const int offLA = 4 * rg * rowLA + (SG ? 0 : i0 * 4);
-            rbeta = buf_load_f1(rb_r, loads_beta ? lane * rowB : kNoAccess, 0);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                if constexpr (SG) {
-                    const float x = buf_load_f1(rl_r, offLA, rr * rowLA);
-                    rla[rr] = make_float4(x, x, x, x);
-                } else {
-                    rla[rr] = buf_load_f4(rl_r, offLA, rr * rowLA);
-                }
-                rk[rr] = bc_load_raw4<BF16>(rk_r, offK, rr * rowK);
-                rq[rr] = bc_load_raw4<BF16>(rq_r, offK, rr * rowK);
+        for (int rr = 0; rr < 4; ++rr) {
+            if constexpr (SG) {
+                const float x = buf_load_f1(rl_r, offLA, rr * rowLA);
+                rla[rr] = make_float4(x, x, x, x);
+            } else {
+                rla[rr] = buf_load_f4(rl_r, offLA, rr * rowLA);
             }
+            rk[rr] = bc_load_raw4<BF16>(rk_r, offK, rr * rowK);
+            rq[rr] = bc_load_raw4<BF16>(rq_r, offK, rr * rowK);
         }
-
     };
 
     __syncthreads();  // zeroed tiles visible
@@ -404,17 +404,232 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
     for (int j = 0; j < 4; ++j) eye[j] = T::to_e(4 * lg + j == ln ? 1.f : 0.f);
     const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
 
-    // scalar gate: dlog alpha of one head summed over the channels of every
-    // leaf wave (partials in sSG), stored for chunk m
+    // scalar gate: dlog alpha of one head, the sum of the channel tiles'
+    // partials (sSG), stored for chunk m by the first leaf wave
     auto flush_sg = [&](int m) __attribute__((always_inline)) {
         if constexpr (SG) {
             if (wave == NC && lane < rows_of(m)) {
                 float s = 0.f;
 #pragma unroll
-                for (int u = 0; u < NL; ++u) s += sSG[u * C + lane];
+                for (int u = 0; u < NCT; ++u) s += sSG[u * C + lane];
                 a.dla[static_cast<size_t>(t_beg + m * C + lane) * H + h] = s;
             }
         }
+    };
+
+    // ---- stages that every wave shares -----------------------------------
+    // S rows of channel tile cti (channels 16 cti .. + 15) of chunk m, as
+    // A-operand fragments over the value columns
+    auto load_stile = [&](int m, int cti, F8 (&sf)[KBV]) __attribute__((always_inline)) {
+        const E* sb = static_cast<const E*>(a.cks) + ((slot0 + m) * H + h) * DK * DV;
+#pragma unroll
+        for (int kb = 0; kb < KBV; ++kb)
+            sf[kb] = *reinterpret_cast<const F8*>(sb + (static_cast<size_t>(cti * KBV + kb) * 64 + lane) * 8);
+    };
+    // raw k and q of chunk m for channel tile cti in the epilogue layout
+    // (lane: token 16 rt + ln, channels 16 cti + 4 lg .. + 3); rows past the
+    // chunk read zero
+    auto load_kq = [&](int m, int cti, R4 (&ek)[NB], R4 (&eq)[NB]) __attribute__((always_inline)) {
+        const int nrow = __builtin_amdgcn_readfirstlane(rows_of(m));
+        const size_t tok = static_cast<size_t>(t_beg + m * C) * H * DK;
+        const auto rk_r = buffer_rsrc(kh + tok, nrow * rowK);
+        const auto rq_r = buffer_rsrc(qh + tok, nrow * rowK);
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+            const int off = (16 * rt + ln) * rowK + (16 * cti + 4 * lg) * GS;
+            ek[rt] = bc_load_raw4<BF16>(rk_r, off, 0);
+            eq[rt] = bc_load_raw4<BF16>(rq_r, off, 0);
+        }
+    };
+
+    // Stage LA: the C x C products dA = lower_incl(dO U^T) and
+    // dL = -strictly_lower(dR U^T) (from tDR = -dR), 16 x 16 blocks dealt
+    // round-robin to the waves.
+    auto stage_LA = [&]() __attribute__((always_inline)) {
+        for (int jb = wave; jb < 2 * NJOB; jb += NW) {
+            const bool isA = jb < NJOB;
+            const int jc = isA ? jb : jb - NJOB;
+            const int sb = jc == 2 ? 0 : jc, rb = jc == 2 ? 1 : jc;
+            const E* xa = isA ? tDO : tDR;
+            const int lda = isA ? LO : LK;
+            f32x4_t acc = z4;
+#pragma unroll
+            for (int kb = 0; kb < KBV; ++kb)
+                acc = mma8<BF16>(acc, lds_frag8<BF16>(xa + 16 * rb * lda + 32 * kb, lda, lane),
+                                 lds_frag8<BF16>(tU + 16 * sb * LK + 32 * kb, LK, lane));
+            // lane (ln = s): rows r = 16 rb + 4 lg + j of column s = 16 sb + ln
+            const int s = 16 * sb + ln;
+            const float4 b4 = *reinterpret_cast<const float4*>(sBeta + 16 * rb + 4 * lg);
+            const float bj[4] = {b4.x, b4.y, b4.z, b4.w};
+            f32x4_t x;
+            if (isA) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = (s <= 16 * rb + 4 * lg + j) ? acc[j] : 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) tdA[(16 * rb + 4 * lg + j) * LT + s] = T::to_e(x[j]);
+                bc_put4<BF16>(tdAt + s * LT + 16 * rb + 4 * lg, x[0], x[1], x[2], x[3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = (s < 16 * rb + 4 * lg + j) ? acc[j] : 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) tdL[(16 * rb + 4 * lg + j) * LT + s] = T::to_e(x[j]);
+                bc_put4<BF16>(tbdLt + s * LT + 16 * rb + 4 * lg, bj[0] * x[0], bj[1] * x[1], bj[2] * x[2],
+                              bj[3] * x[3]);
+                // second term of dbeta: sum over s of dL[r][s] G[r][s]
+                const f32x4_t gv = bc_widen<BF16>(*reinterpret_cast<const F4*>(tGt + s * LT + 16 * rb + 4 * lg));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float t = row_sum(x[j] * gv[j]);
+                    if (ln == 0) sDbL[jc * C + 16 * rb + 4 * lg + j] = t;
+                }
+            }
+        }
+    };
+
+    // Stage LB for channel tile cti: the products over the value columns and
+    // over the chunk's tokens, then dq, dk and dlog alpha of those 16 channels
+    // for every token of the chunk.
+    auto lb_tile = [&](int cti, const F8 (&sf)[KBV], const R4 (&ek)[NB], const R4 (&eq)[NB], int t0, int rows)
+        __attribute__((always_inline)) {
+        const int crow = 16 * cti;
+        // value-column products, one 32-column block at a time:
+        //   aq = S dO^T,  akk = -S dR^T (tDR holds -dR),  akb = Dg U^T
+        // and c = sum_j S_ij Dg_ij
+        f32x4_t aq[NB], akk[NB], akh[NB], akb[NB];
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+            aq[rt] = z4;
+            akk[rt] = z4;
+            akb[rt] = z4;
+        }
+        float cpart = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KBV; ++kb) {
+            const F8 dga = lds_frag8<BF16>(tDS + crow * LS + 32 * kb, LS, lane);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                cpart = __builtin_fmaf(static_cast<float>(sf[kb][e]), static_cast<float>(dga[e]), cpart);
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) {
+                aq[rt] = mma8<BF16>(aq[rt], sf[kb], lds_frag8<BF16>(tDO + 16 * rt * LO + 32 * kb, LO, lane));
+                akk[rt] = mma8<BF16>(akk[rt], sf[kb], lds_frag8<BF16>(tDR + 16 * rt * LK + 32 * kb, LK, lane));
+                akb[rt] = mma8<BF16>(akb[rt], dga, lds_frag8<BF16>(tU + 16 * rt * LK + 32 * kb, LK, lane));
+            }
+        }
+        // c for channel crow + ln, in every lane of that column
+        cpart += __shfl_xor(cpart, 16);
+        cpart += __shfl_xor(cpart, 32);
+        // token products: dQ~ += dA K^, dK~ / beta = dL K^ - dR S^T, dK^ = dA^T Q~ + (beta dL)^T K~
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+            aq[rt] = mma_rows<BF16, C>(aq[rt], tKhT + crow * LT, LT, tdA + 16 * rt * LT, LT, lane);
+            akk[rt] = mma_rows<BF16, C>(akk[rt], tKhT + crow * LT, LT, tdL + 16 * rt * LT, LT, lane);
+            akh[rt] = mma_rows<BF16, C>(z4, tQtT + crow * LT, LT, tdAt + 16 * rt * LT, LT, lane);
+            akh[rt] = mma_rows<BF16, C>(akh[rt], tKtT + crow * LT, LT, tbdLt + 16 * rt * LT, LT, lane);
+        }
+        // epilogue: lane (ln, lg) holds channels ch0 .. ch0 + 3 of token 16 rt + ln
+        const int ch0 = crow + 4 * lg;
+        float dg[NB][4], ex[4] = {0.f, 0.f, 0.f, 0.f};
+        float dqv[NB][4], dkv[NB][4];
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+            const int r = 16 * rt + ln;
+            float kk[4], qq[4];
+            T::unpack4(ek[rt], kk);
+            T::unpack4(eq[rt], qq);
+            // cumulative decay (log2 units) of these channels up to token r
+            const float4 g4 = *reinterpret_cast<const float4*>(sG + r * DK + ch0);
+            const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+            const float br = sBeta[r];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float p = gv[j];
+                const float gm = __builtin_amdgcn_exp2f(p), ig = __builtin_amdgcn_exp2f(-p);
+                const float dqt = aq[rt][j];
+                const float dkt = br * akk[rt][j];
+                const float dkh = akh[rt][j] + akb[rt][j];
+                const float a1 = dkt * gm, a2 = dkh * ig, a3 = dqt * gm;
+                dqv[rt][j] = a3;
+                dkv[rt][j] = a1 + a2;
+                dg[rt][j] = kk[j] * (a1 - a2) + qq[j] * a3;
+                ex[j] = __builtin_fmaf(akb[rt][j] * kk[j], ig, ex[j]);
+            }
+        }
+        // extra term of every row: c (moved to the epilogue layout) plus the
+        // sum over the chunk's tokens of dKbar' k / Gamma
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ex[j] = row_sum(ex[j]) + __shfl(cpart, 4 * lg + j);
+        // suffix sums of dg over the tokens, from the last block
+        const int rowDK = H * DK * 4;
+        const size_t gbase = (static_cast<size_t>(t0) * H + h) * DK;
+        const auto dq_r = buffer_rsrc(a.dq + gbase, rows * rowDK);
+        const auto dk_r = buffer_rsrc(a.dk + gbase, rows * rowDK);
+        const auto dla_r = buffer_rsrc(a.dla + (SG ? 0 : gbase), SG ? 0 : rows * rowDK);
+        const int eo = ln * rowDK + 4 * ch0;
+        float sfx[4] = {0.f, 0.f, 0.f, 0.f};
+        float sg_row[NB];
+#pragma unroll
+        for (int rt = NB - 1; rt >= 0; --rt) {
+            float out[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float sv = row_suffix(dg[rt][j]) + sfx[j];
+                sfx[j] += row_sum(dg[rt][j]);
+                out[j] = sv + ex[j];
+            }
+            // rows past the sequence fall outside the buffer ranges
+            buf_store_f4(dq_r, eo, 16 * rt * rowDK, dqv[rt][0], dqv[rt][1], dqv[rt][2], dqv[rt][3]);
+            buf_store_f4(dk_r, eo, 16 * rt * rowDK, dkv[rt][0], dkv[rt][1], dkv[rt][2], dkv[rt][3]);
+            if constexpr (!SG) buf_store_f4(dla_r, eo, 16 * rt * rowDK, out[0], out[1], out[2], out[3]);
+            sg_row[rt] = (out[0] + out[1]) + (out[2] + out[3]);
+        }
+        if constexpr (SG) {
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) {
+                float sv = sg_row[rt];
+                sv += __shfl_xor(sv, 16);
+                sv += __shfl_xor(sv, 32);
+                if (lg == 0) sSG[cti * C + 16 * rt + ln] = sv;
+            }
+        }
+    };
+    // Stage LB of this wave: channel tiles wave, wave + NW, ...; the first
+    // tile's S rows and k, q were loaded at the chunk's start.
+    auto stage_LB = [&](int m, const F8 (&sf0)[KBV], const R4 (&ek0)[NB], const R4 (&eq0)[NB])
+        __attribute__((always_inline)) {
+        const int t0 = t_beg + m * C;
+        const int rows = rows_of(m);
+        if (wave < NCT) lb_tile(wave, sf0, ek0, eq0, t0, rows);
+#pragma unroll
+        for (int k2 = 1; k2 < TPW; ++k2) {
+            const int cti = wave + k2 * NW;
+            if (cti < NCT) {
+                F8 sf[KBV];
+                R4 ek[NB], eq[NB];
+                load_stile(m, cti, sf);
+                load_kq(m, cti, ek, eq);
+                lb_tile(cti, sf, ek, eq, t0, rows);
+            }
+        }
+        // dbeta of the chunk's tokens: the chain waves' partials plus the C x C term
+        if (wave == NW - 1 && lane < rows) {
+            float sv = 0.f;
+#pragma unroll
+            for (int u = 0; u < NC; ++u) sv += sDb[u * C + lane];
+            const int rb = lane >> 4;
+#pragma unroll
+            for (int jc = 0; jc < NJOB; ++jc) {
+                const int rbj = jc == 2 ? 1 : jc;
+                if (rbj == rb) sv += sDbL[jc * C + lane];
+            }
+            a.dbeta[static_cast<size_t>(t0 + lane) * H + h] = sv;
+        }
+    };
+    // the first LB tile's operands for chunk m, loaded at the chunk's start
+    auto load_lb0 = [&](int m, F8 (&sf0)[KBV], R4 (&ek0)[NB], R4 (&eq0)[NB]) __attribute__((always_inline)) {
+        const int cti0 = min(wave, NCT - 1);
+        load_stile(m, cti0, sf0);
+        load_kq(m, cti0, ek0, eq0);
     };
 
     if (is_chain) {
@@ -429,8 +644,10 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
                     dS[ct][it][j] = a.dST ? a.dST[pair * DK * DV + static_cast<size_t>(16 * it + 4 * lg + j) * DV + col] : 0.f;
             }
         }
-        if (nch > 0) issue_chain(nch - 1);
+        issue_dO(nch - 1);
         for (int m = nch - 1; m >= 0; --m) {
+            // =============================== P: dO rows; this chunk's loads
+            load_w0(m);
             const int t0 = t_beg + m * C;
             const int rows = rows_of(m);
 #pragma unroll
@@ -442,12 +659,6 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
                     for (int rr = 0; rr < 4; ++rr) T::lds_put_raw4(tDO + (r0 + rr) * LO + c4, rdo[t][rr]);
                 }
             }
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-#pragma unroll
-                for (int rt = 0; rt < NB; ++rt) w0c[ct][rt] = w0n[ct][rt];
-            }
-            if (m > 0) issue_chain(m - 1);
             bc_barrier();
 
             // =============================== J: C x C products and block inverses
@@ -538,28 +749,11 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
                 if constexpr (NB == 2) return mma8<BF16>(acc, lds_frag8<BF16>(arow, ld, lane), dof8[ct]);
                 else return mma4<BF16>(acc, lds_frag4<BF16>(arow, ld, lane), dof4[ct][0]);
             };
-            // U = (I + L)^-1 beta W0, block by block: U_b = (-T_bb)(-beta W0_b + sum_{c<b} L_bc U_c)
-            f32x4_t U[2][NB], w0f[2][NB];
-            F4 uf[2][NB];
+            f32x4_t w0f[2][NB];
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
                 for (int rt = 0; rt < NB; ++rt) w0f[ct][rt] = bc_widen<BF16>(w0c[ct][rt]);
-            }
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const F4 tb = lds_frag4<BF16>(tTn + 16 * b * LB, LB, lane);
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    f32x4_t y;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) y[j] = -(bt[b][j] * w0f[ct][b][j]);
-#pragma unroll
-                    for (int c = 0; c < b; ++c)
-                        y = mma4<BF16>(y, lds_frag4<BF16>(tL + 16 * b * LT + 16 * c, LT, lane), uf[ct][c]);
-                    U[ct][b] = mma4<BF16>(z4, tb, acc_frag4<BF16>(y));
-                    uf[ct][b] = acc_frag4<BF16>(U[ct][b]);
-                }
             }
             // Dg = Gamma_C D (rows scaled), as B-operand fragments over the key channels
             F8 dgf[2][KBK];
@@ -601,18 +795,20 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
                     drf[ct][b] = acc_frag4<BF16>(dR[ct][b]);
                 }
             }
-            // dv = beta dR (fp32, from the C layout: lane holds 4 tokens of one column),
-            // and the first term of dbeta, sum over this wave's columns of dR * W0
+            // dv = beta dR (fp32, from the C layout: lane holds 4 tokens of one column;
+            // rows past the sequence fall outside the buffer range), and the first
+            // term of dbeta, sum over this wave's columns of dR * W0
+            const int rowDV = H * DV * 4;
+            const auto dv_r = buffer_rsrc(a.dv + (static_cast<size_t>(t0) * H + h) * DV, rows * rowDV);
+            const int dvo = 4 * lg * rowDV + 4 * (32 * w + ln);
 #pragma unroll
             for (int rt = 0; rt < NB; ++rt) {
                 float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
-                    const int col = 32 * w + 16 * ct + ln;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int r = 16 * rt + 4 * lg + j;
-                        if (r < rows) a.dv[(static_cast<size_t>(t0 + r) * H + h) * DV + col] = bt[rt][j] * dR[ct][rt][j];
+                        buf_store_f1(dv_r, dvo + 64 * ct, (16 * rt + j) * rowDV, bt[rt][j] * dR[ct][rt][j]);
                         part[j] = __builtin_fmaf(dR[ct][rt][j], w0f[ct][rt][j], part[j]);
                     }
                 }
@@ -622,16 +818,14 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
                     if (ln == 0) sDb[w * C + 16 * rt + 4 * lg + j] = s;
                 }
             }
-            // publish U and dR rows (transposed by the identity product) and Dg rows
+            // publish -dR rows (transposed by the identity product) and Dg rows
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
                 for (int rt = 0; rt < NB; ++rt) {
                     const int off = (16 * rt + ln) * LK + 32 * w + 16 * ct + 4 * lg;
-                    const f32x4_t tu = mma4<BF16>(z4, uf[ct][rt], eye);
-                    bc_put4<BF16>(tU + off, tu[0], tu[1], tu[2], tu[3]);
                     const f32x4_t tr = mma4<BF16>(z4, drf[ct][rt], eye);
-                    bc_put4<BF16>(tDR + off, tr[0], tr[1], tr[2], tr[3]);
+                    bc_put4<BF16>(tDR + off, -tr[0], -tr[1], -tr[2], -tr[3]);
                 }
 #pragma unroll
                 for (int it = 0; it < DK / 16; ++it) {
@@ -670,9 +864,18 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
                     dS[ct][it] = acc;
                 }
             }
+            // stage LB's operands, in flight during stage LA (the registers of
+            // stage CH are free again)
+            F8 sf0[KBV];
+            R4 ek0[NB], eq0[NB];
+            load_lb0(m, sf0, ek0, eq0);
             bc_barrier();
-            bc_barrier();  // LA (leaf waves)
-            bc_barrier();  // LB (leaf waves)
+            stage_LA();
+            bc_barrier();
+            stage_LB(m, sf0, ek0, eq0);
+            // the next chunk's dO rows (in flight over the leaf waves' stage P)
+            issue_dO(m - 1);
+            bc_barrier();
         }
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
@@ -685,16 +888,14 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
             }
         }
     } else {
-        if (nch > 0) issue_leaf(nch - 1);
+        issue_strip(nch - 1);
         for (int m = nch - 1; m >= 0; --m) {
-            const int t0 = t_beg + m * C;
-            const int rows = rows_of(m);
             if (m + 1 < nch) flush_sg(m + 1);
-#pragma unroll
-            for (int ci = 0; ci < 2; ++ci) {
-#pragma unroll
-                for (int kb = 0; kb < KBV; ++kb) sfc[ci][kb] = sfn[ci][kb];
-            }
+            // =============================== P: operand tiles; this chunk's loads
+            load_w0(m);  // the first 32-column block of stage U
+            F8 sf0[KBV];
+            R4 ek0[NB], eq0[NB];
+            load_lb0(m, sf0, ek0, eq0);
             if (strip_wave) {
                 if (loads_beta) sBeta[lane] = rbeta;
                 if (qok) {
@@ -742,6 +943,7 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
                             kh4[rr][c] = kk[c] * __builtin_amdgcn_exp2f(-g[c]);
                             qt[rr][c] = qq[c] * gm;
                         }
+                        *reinterpret_cast<float4*>(sG + r * DK + i0) = make_float4(g[0], g[1], g[2], g[3]);
                         bc_put4<BF16>(tKt + r * LK + i0, kt[rr][0], kt[rr][1], kt[rr][2], kt[rr][3]);
                         bc_put4<BF16>(tKh + r * LK + i0, kh4[rr][0], kh4[rr][1], kh4[rr][2], kh4[rr][3]);
                         bc_put4<BF16>(tQt + r * LK + i0, qt[rr][0], qt[rr][1], qt[rr][2], qt[rr][3]);
@@ -755,191 +957,49 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
                     }
                 }
             }
-            if (m > 0) issue_leaf(m - 1);
+            issue_strip(m - 1);
             bc_barrier();
             bc_barrier();  // J (chain waves)
-            bc_barrier();  // CH (chain waves)
 
-            // =============================== LA: dA and dL (C x C), leaf waves
-            for (int jb = v; jb < 2 * NJOB; jb += NL) {
-                const bool isA = jb < NJOB;
-                const int jc = isA ? jb : jb - NJOB;
-                const int sb = jc == 2 ? 0 : jc, rb = jc == 2 ? 1 : jc;
-                const E* xa = isA ? tDO : tDR;
-                const int lda = isA ? LO : LK;
-                f32x4_t acc = z4;
+            // =============================== U: (I + L) U = beta W0 (32-column blocks v, v + NL, ...)
+            // Only stages LA and LB use U, so it is solved beside stage CH,
+            // off the carried gradient's chain.
+            for (int cb = v; cb < DV / 32; cb += NL) {
+                if (cb != v) load_w0_block(m, cb);
+                float bt[NB][4];
 #pragma unroll
-                for (int kb = 0; kb < KBV; ++kb)
-                    acc = mma8<BF16>(acc, lds_frag8<BF16>(xa + 16 * rb * lda + 32 * kb, lda, lane),
-                                     lds_frag8<BF16>(tU + 16 * sb * LK + 32 * kb, LK, lane));
-                // lane (ln = s): rows r = 16 rb + 4 lg + j of column s = 16 sb + ln
-                const int s = 16 * sb + ln;
-                const float4 b4 = *reinterpret_cast<const float4*>(sBeta + 16 * rb + 4 * lg);
-                const float bj[4] = {b4.x, b4.y, b4.z, b4.w};
-                f32x4_t x;
-                if (isA) {
+                for (int rt = 0; rt < NB; ++rt) {
+                    const float4 b4 = *reinterpret_cast<const float4*>(sBeta + 16 * rt + 4 * lg);
+                    bt[rt][0] = b4.x;
+                    bt[rt][1] = b4.y;
+                    bt[rt][2] = b4.z;
+                    bt[rt][3] = b4.w;
+                }
+                // U_b = (-T_bb)(-beta W0_b + sum_{c<b} L_bc U_c); each 16 x 16 tile of U
+                // goes to LDS as rows (transposed by the identity product)
+                F4 uf[2][NB];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) x[j] = (s <= 16 * rb + 4 * lg + j) ? acc[j] : 0.f;
+                for (int b = 0; b < NB; ++b) {
+                    const F4 tb = lds_frag4<BF16>(tTn + 16 * b * LB, LB, lane);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) tdA[(16 * rb + 4 * lg + j) * LT + s] = T::to_e(x[j]);
-                    bc_put4<BF16>(tdAt + s * LT + 16 * rb + 4 * lg, x[0], x[1], x[2], x[3]);
-                } else {
+                    for (int ct = 0; ct < 2; ++ct) {
+                        const f32x4_t w0f = bc_widen<BF16>(w0c[ct][b]);
+                        f32x4_t y;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) x[j] = (s < 16 * rb + 4 * lg + j) ? -acc[j] : 0.f;
+                        for (int j = 0; j < 4; ++j) y[j] = -(bt[b][j] * w0f[j]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) tdL[(16 * rb + 4 * lg + j) * LT + s] = T::to_e(x[j]);
-                    bc_put4<BF16>(tbdLt + s * LT + 16 * rb + 4 * lg, bj[0] * x[0], bj[1] * x[1], bj[2] * x[2],
-                                  bj[3] * x[3]);
-                    // second term of dbeta: sum over s of dL[r][s] G[r][s]
-                    const f32x4_t gv = bc_widen<BF16>(*reinterpret_cast<const F4*>(tGt + s * LT + 16 * rb + 4 * lg));
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float t = row_sum(x[j] * gv[j]);
-                        if (ln == 0) sDbL[jc * C + 16 * rb + 4 * lg + j] = t;
+                        for (int c = 0; c < b; ++c)
+                            y = mma4<BF16>(y, lds_frag4<BF16>(tL + 16 * b * LT + 16 * c, LT, lane), uf[ct][c]);
+                        uf[ct][b] = acc_frag4<BF16>(mma4<BF16>(z4, tb, acc_frag4<BF16>(y)));
+                        const f32x4_t tu = mma4<BF16>(z4, uf[ct][b], eye);
+                        bc_put4<BF16>(tU + (16 * b + ln) * LK + 32 * cb + 16 * ct + 4 * lg, tu[0], tu[1], tu[2], tu[3]);
                     }
                 }
             }
             bc_barrier();
-
-            // =============================== LB: gradients of the chunk's tokens, leaf waves
-            const float* const lar = a.la + (SG ? static_cast<size_t>(h) : static_cast<size_t>(h) * DK);
-            float sgp[NB][4];  // scalar gate: this wave's partial sums per token (lane ln of each row)
-#pragma unroll
-            for (int rt = 0; rt < NB; ++rt) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sgp[rt][j] = 0.f;
-            }
-            float sg_row[NB];
-#pragma unroll
-            for (int rt = 0; rt < NB; ++rt) sg_row[rt] = 0.f;
-#pragma unroll
-            for (int ci = 0; ci < 2; ++ci) {
-                const int crow = 32 * v + 16 * ci;  // first channel of this tile
-                F8 dga[KBV];
-                float cpart = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < KBV; ++kb) {
-                    dga[kb] = lds_frag8<BF16>(tDS + crow * LS + 32 * kb, LS, lane);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        cpart = __builtin_fmaf(static_cast<float>(sfc[ci][kb][e]), static_cast<float>(dga[kb][e]), cpart);
-                }
-                // c for channel crow + ln, in every lane of that column
-                cpart += __shfl_xor(cpart, 16);
-                cpart += __shfl_xor(cpart, 32);
-                f32x4_t aq[NB], aks[NB], akl[NB], akh[NB], akb[NB];
-#pragma unroll
-                for (int rt = 0; rt < NB; ++rt) {
-                    aq[rt] = z4;
-                    aks[rt] = z4;
-                    akb[rt] = z4;
-#pragma unroll
-                    for (int kb = 0; kb < KBV; ++kb) {
-                        aq[rt] = mma8<BF16>(aq[rt], sfc[ci][kb], lds_frag8<BF16>(tDO + 16 * rt * LO + 32 * kb, LO, lane));
-                        aks[rt] = mma8<BF16>(aks[rt], sfc[ci][kb], lds_frag8<BF16>(tDR + 16 * rt * LK + 32 * kb, LK, lane));
-                        akb[rt] = mma8<BF16>(akb[rt], dga[kb], lds_frag8<BF16>(tU + 16 * rt * LK + 32 * kb, LK, lane));
-                    }
-                    aq[rt] = mma_rows<BF16, C>(aq[rt], tKhT + crow * LT, LT, tdA + 16 * rt * LT, LT, lane);
-                    akl[rt] = mma_rows<BF16, C>(z4, tKhT + crow * LT, LT, tdL + 16 * rt * LT, LT, lane);
-                    akh[rt] = mma_rows<BF16, C>(z4, tQtT + crow * LT, LT, tdAt + 16 * rt * LT, LT, lane);
-                    akh[rt] = mma_rows<BF16, C>(akh[rt], tKtT + crow * LT, LT, tbdLt + 16 * rt * LT, LT, lane);
-                }
-                // epilogue: lane (ln, lg) holds channels ch0 .. ch0 + 3 of token 16 rt + ln
-                const int ch0 = crow + 4 * lg;
-                float gsc[NB][4], dg[NB][4], ex[4] = {0.f, 0.f, 0.f, 0.f};
-                float dqv[NB][4], dkv[NB][4];
-                float carry[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int rt = 0; rt < NB; ++rt) {
-                    const int r = 16 * rt + ln;
-                    const bool ok = r < rows;
-                    const size_t tok = static_cast<size_t>(t0 + r) * H;
-                    float la4[4], kk[4], qq[4];
-                    if (ok) {
-                        if constexpr (SG) {
-                            const float x = lar[tok];
-                            la4[0] = la4[1] = la4[2] = la4[3] = x;
-                        } else {
-                            const float4 x = *reinterpret_cast<const float4*>(lar + tok * DK + ch0);
-                            la4[0] = x.x;
-                            la4[1] = x.y;
-                            la4[2] = x.z;
-                            la4[3] = x.w;
-                        }
-                        T::load4(static_cast<const G*>(a.k) + tok * DK + static_cast<size_t>(h) * DK + ch0, kk);
-                        T::load4(static_cast<const G*>(a.q) + tok * DK + static_cast<size_t>(h) * DK + ch0, qq);
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) la4[j] = kk[j] = qq[j] = 0.f;
-                    }
-                    const float br = sBeta[r];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        // cumulative decay (log2 units) of this channel up to token r
-                        const float p = row_prefix(la4[j] * kLog2e) + carry[j];
-                        carry[j] = __shfl(p, (lane & 48) | 15);
-                        gsc[rt][j] = p;
-                        const float gm = __builtin_amdgcn_exp2f(p), ig = __builtin_amdgcn_exp2f(-p);
-                        const float dqt = aq[rt][j];
-                        const float dkt = br * (akl[rt][j] - aks[rt][j]);
-                        const float dkh = akh[rt][j] + akb[rt][j];
-                        const float a1 = dkt * gm, a2 = dkh * ig, a3 = dqt * gm;
-                        dqv[rt][j] = a3;
-                        dkv[rt][j] = a1 + a2;
-                        dg[rt][j] = kk[j] * (a1 - a2) + qq[j] * a3;
-                        ex[j] = __builtin_fmaf(akb[rt][j] * kk[j], ig, ex[j]);
-                    }
-                }
-                (void)gsc;
-                // extra term of every row: c (moved to the epilogue layout) plus the
-                // sum over the chunk's tokens of dKbar' k / Gamma
-#pragma unroll
-                for (int j = 0; j < 4; ++j) ex[j] = row_sum(ex[j]) + __shfl(cpart, 4 * lg + j);
-                // suffix sums of dg over the tokens, from the last block
-                float sfx[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int rt = NB - 1; rt >= 0; --rt) {
-                    const int r = 16 * rt + ln;
-                    float out[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float s = row_suffix(dg[rt][j]) + sfx[j];
-                        sfx[j] = __shfl(s, lane & 48);
-                        out[j] = s + ex[j];
-                    }
-                    if (r < rows) {
-                        const size_t base = (static_cast<size_t>(t0 + r) * H + h) * DK + ch0;
-                        *reinterpret_cast<float4*>(a.dq + base) = make_float4(dqv[rt][0], dqv[rt][1], dqv[rt][2], dqv[rt][3]);
-                        *reinterpret_cast<float4*>(a.dk + base) = make_float4(dkv[rt][0], dkv[rt][1], dkv[rt][2], dkv[rt][3]);
-                        if constexpr (!SG)
-                            *reinterpret_cast<float4*>(a.dla + base) = make_float4(out[0], out[1], out[2], out[3]);
-                    }
-                    if constexpr (SG) sg_row[rt] += (out[0] + out[1]) + (out[2] + out[3]);
-                }
-            }
-            if constexpr (SG) {
-#pragma unroll
-                for (int rt = 0; rt < NB; ++rt) {
-                    float s = sg_row[rt];
-                    s += __shfl_xor(s, 16);
-                    s += __shfl_xor(s, 32);
-                    if (lg == 0) sSG[v * C + 16 * rt + ln] = s;
-                }
-            }
-            (void)sgp;
-            // dbeta of the chunk's tokens: the chain waves' partials plus the C x C term
-            if (v == 0 && lane < C && lane < rows) {
-                float s = 0.f;
-#pragma unroll
-                for (int u = 0; u < NC; ++u) s += sDb[u * C + lane];
-                const int rb = lane >> 4;
-#pragma unroll
-                for (int jc = 0; jc < NJOB; ++jc) {
-                    const int rbj = jc == 2 ? 1 : jc;
-                    if (rbj == rb) s += sDbL[jc * C + lane];
-                }
-                a.dbeta[static_cast<size_t>(t0 + lane) * H + h] = s;
-            }
+            stage_LA();
+            bc_barrier();
+            stage_LB(m, sf0, ek0, eq0);
             bc_barrier();
         }
         if (nch > 0) flush_sg(0);

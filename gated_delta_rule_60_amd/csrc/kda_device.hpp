@@ -240,4 +240,17 @@ __device__ __forceinline__ float buf_load_f1(__amdgpu_buffer_rsrc_t r, int voff,
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// Stores through a buffer range: a store whose offset (voffset + soffset)
+// falls past the range is dropped by the hardware, like the loads above read
+// zero there.
+__device__ __forceinline__ void buf_store_f1(__amdgpu_buffer_rsrc_t r, int voff, int soff, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
+}
+
+__device__ __forceinline__ void buf_store_f4(__amdgpu_buffer_rsrc_t r, int voff, int soff, float a, float b, float c,
+                                             float d) {
+    const u32x4_t x = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
+}
+
 }  // namespace kda

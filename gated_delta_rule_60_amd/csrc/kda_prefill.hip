@@ -651,7 +651,8 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                 const F8 a = tile_frag8<BF16, UK>(tKh(S), 16 * st + ln, kb, lg);
                 const F8 bk = tile_frag8<BF16, UK>(tKb(S), 16 * rt + ln, kb, lg);
                 accL = mma8<BF16>(accL, a, bk);
-                accA = mma8<BF16>(accA, a, tile_frag8<BF16, UK>(tQ(S), 16 * rt + ln, kb, lg));
+                if constexpr (!CK)  // the checkpointing pass forms no outputs
+                    accA = mma8<BF16>(accA, a, tile_frag8<BF16, UK>(tQ(S), 16 * rt + ln, kb, lg));
                 accN = mma8<BF16>(accN, bk, a);  // P^T: C layout of N (used by diagonal jobs)
             }
             Job res;
@@ -912,6 +913,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                     }
                 }
                 ctr_signal(nSolved, lane);
+                if constexpr (CK) ck_store_state(0);
             }
             int P = 0;
             for (int i = 0; i < nchunks; ++i) {
@@ -924,7 +926,6 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
 #pragma unroll
                     for (int t = 0; t < JPW; ++t) jobs[t] = prep3_compute(Pn, t);
                 }
-                if constexpr (CK) ck_store_state(i);
                 chain_R(P, i);
                 chain_UO(P, J);
                 chain_S(P);
@@ -935,6 +936,9 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                         for (int t = 0; t < JPW; ++t) prep3_store(1 - J, t, jobs[t]);
                     }
                     ctr_signal(nSolved, lane);
+                    // the state entering the next chunk, stored while the
+                    // next chunk's hand-offs are awaited
+                    if constexpr (CK) ck_store_state(i + 1);
                 }
                 P = Pn;
             }
@@ -1015,7 +1019,8 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             // chunks past the end: empty ranges, no access (kept in a scalar register)
             const int len = __builtin_amdgcn_readfirstlane(max(0, chunk_len(m)));
             const size_t tok = static_cast<size_t>(c0) * strideK;
-            return Rsrc{buffer_rsrc(kh + tok, len * rowK), buffer_rsrc(qh + tok, len * rowK),
+            // (the checkpointing pass forms no outputs and reads no q: empty range)
+            return Rsrc{buffer_rsrc(kh + tok, len * rowK), buffer_rsrc(qh + tok, CK ? 0 : len * rowK),
                         buffer_rsrc(lah + static_cast<size_t>(c0) * strideLA, len * rowLA),
                         buffer_rsrc(vh + static_cast<size_t>(c0) * strideV, mode == 2 ? 0 : len * rowV),
                         buffer_rsrc(bh + static_cast<size_t>(c0) * H, len * rowB)};
