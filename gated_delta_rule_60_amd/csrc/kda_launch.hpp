@@ -18,8 +18,11 @@ namespace kda {
 // identity run over it (V = 0, S0 = I) gives its transition M and
 // q^_t = M_t^T q_t; fix-up passes then add the true entering state's
 // contribution.  With enough pairs the extra identity work and fix-up
-// traffic cost more than the shorter critical path saves.
-constexpr int kSegTokens = 4096;     // longest segment
+// traffic cost more than the shorter critical path saves.  Few, long
+// segments keep that extra work small: a 128k-token sequence runs as four
+// 32k-token segments, seven runs per head (one round of workgroups for 32
+// heads on 256 compute units), three identity runs and three chain steps.
+constexpr int kSegTokens = 32768;    // longest segment
 constexpr int kSegMinTokens = 1024;  // shortest segment length a sequence is cut at
 // Compute units assumed when the current device cannot be queried (MI355X).
 constexpr int kDefaultCUs = 256;

@@ -32,6 +32,7 @@ constexpr int kPlanSortMax = 64;  // sequences ordered by length (longest first)
 constexpr int kFixCols = 32;      // value columns per state-chain workgroup
 constexpr int kFixThreads = 256;  // threads per output-correction workgroup
 constexpr int kOutTokens = 512;  // tokens per output fix-up workgroup
+constexpr int kOutGroups = 8;    // output workgroups per (segment, head)
 static_assert(kSegTokens % kOutTokens == 0, "output tiles cover a segment");
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -262,8 +263,9 @@ __global__ __launch_bounds__(ChainShape<DK>::NT) void seg_chain_kernel(const int
 
 // ---------------------------------------------------------------------------
 // Outputs of later segments: o_t += S_in^T q^_t for every token t of the
-// segment.  One workgroup per (unit, head, kOutTokens tokens); S_in^T is
-// staged once in LDS in the operand type.  Each wave takes 16-token tiles:
+// segment.  kOutGroups workgroups per (unit, head), each taking every
+// kOutGroups-th tile of kOutTokens tokens; S_in^T is staged once per
+// workgroup in LDS in the operand type.  Each wave takes 16-token tiles:
 //   1. q^ and o rows are loaded 16 bytes per lane along each row (every
 //      instruction reads whole row segments), one tile ahead;
 //   2. the q^ rows pass through the wave's LDS staging area into MFMA
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(kFixThreads) void seg_out_kernel(const int4* __rest
     constexpr int KB = DK / 32;
     constexpr int NCT = DV / 16;
     constexpr int LDB = Sh::LDB, NI = Sh::NI, LPR = Sh::LPR, RPI = Sh::RPI, OE = Sh::OE;
-    constexpr int TILES = kSegTokens / kOutTokens;
+    constexpr int TILES = kOutGroups;  // workgroups per (unit, head); each takes every TILES-th tile
     constexpr int SQ = DK * DV / 4 / kFixThreads;  // float4 of S_in per thread
     static_assert(SQ >= 1, "state staging");
     __shared__ __attribute__((aligned(16))) E sBt[DV * LDB];
@@ -320,9 +322,7 @@ __global__ __launch_bounds__(kFixThreads) void seg_out_kernel(const int4* __rest
     if (u >= counts[0]) return;  // whole workgroup: before any barrier
     const int4 it = units[u];
     if (it.y == 0) return;  // a first segment starts from the true state
-    const int t0 = it.z + tile * kOutTokens;
-    const int t1 = min(it.w, t0 + kOutTokens);
-    if (t0 >= t1) return;
+    if (it.z + tile * kOutTokens >= it.w) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -348,88 +348,93 @@ __global__ __launch_bounds__(kFixThreads) void seg_out_kernel(const int4* __rest
     }
     __syncthreads();
 
-    // Byte ranges: rows tt .. min(tt + 16, t1) - 1 of this head's q^ / o
-    // slices (one token row is H * DK elements; at most 16 rows, so every
-    // offset stays far below 2^31 under the host's H * d <= 2^20).
-    const int rowB = H * Sh::RB;
-    auto rsrc = [&](const G* base, int tt) __attribute__((always_inline)) {
-        const int rows = __builtin_amdgcn_readfirstlane(min(16, t1 - tt));
-        const int bytes = rows > 0 ? (rows - 1) * rowB + Sh::RB : 0;
-        const G* p = rows > 0 ? base + static_cast<size_t>(tt) * H * DK : base;
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<G*>(p), 0, bytes, 0x00020000);
-    };
-    const G* const qh = qhat + static_cast<size_t>(h) * DK;
-    G* const oh = o + static_cast<size_t>(h) * DV;
-    // this lane's row and 16-byte column block in load instruction j
-    const int lrow = lane / LPR, lcol = (lane % LPR) * 16;
-    auto voff = [&](int j) __attribute__((always_inline)) { return (j * RPI + lrow) * rowB + lcol; };
+    // the tiles of this workgroup: tile, tile + TILES, ... while inside the segment
+    for (int tl = tile; it.z + tl * kOutTokens < it.w; tl += TILES) {
+        const int t0 = it.z + tl * kOutTokens;
+        const int t1 = min(it.w, t0 + kOutTokens);
+        // Byte ranges: rows tt .. min(tt + 16, t1) - 1 of this head's q^ / o
+        // slices (one token row is H * DK elements; at most 16 rows, so every
+        // offset stays far below 2^31 under the host's H * d <= 2^20).
+        const int rowB = H * Sh::RB;
+        auto rsrc = [&](const G* base, int tt) __attribute__((always_inline)) {
+            const int rows = __builtin_amdgcn_readfirstlane(min(16, t1 - tt));
+            const int bytes = rows > 0 ? (rows - 1) * rowB + Sh::RB : 0;
+            const G* p = rows > 0 ? base + static_cast<size_t>(tt) * H * DK : base;
+            return __builtin_amdgcn_make_buffer_rsrc(const_cast<G*>(p), 0, bytes, 0x00020000);
+        };
+        const G* const qh = qhat + static_cast<size_t>(h) * DK;
+        G* const oh = o + static_cast<size_t>(h) * DV;
+        // this lane's row and 16-byte column block in load instruction j
+        const int lrow = lane / LPR, lcol = (lane % LPR) * 16;
+        auto voff = [&](int j) __attribute__((always_inline)) { return (j * RPI + lrow) * rowB + lcol; };
 
-    u32x4_t qn[NI], on[NI];
-    auto fetch = [&](int tt) __attribute__((always_inline)) {
-        const auto rq = rsrc(qh, tt);
-        const auto ro = rsrc(oh, tt);
+        u32x4_t qn[NI], on[NI];
+        auto fetch = [&](int tt) __attribute__((always_inline)) {
+            const auto rq = rsrc(qh, tt);
+            const auto ro = rsrc(oh, tt);
 #pragma unroll
-        for (int j = 0; j < NI; ++j) qn[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff(j), 0, 0);
+            for (int j = 0; j < NI; ++j) qn[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff(j), 0, 0);
 #pragma unroll
-        for (int j = 0; j < NI; ++j) on[j] = __builtin_amdgcn_raw_buffer_load_b128(ro, voff(j), 0, 0);
-    };
+            for (int j = 0; j < NI; ++j) on[j] = __builtin_amdgcn_raw_buffer_load_b128(ro, voff(j), 0, 0);
+        };
 
-    int tt = t0 + 16 * wave;
-    fetch(tt);
-    for (; tt < t1; tt += 64) {
-        u32x4_t qc[NI], oc[NI];
+        int tt = t0 + 16 * wave;
+        fetch(tt);
+        for (; tt < t1; tt += 64) {
+            u32x4_t qc[NI], oc[NI];
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            qc[j] = qn[j];
-            oc[j] = on[j];
-        }
-        fetch(tt + 64);  // the next tile (an empty range past the end)
-        // q^ rows -> staging -> operand fragments (lane: token ln, k slots)
+            for (int j = 0; j < NI; ++j) {
+                qc[j] = qn[j];
+                oc[j] = on[j];
+            }
+            fetch(tt + 64);  // the next tile (an empty range past the end)
+            // q^ rows -> staging -> operand fragments (lane: token ln, k slots)
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-            *reinterpret_cast<u32x4_t*>(stage + (j * RPI + lrow) * Sh::LDQ + lcol) = qc[j];
-        F8 b[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-            b[kb] = lds_frag8<BF16>(reinterpret_cast<const E*>(stage) + 32 * kb, Sh::LDQ / Sh::ES, lane);
-        // o^T tiles: lane holds columns 16 ct + 4 lgp .. + 3 of token ln;
-        // staged as fp32 rows (the q^ rows above are consumed)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NI; ++j)
+                *reinterpret_cast<u32x4_t*>(stage + (j * RPI + lrow) * Sh::LDQ + lcol) = qc[j];
+            F8 b[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-                acc = mma8<BF16>(acc, lds_frag8<BF16>(sBt + (16 * ct) * LDB + 32 * kb, LDB, lane), b[kb]);
-            *reinterpret_cast<f32x4_t*>(stage + ln * Sh::LDA + (16 * ct + 4 * lgp) * 4) = acc;
-        }
-        // row order again: o += products, 16 bytes per lane along each row
-        const auto ro = rsrc(oh, tt);
+                b[kb] = lds_frag8<BF16>(reinterpret_cast<const E*>(stage) + 32 * kb, Sh::LDQ / Sh::ES, lane);
+            // o^T tiles: lane holds columns 16 ct + 4 lgp .. + 3 of token ln;
+            // staged as fp32 rows (the q^ rows above are consumed)
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            const unsigned char* src = stage + (j * RPI + lrow) * Sh::LDA + (lcol / Sh::ES) * 4;
-            float add[OE];
+            for (int ct = 0; ct < NCT; ++ct) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < OE; e += 4) {
-                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + 4 * e);
-                add[e] = v[0];
-                add[e + 1] = v[1];
-                add[e + 2] = v[2];
-                add[e + 3] = v[3];
+                for (int kb = 0; kb < KB; ++kb)
+                    acc = mma8<BF16>(acc, lds_frag8<BF16>(sBt + (16 * ct) * LDB + 32 * kb, LDB, lane), b[kb]);
+                *reinterpret_cast<f32x4_t*>(stage + ln * Sh::LDA + (16 * ct + 4 * lgp) * 4) = acc;
             }
-            u32x4_t out;
-            if constexpr (BF16) {
+            // row order again: o += products, 16 bytes per lane along each row
+            const auto ro = rsrc(oh, tt);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const unsigned x = oc[j][e];
-                    const float lo = __uint_as_float(x << 16) + add[2 * e];
-                    const float hi = __uint_as_float(x & 0xFFFF0000u) + add[2 * e + 1];
-                    out[e] = static_cast<unsigned>(f32_to_bf16(lo)) | (static_cast<unsigned>(f32_to_bf16(hi)) << 16);
+            for (int j = 0; j < NI; ++j) {
+                const unsigned char* src = stage + (j * RPI + lrow) * Sh::LDA + (lcol / Sh::ES) * 4;
+                float add[OE];
+#pragma unroll
+                for (int e = 0; e < OE; e += 4) {
+                    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + 4 * e);
+                    add[e] = v[0];
+                    add[e + 1] = v[1];
+                    add[e + 2] = v[2];
+                    add[e + 3] = v[3];
                 }
-            } else {
+                u32x4_t out;
+                if constexpr (BF16) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = __float_as_uint(__uint_as_float(oc[j][e]) + add[e]);
+                    for (int e = 0; e < 4; ++e) {
+                        const unsigned x = oc[j][e];
+                        const float lo = __uint_as_float(x << 16) + add[2 * e];
+                        const float hi = __uint_as_float(x & 0xFFFF0000u) + add[2 * e + 1];
+                        out[e] = static_cast<unsigned>(f32_to_bf16(lo)) | (static_cast<unsigned>(f32_to_bf16(hi)) << 16);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = __float_as_uint(__uint_as_float(oc[j][e]) + add[e]);
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(out, ro, voff(j), 0, 0);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(out, ro, voff(j), 0, 0);
         }
     }
 }
@@ -479,7 +484,7 @@ static hipError_t launch_fixup_t(const PrefillArgs& a, const SegView& v) {
     hipLaunchKernelGGL((seg_chain_kernel<DK>), dim3(gchain), dim3(ChainShape<DK>::NT), 0, st, v.count, longs,
                        v.mstate, v.dstate, a.H, a.d_v, a.S_T);
     const unsigned gout = static_cast<unsigned>(L.umax) * static_cast<unsigned>(a.H) *
-                          static_cast<unsigned>(kSegTokens / kOutTokens);
+                          static_cast<unsigned>(kOutGroups);
     hipLaunchKernelGGL((seg_out_kernel<BF16, DK>), dim3(gout), dim3(kFixThreads), 0, st, v.units, v.count,
                        static_cast<const G*>(v.qhat), v.dstate, a.H, static_cast<G*>(a.o));
     return hipGetLastError();

@@ -143,10 +143,10 @@ def test_workspace_and_default_split_queries():
     assert kda.kda_prefill_workspace_size(3, 32677, 42, 128, 128, BF16) > 0   # 126 pairs
     assert kda.kda_prefill_workspace_size(4, 32677, 32, 128, 128, BF16) == 0  # 128 pairs
     ws = kda.kda_prefill_workspace_size(1, 131072, 32, 128, 128, BF16)
-    # the identity runs' outputs and M, D for N + min(T_tot // 1024, 3 N + T_tot // 4096)
-    # segments (36 here; 32 are used), plus the plan
-    segs = 1 + min(131072 // 1024, 3 + 131072 // 4096)
-    assert segs == 36
+    # the identity runs' outputs and M, D for N + min(T_tot // 1024, 3 N + T_tot // 32768)
+    # segments (8 here; 4 are used), plus the plan
+    segs = 1 + min(131072 // 1024, 3 + 131072 // 32768)
+    assert segs == 8
     body = 131072 * 32 * 128 * 2 + 2 * segs * 32 * 128 * 128 * 4
     assert body <= ws <= body + 4096
     assert kda.kda_prefill_workspace_size(1, 131072, 32, 128, 128, F32) > ws

@@ -138,8 +138,9 @@ def test_wide_decay_keeps_the_bits_within_the_default_contract(lengths):
 
 
 SEGMENTED = [
-    # lengths (batches past 1024 tokens run in segments of 1024-4096 tokens), H, d_k = d_v, dtype, s0
+    # lengths (batches past 1024 tokens run in segments of 1024-32768 tokens), H, d_k = d_v, dtype, s0
     ([2 * 4096 + 77, 300, 4096, 4097], 2, 128, "bf16", True),
+    ([20000, 300], 2, 64, "bf16", True),  # 5120-token segments: ten output tiles each
     ([3 * 4096 + 5, 10], 1, 128, "f32", True),
     ([4100, 0, 9000], 2, 64, "bf16", True),
     ([8192, 1], 2, 32, "f32", False),

@@ -64,7 +64,7 @@ def test_random_shape_forward_and_backward(case):
 
 def _segment_cases(n=14, seed=4242):
     """Small batches past 1024 tokens, d_k = d_v: the segmented path. Lengths
-    mix the cut points of the 1024-4096-token segments (one token past a
+    mix the cut points of the 1024-32768-token segments (one token past a
     multiple of 512 or 1024) with random lengths and empty sequences."""
     rng = np.random.default_rng(seed)
     edges = [1025, 1536, 1537, 2049, 4096, 4097, 6145]
