@@ -426,22 +426,6 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
         for (int kb = 0; kb < KBV; ++kb)
             sf[kb] = *reinterpret_cast<const F8*>(sb + (static_cast<size_t>(cti * KBV + kb) * 64 + lane) * 8);
     };
-    // raw k and q of chunk m for channel tile cti in the epilogue layout
-    // (lane: token 16 rt + ln, channels 16 cti + 4 lg .. + 3); rows past the
-    // chunk read zero
-    auto load_kq = [&](int m, int cti, R4 (&ek)[NB], R4 (&eq)[NB]) __attribute__((always_inline)) {
-        const int nrow = __builtin_amdgcn_readfirstlane(rows_of(m));
-        const size_t tok = static_cast<size_t>(t_beg + m * C) * H * DK;
-        const auto rk_r = buffer_rsrc(kh + tok, nrow * rowK);
-        const auto rq_r = buffer_rsrc(qh + tok, nrow * rowK);
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-            const int off = (16 * rt + ln) * rowK + (16 * cti + 4 * lg) * GS;
-            ek[rt] = bc_load_raw4<BF16>(rk_r, off, 0);
-            eq[rt] = bc_load_raw4<BF16>(rq_r, off, 0);
-        }
-    };
-
     // Stage LA: the C x C products dA = lower_incl(dO U^T) and
     // dL = -strictly_lower(dR U^T) (from tDR = -dR), 16 x 16 blocks dealt
     // round-robin to the waves.
@@ -489,8 +473,7 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
     // Stage LB for channel tile cti: the products over the value columns and
     // over the chunk's tokens, then dq, dk and dlog alpha of those 16 channels
     // for every token of the chunk.
-    auto lb_tile = [&](int cti, const F8 (&sf)[KBV], const R4 (&ek)[NB], const R4 (&eq)[NB], int t0, int rows)
-        __attribute__((always_inline)) {
+    auto lb_tile = [&](int cti, const F8 (&sf)[KBV], int t0, int rows) __attribute__((always_inline)) {
         const int crow = 16 * cti;
         // value-column products, one 32-column block at a time:
         //   aq = S dO^T,  akk = -S dR^T (tDR holds -dR),  akb = Dg U^T
@@ -527,16 +510,23 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
             akh[rt] = mma_rows<BF16, C>(z4, tQtT + crow * LT, LT, tdAt + 16 * rt * LT, LT, lane);
             akh[rt] = mma_rows<BF16, C>(akh[rt], tKtT + crow * LT, LT, tbdLt + 16 * rt * LT, LT, lane);
         }
-        // epilogue: lane (ln, lg) holds channels ch0 .. ch0 + 3 of token 16 rt + ln
+        // epilogue: lane (ln, lg) holds channels ch0 .. ch0 + 3 of token 16 rt + ln.
+        // k and q enter dlog alpha only through the decayed tiles of the chunk,
+        // k Gamma, k / Gamma and q Gamma (the operands of the chunk's products):
+        // K^ from its rows, K~ and Q~ from their transposes.
         const int ch0 = crow + 4 * lg;
         float dg[NB][4], ex[4] = {0.f, 0.f, 0.f, 0.f};
         float dqv[NB][4], dkv[NB][4];
 #pragma unroll
         for (int rt = 0; rt < NB; ++rt) {
             const int r = 16 * rt + ln;
-            float kk[4], qq[4];
-            T::unpack4(ek[rt], kk);
-            T::unpack4(eq[rt], qq);
+            const f32x4_t khv = bc_widen<BF16>(*reinterpret_cast<const F4*>(tKh + r * LK + ch0));
+            float ktv[4], qtv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                ktv[j] = static_cast<float>(tKtT[(ch0 + j) * LT + r]);
+                qtv[j] = static_cast<float>(tQtT[(ch0 + j) * LT + r]);
+            }
             // cumulative decay (log2 units) of these channels up to token r
             const float4 g4 = *reinterpret_cast<const float4*>(sG + r * DK + ch0);
             const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
@@ -551,8 +541,8 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
                 const float a1 = dkt * gm, a2 = dkh * ig, a3 = dqt * gm;
                 dqv[rt][j] = a3;
                 dkv[rt][j] = a1 + a2;
-                dg[rt][j] = kk[j] * (a1 - a2) + qq[j] * a3;
-                ex[j] = __builtin_fmaf(akb[rt][j] * kk[j], ig, ex[j]);
+                dg[rt][j] = (dkt * ktv[j] - dkh * khv[j]) + dqt * qtv[j];
+                ex[j] = __builtin_fmaf(akb[rt][j], khv[j], ex[j]);
             }
         }
         // extra term of every row: c (moved to the epilogue layout) plus the
@@ -594,21 +584,18 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
         }
     };
     // Stage LB of this wave: channel tiles wave, wave + NW, ...; the first
-    // tile's S rows and k, q were loaded at the chunk's start.
-    auto stage_LB = [&](int m, const F8 (&sf0)[KBV], const R4 (&ek0)[NB], const R4 (&eq0)[NB])
-        __attribute__((always_inline)) {
+    // tile's S rows were loaded at the chunk's start.
+    auto stage_LB = [&](int m, const F8 (&sf0)[KBV]) __attribute__((always_inline)) {
         const int t0 = t_beg + m * C;
         const int rows = rows_of(m);
-        if (wave < NCT) lb_tile(wave, sf0, ek0, eq0, t0, rows);
+        if (wave < NCT) lb_tile(wave, sf0, t0, rows);
 #pragma unroll
         for (int k2 = 1; k2 < TPW; ++k2) {
             const int cti = wave + k2 * NW;
             if (cti < NCT) {
                 F8 sf[KBV];
-                R4 ek[NB], eq[NB];
                 load_stile(m, cti, sf);
-                load_kq(m, cti, ek, eq);
-                lb_tile(cti, sf, ek, eq, t0, rows);
+                lb_tile(cti, sf, t0, rows);
             }
         }
         // dbeta of the chunk's tokens: the chain waves' partials plus the C x C term
@@ -626,10 +613,8 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
         }
     };
     // the first LB tile's operands for chunk m, loaded at the chunk's start
-    auto load_lb0 = [&](int m, F8 (&sf0)[KBV], R4 (&ek0)[NB], R4 (&eq0)[NB]) __attribute__((always_inline)) {
-        const int cti0 = min(wave, NCT - 1);
-        load_stile(m, cti0, sf0);
-        load_kq(m, cti0, ek0, eq0);
+    auto load_lb0 = [&](int m, F8 (&sf0)[KBV]) __attribute__((always_inline)) {
+        load_stile(m, min(wave, NCT - 1), sf0);
     };
 
     if (is_chain) {
@@ -867,12 +852,11 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
             // stage LB's operands, in flight during stage LA (the registers of
             // stage CH are free again)
             F8 sf0[KBV];
-            R4 ek0[NB], eq0[NB];
-            load_lb0(m, sf0, ek0, eq0);
+            load_lb0(m, sf0);
             bc_barrier();
             stage_LA();
             bc_barrier();
-            stage_LB(m, sf0, ek0, eq0);
+            stage_LB(m, sf0);
             // the next chunk's dO rows (in flight over the leaf waves' stage P)
             issue_dO(m - 1);
             bc_barrier();
@@ -894,8 +878,7 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
             // =============================== P: operand tiles; this chunk's loads
             load_w0(m);  // the first 32-column block of stage U
             F8 sf0[KBV];
-            R4 ek0[NB], eq0[NB];
-            load_lb0(m, sf0, ek0, eq0);
+            load_lb0(m, sf0);
             if (strip_wave) {
                 if (loads_beta) sBeta[lane] = rbeta;
                 if (qok) {
@@ -999,7 +982,7 @@ __global__ __launch_bounds__((BcLayout<BF16, DK, DV, C>::NT)) void bwd_chunk_ker
             bc_barrier();
             stage_LA();
             bc_barrier();
-            stage_LB(m, sf0, ek0, eq0);
+            stage_LB(m, sf0);
             bc_barrier();
         }
         if (nch > 0) flush_sg(0);
