@@ -990,9 +990,9 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
         const float* const bh = beta + h;
         const G* const vh = v + static_cast<size_t>(h) * dv + j0;
 
-        // Raw inputs of chunks m+1 and m+2 are in flight while chunk m is
-        // prepared: two register sets, even chunks in set 0 and odd chunks in
-        // set 1, each reloaded right after its chunk's prep consumed it
+        // Raw inputs of the next chunks are in flight while chunk m is
+        // prepared: NSET register sets used in turn (chunk m in set m mod
+        // NSET), each reloaded right after its chunk's prep consumed it
         // (one set, one chunk ahead, where the raw tiles are large: fp32).
         // Every load is unconditional (rows past the end of the sequence, and
         // chunks past the last, fall outside the buffer ranges and read as
@@ -1007,7 +1007,9 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
         const int offK = 4 * rg * rowK + i0 * GS;
         const int offLA = 4 * rg * rowLA + (SG ? 0 : i0 * 4);
         const bool loads_beta = strip == 0 && lane < C;  // beta of row `lane`, for the consumers
-        constexpr int NSET = BF16 && PP == 1 ? 2 : 1;
+        // (three where the V items are few, d_k >= 64: the raw loads of three
+        // chunks in flight keep more bytes moving per CU when every CU is busy)
+        constexpr int NSET = BF16 && PP == 1 ? (DK >= 64 ? 3 : 2) : 1;
         float4 rla[NSET][4];
         R4 rk[NSET][4], rq[NSET][4], rv[NSET][VPT][4];
         float rbeta[NSET];
@@ -1161,18 +1163,23 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
         };
 
         // Chunk m uses LDS slot m mod 3.  With two producer waves per strip
-        // (PP == 2) each takes the chunks of its parity; with one, its two
-        // register sets alternate (NSET == 2), and an odd chunk count ends
-        // with one virtual chunk past the end (zero inputs): its tiles go to
-        // a slot every consumer has released and nothing reads them.
+        // (PP == 2) each takes the chunks of its parity; with one, its NSET
+        // register sets take turns, and a chunk count that is not a multiple
+        // of NSET ends with up to NSET - 1 virtual chunks past the end (zero
+        // inputs): their tiles go to slots every consumer has released and
+        // nothing reads them.
         constexpr int STRIDE = PP * NSET;  // chunks between two uses of one register set
         const int m0 = PP == 2 ? par : 0;
         load_chunk(ic<0>{}, m0);
-        if constexpr (NSET == 2) {
+        if constexpr (NSET >= 2) {
             // issued in this order on every path into the loop, so the waits
-            // for set 0 count set 1's loads as issued after it
+            // for set 0 count the later sets' loads as issued after it
             asm volatile("" ::: "memory");
             load_chunk(ic<1>{}, m0 + 1);
+        }
+        if constexpr (NSET >= 3) {
+            asm volatile("" ::: "memory");
+            load_chunk(ic<2>{}, m0 + 2);
         }
         // O of chunk j, staged by the consumers as O^T quads in the V^T tile
         // of slot S: exactly the quads this wave's V items cover (so no other
@@ -1224,7 +1231,8 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
         int m = m0;
         for (; m < nchunks; m += STRIDE) {
             step(ic<0>{}, m);
-            if constexpr (NSET == 2) step(ic<1>{}, m + 1);
+            if constexpr (NSET >= 2) step(ic<1>{}, m + 1);
+            if constexpr (NSET >= 3) step(ic<2>{}, m + 2);
         }
         // The last chunks' O stay in slots nobody refills: once every chunk is
         // done, this wave stores those a continued loop would have.
