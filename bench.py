@@ -214,9 +214,10 @@ def decode_cpu_baseline(seconds: float, n_sample: int = 32):
                       f"scaled to all {N}"}
 
 
-def bench_prefill(kda, torch, x, steps: int, warmup: int, v_split: int, scalar_gate: bool = False):
+def bench_prefill(kda, torch, x, steps: int, warmup: int, v_split: int, scalar_gate: bool = False, **run_kw):
     """Event-timed launches of kda_prefill (or gdn_prefill with the gate of
-    channel 0 per token and head when ``scalar_gate``)."""
+    channel 0 per token and head when ``scalar_gate``); ``run_kw`` goes to
+    every call (options of the prefill)."""
 
     dev = torch.device("cuda:0")
     td = torch.bfloat16 if x.dtype == "bf16" else torch.float32
@@ -237,7 +238,7 @@ def bench_prefill(kda, torch, x, steps: int, warmup: int, v_split: int, scalar_g
         d["S_T"] = torch.empty((x.N, x.H, x.d_k, x.d_v), dtype=torch.float32, device=dev)
         sets.append(d)
     for i in range(warmup):
-        run(**sets[i % 2], v_split=v_split)
+        run(**sets[i % 2], v_split=v_split, **run_kw)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -246,12 +247,59 @@ def bench_prefill(kda, torch, x, steps: int, warmup: int, v_split: int, scalar_g
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
-        run(**sets[i % 2], v_split=v_split)
+        run(**sets[i % 2], v_split=v_split, **run_kw)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
     return wall, kernel_ms
+
+
+def bench_any_decay(kda, torch, steps: int, warmup: int, rec_steps: int, default_ms: float):
+    """The any-decay prefill (KDA_PREFILL_ANY_DECAY) on the 32k-token batch
+    with -U(0, 5) gates and eight resets per sequence: the chunked path (chunk
+    lists, then the prefill kernel over them: one call between the events)
+    and the token-recurrent kernel."""
+    import numpy as np
+    from gated_delta_rule_60_amd import inputs
+
+    x = inputs.make_any_decay_workload()
+    C = chunk_len(x.dtype, x.d_k)
+    strong = (x.log_alpha < -5.0).any(axis=2)  # [T, H]
+    chunks = 0
+    for n in range(x.N):
+        a, b = int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1])
+        for h in range(x.H):
+            cuts = np.concatenate(([a], a + np.nonzero(strong[a:b, h])[0], [b]))
+            seg = np.diff(np.unique(cuts))
+            chunks += int(np.sum((seg + C - 1) // C))
+    ws = torch.empty(kda.kda_prefill_workspace_size_ex(x.N, x.T_tot, x.H, x.d_k, x.d_v, 0,
+                                                       kda.KDA_PREFILL_ANY_DECAY),
+                     dtype=torch.uint8, device="cuda:0")
+    _, cms = bench_prefill(kda, torch, x, steps, warmup, 0, any_decay=True, workspace=ws)
+    _, rms = bench_prefill(kda, torch, x, rec_steps, 1, 0, any_decay=True, token_recurrent=True)
+    c_avg, r_avg = sum(cms) / len(cms), sum(rms) / len(rms)
+    nbytes = prefill_bytes(x.T_tot, x.N, x.H, x.d_k, x.d_v, 2)
+    return {
+        "workload": "prefill_varlen8_32k_h32_d128_bf16 shapes, log alpha -U(0, 5) per channel, "
+                    "8 resets (log alpha -1000) per sequence",
+        "what": "kda_prefill_ex with KDA_PREFILL_ANY_DECAY: chunk lists + chunked kernel (workspace given), "
+                "and the token-recurrent kernel (no workspace)",
+        "strong_tokens": int(strong.any(axis=1).sum()), "chunks_per_call": chunks,
+        "chunks_if_uniform": int(x.H * sum((int(b - a) + C - 1) // C
+                                           for a, b in zip(x.cu_seqlens[:-1], x.cu_seqlens[1:]))),
+        "chunked_ms_avg": c_avg, "chunked_ms_min": min(cms),
+        "chunked_tokens_per_s": x.T_tot / (c_avg * 1e-3),
+        "chunked_vs_default_prefill": c_avg / default_ms,
+        "recurrent_ms_avg": r_avg, "recurrent_ms_min": min(rms),
+        "speedup_chunked_vs_recurrent": r_avg / c_avg,
+        "roofline": {"bound": "hbm", "achieved": nbytes / (c_avg * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": nbytes / (c_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("prefill_any_decay", "prefill_varlen8_32k_h32_d128_bf16_resets",
+                                                 ["kda_anymap.hip", "kda_prefill.hip", "kda_device.hpp"]),
+                     "kernel": "kda::any_map_kernel + kda::prefill_kernel (chunk lists)",
+                     "alg_bytes_per_launch": nbytes},
+    }
 
 
 def bench_prefill_flushed(kda, torch, x, steps: int, warmup: int, flush_bytes: int):
@@ -423,6 +471,8 @@ def main():
     ap.add_argument("--no-gdn", action="store_true", help="skip the scalar-gate (Gated DeltaNet) prefill line")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass line")
     ap.add_argument("--backward-steps", type=int, default=5)
+    ap.add_argument("--no-any-decay", action="store_true", help="skip the any-decay prefill line")
+    ap.add_argument("--any-recurrent-steps", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other prefill workloads (256-token fp32, 4096- and 131,072-token sequences)")
@@ -541,6 +591,8 @@ def main():
                          "mfma_counter_busy_frac_pass2": measured_mfma_busy("prefill_backward", args.workload, bsrc),
                          "token_recurrence_flops_per_launch": bfl},
         }
+    if not args.no_any_decay and args.workload == "prefill_varlen8_32k_h32_d128_bf16":
+        out["any_decay"] = bench_any_decay(kda, torch, args.steps, args.warmup, args.any_recurrent_steps, k_avg_ms)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     if not args.no_configs and args.workload == "prefill_varlen8_32k_h32_d128_bf16":

@@ -41,6 +41,7 @@ from ._lib import (  # noqa: F401
     kda_prefill_plan,
     kda_prefill_split,
     kda_prefill_workspace_size,
+    kda_prefill_workspace_size_ex,
     kda_status_string,
     kda_version,
     library_path,

@@ -39,6 +39,7 @@ SIGNATURES = {
     "kda_prefill_ex": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _ip, _i32, _i64, _i32, _i32, _i32,
                                       ctypes.c_int, _vp, _fp, _vp, _sz, _i32, ctypes.c_uint32, _vp]),
     "kda_prefill_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int]),
+    "kda_prefill_workspace_size_ex": (_sz, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int, ctypes.c_uint32]),
     "kda_prefill_default_split": (_i32, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int]),
     "kda_prefill_plan": (ctypes.c_int, [_i32, _i64, _i32, _i32, _i32, ctypes.c_int, _i32, _vp, _vp]),
     "kda_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _fp, _fp, _fp, _i32, _i32, _i32, _i32,
@@ -120,6 +121,10 @@ def kda_prefill_ex(q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d
 
 def kda_prefill_workspace_size(N, T_tot, H, d_k, d_v, dtype) -> int:
     return int(load().kda_prefill_workspace_size(N, T_tot, H, d_k, d_v, dtype))
+
+
+def kda_prefill_workspace_size_ex(N, T_tot, H, d_k, d_v, dtype, flags) -> int:
+    return int(load().kda_prefill_workspace_size_ex(N, T_tot, H, d_k, d_v, dtype, flags))
 
 
 def kda_prefill_default_split(N, T_tot, H, d_k, d_v, dtype) -> int:
@@ -248,7 +253,8 @@ def _stream_of(stream, device):
 
 
 def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream,
-             scalar_gate: bool, wide_decay: bool = False, any_decay: bool = False):
+             scalar_gate: bool, wide_decay: bool = False, any_decay: bool = False,
+             token_recurrent: bool = False):
     """Chunked prefill on torch tensors; returns (o, S_T).
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
@@ -257,10 +263,12 @@ def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspac
     or None; cu_seqlens: int32 [N + 1] on the device (None = one sequence).
     ``S_T`` may be ``S0`` itself (in-place update of the states).
     ``workspace`` (optional): a uint8 device tensor of at least
-    ``kda_prefill_workspace_size(...)`` bytes; one is allocated when needed
-    and not given.  ``wide_decay`` selects the wide-decay kernel variant
-    (KDA_PREFILL_WIDE_DECAY); ``any_decay`` the token-recurrent kernel with no
-    decay-range contract (KDA_PREFILL_ANY_DECAY).
+    ``kda_prefill_workspace_size_ex(...)`` bytes for these flags; one is
+    allocated when needed and not given.  ``wide_decay`` selects the
+    wide-decay kernel variant (KDA_PREFILL_WIDE_DECAY); ``any_decay`` drops
+    the decay-range contract (KDA_PREFILL_ANY_DECAY): the chunked kernel over
+    chunk lists, or with ``token_recurrent`` the token-recurrent kernel (no
+    workspace).
     """
     import torch
     if not q.is_cuda:
@@ -269,11 +277,11 @@ def _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspac
     st = _stream_of(stream, dev)
     with torch.cuda.device(dev), torch.cuda.stream(st):
         return _prefill_on(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, st,
-                           scalar_gate, wide_decay, any_decay)
+                           scalar_gate, wide_decay, any_decay, token_recurrent)
 
 
 def _prefill_on(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, st,
-                scalar_gate, wide_decay, any_decay):
+                scalar_gate, wide_decay, any_decay, token_recurrent):
     import torch
     dev = q.device
     T, H, dk = (int(x) for x in q.shape)
@@ -296,7 +304,11 @@ def _prefill_on(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, works
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _need(o, "o", (T, H, dv), q.dtype, dev)
     _need(S_T, "S_T", (N, H, dk, dv), torch.float32, dev)
-    ws = kda_prefill_workspace_size(N, T, H, dk, dv, code)
+    flags = ((KDA_PREFILL_SCALAR_GATE if scalar_gate else 0) | (KDA_PREFILL_WIDE_DECAY if wide_decay else 0)
+             | (KDA_PREFILL_ANY_DECAY if any_decay else 0))
+    if token_recurrent and not any_decay:
+        raise ValueError("token_recurrent applies to any_decay")
+    ws = 0 if token_recurrent else kda_prefill_workspace_size_ex(N, T, H, dk, dv, code, flags)
     wbuf = None
     if ws:
         if workspace is None:
@@ -307,8 +319,6 @@ def _prefill_on(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, works
             if workspace.numel() < ws:
                 raise ValueError(f"workspace holds {workspace.numel()} bytes; {ws} are needed")
             wbuf = workspace
-    flags = ((KDA_PREFILL_SCALAR_GATE if scalar_gate else 0) | (KDA_PREFILL_WIDE_DECAY if wide_decay else 0)
-             | (KDA_PREFILL_ANY_DECAY if any_decay else 0))
     _check(kda_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
                           beta.data_ptr(), S0.data_ptr() if S0 is not None else None,
                           cu_seqlens.data_ptr(), N, T, H, dk, dv, code, o.data_ptr(),
@@ -319,20 +329,20 @@ def _prefill_on(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, works
 
 def prefill(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=None,
             v_split: int = 0, workspace=None, wide_decay: bool = False, any_decay: bool = False,
-            stream=None):
+            token_recurrent: bool = False, stream=None):
     """KDA chunked prefill (per-channel gates, log_alpha [T, H, d_k]) on torch
     tensors; returns (o, S_T).  Arguments as in ``_prefill``."""
     return _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream, False,
-                    wide_decay, any_decay)
+                    wide_decay, any_decay, token_recurrent)
 
 
 def gdn_prefill_t(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o=None, S_T=None,
                   v_split: int = 0, workspace=None, wide_decay: bool = False, any_decay: bool = False,
-                  stream=None):
+                  token_recurrent: bool = False, stream=None):
     """Gated DeltaNet chunked prefill (one gate per token and head, log_alpha
     [T, H]) on torch tensors; returns (o, S_T).  Arguments as in ``_prefill``."""
     return _prefill(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, v_split, workspace, stream, True,
-                    wide_decay, any_decay)
+                    wide_decay, any_decay, token_recurrent)
 
 
 

@@ -15,7 +15,7 @@ _ROOT = os.path.dirname(_HERE)
 _CSRC = os.path.join(_HERE, "csrc")
 
 SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_segment.hip", "kda_decode.hip", "kda_backward.hip",
-           "kda_bwd_chunk.hip", "kda_noalloc.hip"]
+           "kda_bwd_chunk.hip", "kda_noalloc.hip", "kda_anymap.hip"]
 ARCH = "gfx950"
 
 

@@ -127,6 +127,18 @@ int32_t kda_prefill_default_split(int32_t N, int64_t T_tot, int32_t H, int32_t d
     return st == KDA_OK ? split : 0;
 }
 
+size_t kda_prefill_workspace_size_ex(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
+                                     kda_dtype dtype, uint32_t flags) {
+    if ((flags & ~static_cast<uint32_t>(KDA_PREFILL_SCALAR_GATE | KDA_PREFILL_WIDE_DECAY | KDA_PREFILL_ANY_DECAY)) != 0 ||
+        ((flags & KDA_PREFILL_WIDE_DECAY) && (flags & KDA_PREFILL_ANY_DECAY)))
+        return 0;
+    if (N < 1 || H < 1 || T_tot < 0 || !supported_dim(d_k) || !supported_dim(d_v) ||
+        (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32))
+        return 0;
+    if (flags & KDA_PREFILL_ANY_DECAY) return kda::any_map_bytes(N, T_tot, H);
+    return kda_prefill_workspace_size(N, T_tot, H, d_k, d_v, dtype);
+}
+
 size_t kda_prefill_backward_workspace_size_ex(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v,
                                               kda_dtype dtype, uint32_t flags) {
     if (N < 1 || H < 1 || T_tot < 0 || !supported_dim(d_k) || !supported_dim(d_v) ||
@@ -240,8 +252,9 @@ namespace {
 
 // Shared by every prefill entry point.  KDA_PREFILL_SCALAR_GATE changes only
 // the shape of log_alpha ([T_tot, H], 4-byte aligned); KDA_PREFILL_ANY_DECAY
-// selects the token-recurrent kernel; KDA_PREFILL_WIDE_DECAY
-// selects the wide-decay kernel variant.
+// selects the chunked kernel over chunk lists when the workspace holds them,
+// the token-recurrent kernel otherwise; KDA_PREFILL_WIDE_DECAY selects the
+// wide-decay kernel variant.
 kda_status prefill_impl(const void* q, const void* k, const void* v, const float* log_alpha,
                         const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t N,
                         int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, void* o,
@@ -272,7 +285,11 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
         return fail(KDA_ERR_INVALID_ARG, "log_alpha must be 4-byte aligned");
     const bool bf16 = dtype == KDA_DTYPE_BF16;
     const int cus = kda::device_cus_or_default();
-    const size_t ws_need = kda::prefill_workspace_bytes(N, T_tot, H, d_k, d_v, bf16, cus);
+    const bool any_decay = (flags & KDA_PREFILL_ANY_DECAY) != 0;
+    // any decay: the chunk lists when the workspace holds them (else the
+    // token-recurrent kernel, which needs none)
+    const bool mapped = any_decay && workspace && workspace_bytes >= kda::any_map_bytes(N, T_tot, H);
+    const size_t ws_need = any_decay ? 0 : kda::prefill_workspace_bytes(N, T_tot, H, d_k, d_v, bf16, cus);
     if (workspace_bytes < ws_need)
         return fail(KDA_ERR_INVALID_ARG, "workspace smaller than kda_prefill_workspace_size");
     if (ws_need > 0 && !workspace) return fail(KDA_ERR_INVALID_ARG, "workspace must not be NULL");
@@ -290,9 +307,10 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
 
     kda::PrefillArgs a{q, k, v, log_alpha, beta, S0, cu_seqlens, N, T_tot, H, d_k, d_v,
                        bf16, o, S_T, v_split, stream, workspace, cus, scalar_gate,
-                       (flags & KDA_PREFILL_WIDE_DECAY) != 0, (flags & KDA_PREFILL_ANY_DECAY) != 0};
+                       (flags & KDA_PREFILL_WIDE_DECAY) != 0, any_decay};
     (void)hipGetLastError();  // report only this launch's status
-    const hipError_t e = a.any_decay ? kda::launch_prefill_recurrent(a) : kda::launch_prefill(a);
+    const hipError_t e = mapped ? kda::launch_prefill_mapped(a)
+                                : (any_decay ? kda::launch_prefill_recurrent(a) : kda::launch_prefill(a));
     if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
     return KDA_OK;
 }

@@ -71,6 +71,22 @@ struct CkptView {
     void* w0;
 };
 
+// Chunk lists of the any-decay prefill (kda_anymap.hip).  For sequence n and
+// head h: count[n H + h] chunks, starting at the tokens
+// starts[h stride + cu[n] + 2 n + i] (i < count, ascending), followed by the
+// sequence end; each chunk holds at most C tokens (the prefill's chunk
+// length).  A chunk ends early where a token with a strong decay follows, so
+// that such a token is always the first row of its chunk.
+struct ChunkMap {
+    const int* count;
+    const int* starts;
+    int64_t stride;  // T_tot + 2 N
+};
+// A token whose log alpha is below this on some channel (natural log units)
+// starts a chunk of the any-decay prefill.  The wide-decay contract allows
+// -80 over 16 consecutive tokens, so runs of the other tokens stay within it.
+constexpr float kStrongLogAlpha = -5.f;
+
 struct PrefillArgs {
     const void* q;
     const void* k;
@@ -91,7 +107,7 @@ struct PrefillArgs {
     int cus = kDefaultCUs;     // compute units of the device the launch rules assume
     bool scalar_gate = false;  // log_alpha is [T_tot, H] (one gate per token and head)
     bool wide_decay = false;   // exponents of strongly decaying channels from the chunk's middle row
-    bool any_decay = false;    // token-recurrent kernel: any finite log_alpha (kda_backward.hip)
+    bool any_decay = false;    // any finite log_alpha: chunk lists + chunked kernel, or token-recurrent
 };
 
 struct DecodeArgs {
@@ -136,6 +152,12 @@ hipError_t launch_prefill_ckpt(const PrefillArgs& a, const CkptView& ck);
 int prefill_chunk_len(int32_t d_k, bool bf16);
 // Token-recurrent prefill for any decay range (kda_backward.hip).
 hipError_t launch_prefill_recurrent(const PrefillArgs& a);
+// Chunked prefill for any decay range: the chunk lists (kda_anymap.hip), then
+// the wide-decay prefill kernel over those chunks.  The workspace holds the
+// lists: any_map_bytes(...) bytes, 256-byte aligned.
+hipError_t launch_prefill_mapped(const PrefillArgs& a);
+hipError_t launch_any_map(const PrefillArgs& a, ChunkMap* m);
+size_t any_map_bytes(int32_t N, int64_t T_tot, int32_t H);
 
 // Whether a prefill of these sizes runs segmented on a device with `cus`
 // compute units, and the workspace bytes it then needs (0 when it does not).

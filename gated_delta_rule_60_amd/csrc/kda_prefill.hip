@@ -54,7 +54,10 @@
 //
 // Variants (template flags): SG takes one gate per token and head (Gated
 // DeltaNet); WIDE takes the exponents of strongly decaying channels from the
-// chunk's middle row (the wide-decay contract of kda_prefill_ex).
+// chunk's middle row (the wide-decay contract of kda_prefill_ex); MAP (with
+// WIDE) walks the chunk lists of kda_anymap.hip instead of fixed C-token
+// chunks, so that a token with a strong decay is always a chunk's first row
+// (the any-decay prefill).
 #include <type_traits>
 
 #include "kda_device.hpp"
@@ -82,6 +85,12 @@ constexpr float kRefSwitchLog2 = 100.f;
 
 template <int V>
 using ic = std::integral_constant<int, V>;
+
+// A load the compiler must issue as a scalar memory load (the address is
+// wave-uniform): it is counted apart from the vector loads in flight, so
+// reading a chunk bound never waits for them.
+typedef const __attribute__((address_space(4))) int ConstI32;
+__device__ __forceinline__ int scalar_load(const int* p) { return *(ConstI32*)(p); }
 
 // Per-chunk tiles in LDS.  The producers' tiles (decayed operands, V^T,
 // Gamma_C, beta) rotate through three slots, so the producers can run two
@@ -437,13 +446,14 @@ __device__ __forceinline__ void ctr_wait_each(int* ctrs, int n, int target, int*
 // per-channel computation with the value repeated over the channels.
 // WIDE: wide-decay variant (exponents of strongly decaying channels taken
 // relative to the chunk's middle row, the state operand scaled to match).
-template <bool BF16, int DK, int NC, int CT, bool SG, bool WIDE, bool CK = false>
+template <bool BF16, int DK, int NC, int CT, bool SG, bool WIDE, bool CK = false, bool MAP = false>
 __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void prefill_kernel(
     const typename Elem<BF16>::G* __restrict__ q, const typename Elem<BF16>::G* __restrict__ k,
     const typename Elem<BF16>::G* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, const float* __restrict__ S0, const int32_t* __restrict__ cu,
     int N, int H, int dv, int v_split, typename Elem<BF16>::G* __restrict__ o,
-    float* __restrict__ S_T, SegView seg, CkptView ck) {
+    float* __restrict__ S_T, SegView seg, CkptView ck, ChunkMap cm) {
+    static_assert(!MAP || (WIDE && !CK), "chunk lists need the wide-decay variant and outputs");
     using Sh = PrefillShape<BF16, DK, NC, CT, WIDE>;
     using T = Elem<BF16>;
     using E = typename T::E;
@@ -539,6 +549,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             }
             __syncthreads();
             n = sSeq[kSortMax];
+            if constexpr (MAP) n = __builtin_amdgcn_readfirstlane(n);  // addresses of scalar loads
         }
         t_beg = cu[n];
         t_end = cu[n + 1];
@@ -570,9 +581,25 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
         sdst = mode == 0 ? S_T + pair * DK * dv : (mode == 1 ? seg.dstate : seg.mstate) + blk * DK * dv;
         obase = mode == 2 ? static_cast<G*>(seg.qhat) : o;
     }
-    const int nchunks = (t_end - t_beg + C - 1) / C;
+    int nchunks = (t_end - t_beg + C - 1) / C;
+    const int* cs = nullptr;  // MAP: this (sequence, head)'s chunk starts, then the sequence end
+    if constexpr (MAP) {
+        // (every value read from the lists is clamped to the sequence, so
+        // that accesses stay in bounds whatever the lists hold)
+        cs = cm.starts + h * cm.stride + __builtin_amdgcn_readfirstlane(t_beg + 2 * n);
+        nchunks = min(max(scalar_load(cm.count + n * H + h), 0), t_end - t_beg);
+    }
     const int j0 = slice * BV;  // first value column of this workgroup
-    auto chunk_len = [&](int i) __attribute__((always_inline)) { return min(C, t_end - (t_beg + i * C)); };
+    // first token and length of chunk i (length 0 past the last chunk)
+    auto list_at = [&](int i) __attribute__((always_inline)) { return min(max(scalar_load(cs + i), t_beg), t_end); };
+    auto chunk_beg = [&](int i) __attribute__((always_inline)) {
+        if constexpr (MAP) return i < nchunks ? list_at(i) : t_end;
+        else return t_beg + i * C;
+    };
+    auto chunk_len = [&](int i) __attribute__((always_inline)) {
+        if constexpr (MAP) return i < nchunks ? min(max(list_at(i + 1) - list_at(i), 0), C) : 0;
+        else return min(C, t_end - (t_beg + i * C));
+    };
 
     // Per-token offsets below fit in 32 bits (the host rejects tensors of
     // 2^31 elements or more).
@@ -1017,7 +1044,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             __amdgpu_buffer_rsrc_t k, q, la, v, b;
         };
         auto rsrc_of = [&](int m) __attribute__((always_inline)) {
-            const int c0 = t_beg + m * C;
+            const int c0 = chunk_beg(m);
             // chunks past the end: empty ranges, no access (kept in a scalar register)
             const int len = __builtin_amdgcn_readfirstlane(max(0, chunk_len(m)));
             const size_t tok = static_cast<size_t>(c0) * strideK;
@@ -1082,6 +1109,26 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                 la[rr][2] = rla[x][rr].z;
                 la[rr][3] = rla[x][rr].w;
             }
+            // Chunk lists (MAP): a strong decay (below kStrongLogAlpha) can
+            // only be row 0's.  It acts on the entering state alone (no row
+            // of the chunk precedes it), so it is taken out of the rows'
+            // exponents and applied through Gamma_C and the state operand's
+            // scale 2^ref: the exponents keep the precision of the ordinary
+            // rows, and a decay that underflows alpha to 0 (even one whose
+            // log2 overflows to -inf) zeroes the entering state exactly.
+            float d0[4] = {0.f, 0.f, 0.f, 0.f};  // row 0's strong decay, log2 units
+            if constexpr (MAP) {
+                float z[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const bool strong = rg == 0 && la[0][c] < kStrongLogAlpha;
+                    z[c] = strong ? la[0][c] * kLog2e : 0.f;
+                    if (strong) la[0][c] = 0.f;
+                }
+                // lane cq (row group 0) holds row 0 of channel quad cq
+#pragma unroll
+                for (int c = 0; c < 4; ++c) d0[c] = __shfl(z[c], cq);
+            }
 #pragma unroll
             for (int c = 0; c < 4; ++c) tot[c] = ((la[0][c] + la[1][c]) + (la[2][c] + la[3][c])) * kLog2e;
             float4* const scan = reinterpret_cast<float4*>(smem + Sh::OFF_SCAN) + 64 * pw;
@@ -1099,7 +1146,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             }
             float Gc[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) Gc[c] = __builtin_amdgcn_exp2f(sum[c]);
+            for (int c = 0; c < 4; ++c) Gc[c] = __builtin_amdgcn_exp2f(MAP ? d0[c] + sum[c] : sum[c]);
             if (rg == 0) *reinterpret_cast<float4*>(sGC(S) + i0) = make_float4(Gc[0], Gc[1], Gc[2], Gc[3]);
             // Reference point of each channel's exponents: the chunk start; in
             // the wide-decay variant, the middle row for a channel whose decay
@@ -1123,8 +1170,10 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                 }
                 if (rg == 0)
                     *reinterpret_cast<float4*>(sGM(S) + i0) =
-                        make_float4(__builtin_amdgcn_exp2f(ref[0]), __builtin_amdgcn_exp2f(ref[1]),
-                                    __builtin_amdgcn_exp2f(ref[2]), __builtin_amdgcn_exp2f(ref[3]));
+                        make_float4(__builtin_amdgcn_exp2f(MAP ? d0[0] + ref[0] : ref[0]),
+                                    __builtin_amdgcn_exp2f(MAP ? d0[1] + ref[1] : ref[1]),
+                                    __builtin_amdgcn_exp2f(MAP ? d0[2] + ref[2] : ref[2]),
+                                    __builtin_amdgcn_exp2f(MAP ? d0[3] + ref[3] : ref[3]));
             }
             float kbar[4][4];
 #pragma unroll
@@ -1188,7 +1237,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
         // of the sequence fall outside the range and are dropped.
         G* const ohp = obase + static_cast<size_t>(h) * dv + j0;
         auto store_o = [&](int j, int S) __attribute__((always_inline)) {
-            const int c0 = t_beg + j * C;
+            const int c0 = chunk_beg(j);
             const int len = __builtin_amdgcn_readfirstlane(chunk_len(j));
             const auto r = buffer_rsrc(ohp + static_cast<size_t>(c0) * strideV, len * rowV);
             // after a failed hand-off in this workgroup: NaN rows instead
@@ -1253,17 +1302,18 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
 // BV = d_v / v_split: 4 waves x 2 tiles (128), 4 x 1 (64), 2 x 1 (32),
 // 1 x 1 (16); producer waves follow d_k.
 // ---------------------------------------------------------------------------
-template <bool BF16, int DK, int NC, int CT, bool SG, bool WIDE, bool CK = false>
-static hipError_t launch_prefill_t(const PrefillArgs& a, const SegView& seg, const CkptView& ck = CkptView{}) {
+template <bool BF16, int DK, int NC, int CT, bool SG, bool WIDE, bool CK = false, bool MAP = false>
+static hipError_t launch_prefill_t(const PrefillArgs& a, const SegView& seg, const CkptView& ck = CkptView{},
+                                   const ChunkMap& cm = ChunkMap{}) {
     using G = typename Elem<BF16>::G;
     using Sh = PrefillShape<BF16, DK, NC, CT, WIDE>;
     const unsigned units = seg.units ? static_cast<unsigned>(seg.umax) : static_cast<unsigned>(a.N);
     const unsigned per_unit = static_cast<unsigned>(a.v_split) * (seg.units ? 2u : 1u);
     const unsigned grid = units * static_cast<unsigned>(a.H) * per_unit;
-    hipLaunchKernelGGL((prefill_kernel<BF16, DK, NC, CT, SG, WIDE, CK>), dim3(grid), dim3(Sh::NT), 0,
+    hipLaunchKernelGGL((prefill_kernel<BF16, DK, NC, CT, SG, WIDE, CK, MAP>), dim3(grid), dim3(Sh::NT), 0,
                        static_cast<hipStream_t>(a.stream), static_cast<const G*>(a.q),
                        static_cast<const G*>(a.k), static_cast<const G*>(a.v), a.log_alpha, a.beta,
-                       a.S0, a.cu_seqlens, a.N, a.H, a.d_v, a.v_split, static_cast<G*>(a.o), a.S_T, seg, ck);
+                       a.S0, a.cu_seqlens, a.N, a.H, a.d_v, a.v_split, static_cast<G*>(a.o), a.S_T, seg, ck, cm);
     return hipGetLastError();
 }
 
@@ -1344,6 +1394,39 @@ hipError_t launch_prefill(const PrefillArgs& a) {
     const hipError_t e = a.bf16 ? launch_prefill_dt<true>(a, seg) : launch_prefill_dt<false>(a, seg);
     if (e != hipSuccess || !segmented) return e;
     return launch_seg_fixup(a, seg);
+}
+
+template <bool BF16, int DK, int NC, int CT>
+static hipError_t launch_mapped_sg(const PrefillArgs& a, const ChunkMap& cm) {
+    return a.scalar_gate ? launch_prefill_t<BF16, DK, NC, CT, true, true, false, true>(a, SegView{}, CkptView{}, cm)
+                         : launch_prefill_t<BF16, DK, NC, CT, false, true, false, true>(a, SegView{}, CkptView{}, cm);
+}
+
+template <bool BF16, int DK>
+static hipError_t launch_mapped_dk(const PrefillArgs& a, const ChunkMap& cm) {
+    switch (a.d_v / a.v_split) {
+        case 128: return launch_mapped_sg<BF16, DK, 4, 2>(a, cm);
+        case 64: return launch_mapped_sg<BF16, DK, 4, 1>(a, cm);
+        case 32: return launch_mapped_sg<BF16, DK, 2, 1>(a, cm);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Any-decay prefill: the chunk lists, then one workgroup per (sequence,
+// head, value slice) over them (never segmented).  The value split follows
+// the rule of default_v_split for whole sequences.
+hipError_t launch_prefill_mapped(const PrefillArgs& a0) {
+    PrefillArgs a = a0;
+    a.v_split = a.d_v == 128 && static_cast<int64_t>(a.N) * a.H * 2 <= a.cus / 2 ? 2 : 1;
+    ChunkMap cm{};
+    const hipError_t e = launch_any_map(a, &cm);
+    if (e != hipSuccess) return e;
+    switch (a.d_k) {
+        case 32: return a.bf16 ? launch_mapped_dk<true, 32>(a, cm) : launch_mapped_dk<false, 32>(a, cm);
+        case 64: return a.bf16 ? launch_mapped_dk<true, 64>(a, cm) : launch_mapped_dk<false, 64>(a, cm);
+        case 128: return a.bf16 ? launch_mapped_dk<true, 128>(a, cm) : launch_mapped_dk<false, 128>(a, cm);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 int32_t default_v_split(int32_t N, int64_t T_tot, int32_t H, int32_t d_k, int32_t d_v, bool bf16, int cus) {

@@ -208,6 +208,26 @@ def make_workload(name: str) -> PrefillInputs:
                                w["log_alpha_range"], w["s0_std"], rng=rng)
 
 
+def make_any_decay_workload(resets_per_sequence: int = 8, seed: int = 13) -> PrefillInputs:
+    """The 32k-token batch of eight sequences (the lengths, heads, head sizes
+    and dtype of prefill_varlen8_32k_h32_d128_bf16) with gates outside the
+    chunked kernels' contract: log alpha = -U(0, 5) per token, head and
+    channel, and hard resets (log alpha = -1000 on every channel of every
+    head: document boundaries inside a packed sequence) at
+    ``resets_per_sequence`` seeded token positions of each sequence."""
+    x = make_workload("prefill_varlen8_32k_h32_d128_bf16")
+    rng = np.random.default_rng(seed)
+    la = rng.random(x.log_alpha.shape, dtype=np.float32)
+    la *= np.float32(-5.0)
+    cu = x.cu_seqlens
+    for n in range(int(cu.shape[0]) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        rows = rng.choice(b - a, size=min(resets_per_sequence, b - a), replace=False) + a
+        la[rows] = np.float32(-1000.0)
+    x.log_alpha = la
+    return x
+
+
 def make_backward_grads(x: PrefillInputs, seed, with_dS_T: bool = True):
     """Upstream gradients for a backward pass over the batch ``x``: dL/do
     [T_tot, H, d_v] (N(0,1), rounded to x's storage dtype) and dL/dS_T

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 5
+#define KDA_VERSION 6
 
 typedef enum {
     KDA_OK = 0,
@@ -149,10 +149,22 @@ kda_status kda_prefill_split(const void* q, const void* k, const void* v,
  *   KDA_PREFILL_ANY_DECAY    no range contract: any finite log_alpha <= 0,
  *                            including hard resets (a token whose alpha
  *                            underflows to 0 clears the state exactly).
- *                            Runs the recurrence token by token in fp32
- *                            on the vector ALU (no chunk factorization);
- *                            much slower than the chunked kernel.  v_split
- *                            and the workspace are not used.  Excludes
+ *                            With a workspace of at least
+ *                            kda_prefill_workspace_size_ex(..., flags)
+ *                            bytes (256-byte aligned) it runs the chunked
+ *                            kernel over chunk lists: a token with
+ *                            log_alpha below -5 on some channel starts a
+ *                            new chunk (the chunk before it is padded with
+ *                            zero rows), which keeps every chunk within the
+ *                            wide-decay contract; the workspace holds those
+ *                            lists, written by a first kernel on the same
+ *                            stream.  The cost grows with the number of such
+ *                            tokens (at most one chunk per token).  With a
+ *                            smaller (or no) workspace it runs the
+ *                            recurrence token by token in fp32 on the
+ *                            vector ALU, much slower.  v_split is not used
+ *                            (the value split of kda_prefill for whole
+ *                            sequences is taken).  Excludes
  *                            KDA_PREFILL_WIDE_DECAY.
  *
  * Unknown flag bits give KDA_ERR_INVALID_ARG.
@@ -177,6 +189,14 @@ kda_status kda_prefill_ex(const void* q, const void* k, const void* v,
  * the one for 256 compute units (MI355X). */
 size_t kda_prefill_workspace_size(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
                                   int32_t d_v, kda_dtype dtype);
+
+/* Bytes of workspace kda_prefill_ex needs for these sizes and flags: with
+ * KDA_PREFILL_ANY_DECAY, the chunk lists of its chunked path and one flag
+ * byte per token and head: up256(4 N H) + up256(4 H (T_tot + 2 N)) + H T_tot
+ * bytes, up256(x) = x rounded up to a multiple of 256; otherwise
+ * kda_prefill_workspace_size.  0 for unsupported sizes or invalid flags. */
+size_t kda_prefill_workspace_size_ex(int32_t N, int64_t T_tot, int32_t H, int32_t d_k,
+                                     int32_t d_v, kda_dtype dtype, uint32_t flags);
 
 /* The v_split kda_prefill would use for these sizes on the current device
  * (1, 2, 4 or 8), or 0 if the sizes are not supported; 256 compute units

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.kda_version() == 5
+    assert kda.kda_version() == 6
     for s in (0, 1, 2, 3):
         assert kda.kda_status_string(s).startswith("KDA_")
     assert "unknown" in kda.kda_status_string(99)
@@ -157,6 +157,27 @@ def test_workspace_and_default_split_queries():
         assert s in (1, 2, 4, 8)
     assert kda.kda_prefill_default_split(1, 10, 1, 48, 128, BF16) == 0
     assert kda.kda_prefill_default_split(1, 10, 1, 32, 32, BF16) in (1, 2)
+
+
+def test_workspace_size_ex_with_flags():
+    """Any decay: the chunk lists (counts [N H] int32 and H (T_tot + 2 N) int32
+    starts, each rounded up to 256 bytes) and one flag byte per token and head;
+    other flags: kda_prefill_workspace_size."""
+    ANY, WIDE, SG = kda.KDA_PREFILL_ANY_DECAY, kda.KDA_PREFILL_WIDE_DECAY, kda.KDA_PREFILL_SCALAR_GATE
+    for (N, T, H) in ((8, 32677, 32), (1, 131072, 32), (3, 0, 2), (70, 3000, 2)):
+        lists = (4 * N * H + 255) // 256 * 256 + (4 * H * (T + 2 * N) + 255) // 256 * 256 + H * T
+        for extra in (0, SG):
+            assert kda.kda_prefill_workspace_size_ex(N, T, H, 128, 128, BF16, ANY | extra) == lists
+            assert kda.kda_prefill_workspace_size_ex(N, T, H, 64, 32, F32, ANY | extra) == lists
+        for flags in (0, SG, WIDE, WIDE | SG):
+            assert (kda.kda_prefill_workspace_size_ex(N, T, H, 128, 128, BF16, flags)
+                    == kda.kda_prefill_workspace_size(N, T, H, 128, 128, BF16))
+    assert kda.kda_prefill_workspace_size_ex(1, 4096, 32, 128, 128, BF16, 0) > 0  # segmented
+    assert kda.kda_prefill_workspace_size_ex(1, 64, 2, 128, 128, BF16, ANY | WIDE) == 0
+    assert kda.kda_prefill_workspace_size_ex(1, 64, 2, 128, 128, BF16, 8) == 0
+    assert kda.kda_prefill_workspace_size_ex(1, 64, 2, 48, 128, BF16, ANY) == 0
+    assert kda.kda_prefill_workspace_size_ex(0, 64, 2, 128, 128, BF16, ANY) == 0
+    assert kda.kda_prefill_workspace_size_ex(1, -1, 2, 128, 128, BF16, ANY) == 0
 
 
 def _plan(N, T, H, d, cus, dtype=BF16):
