@@ -247,10 +247,22 @@ __device__ __forceinline__ void buf_store_f1(__amdgpu_buffer_rsrc_t r, int voff,
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
 }
 
+// A buffer store of more than 8 bytes followed by a vector-ALU write of its
+// data registers needs a wait state between them.  The compiler inserts it
+// only for stores whose soffset is not a register (it takes the hazard to
+// be absent otherwise), and on gfx950 it is not: with a register soffset a
+// data register overwritten by the next instruction was measured to corrupt
+// one element of some lanes' stores.  Wide stores therefore pass their whole
+// offset in voffset, with an immediate soffset of 0; the sum is formed
+// unsigned, so an offset past the range (kNoAccess) stays past it.
+__device__ __forceinline__ int store_voffset(int voff, int soff) {
+    return static_cast<int>(static_cast<unsigned>(voff) + static_cast<unsigned>(soff));
+}
+
 __device__ __forceinline__ void buf_store_f4(__amdgpu_buffer_rsrc_t r, int voff, int soff, float a, float b, float c,
                                              float d) {
     const u32x4_t x = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
-    __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, store_voffset(voff, soff), 0, 0);
 }
 
 }  // namespace kda
