@@ -1044,7 +1044,7 @@ hipError_t launch_prefill_bwd_chunk(const BackwardArgs& b) {
     void* ckw = ws + (per * b.d_k * b.d_v * es + 255) / 256 * 256;
     // pass 1: the forward with checkpoints (no outputs)
     PrefillArgs p{b.q, b.k, b.v, b.log_alpha, b.beta, b.S0, b.cu_seqlens, b.N, b.T_tot, b.H, b.d_k, b.d_v,
-                  b.bf16, nullptr, nullptr, 1, b.stream, nullptr, kDefaultCUs, b.scalar_gate, false, false};
+                  b.bf16, nullptr, nullptr, 1, b.stream, nullptr, device_cus_or_default(), b.scalar_gate, false, false};
     hipError_t e = launch_prefill_ckpt(p, CkptView{cks, ckw});
     if (e != hipSuccess) return e;
     // pass 2: the reverse walk over the chunks

@@ -78,6 +78,11 @@ constexpr size_t align16(size_t x) { return (x + 15) & ~static_cast<size_t>(15);
 // this many sequences; larger batches run in natural order.
 constexpr int kSortMax = 64;
 constexpr size_t kLdsBudget = 160 * 1024;
+// Pacing of a launch that fills the GPU (see the producer loop): the chunk
+// period assumed for the batch's longest sequence, in ns.  It lies below the
+// period measured for that sequence with every CU busy (about 2.1 us for bf16,
+// d_k = 128, 128 value columns), so paced workgroups finish before it.
+constexpr int kPaceNs = 1700;
 // Wide-decay variant: a channel whose decay over one chunk is below
 // -kRefSwitchLog2 (log2 units, about e^-69) takes its exponents relative to
 // the chunk's middle row.
@@ -366,7 +371,8 @@ __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, int voff, c
     }
 }
 
-// four consecutive storage elements, raw (stores past the range are dropped)
+// four consecutive storage elements, raw (stores past the range are
+// dropped); a 16-byte store takes its whole offset in voffset (store_voffset)
 template <bool BF16>
 __device__ __forceinline__ void buf_store_raw4(__amdgpu_buffer_rsrc_t r, int voff, int soff,
                                                const typename Elem<BF16>::R4& x) {
@@ -375,7 +381,7 @@ __device__ __forceinline__ void buf_store_raw4(__amdgpu_buffer_rsrc_t r, int vof
     } else {
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4_t{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)}, r,
-            voff, soff, 0);
+            store_voffset(voff, soff), 0, 0);
     }
 }
 
@@ -452,7 +458,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
     const typename Elem<BF16>::G* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, const float* __restrict__ S0, const int32_t* __restrict__ cu,
     int N, int H, int dv, int v_split, typename Elem<BF16>::G* __restrict__ o,
-    float* __restrict__ S_T, SegView seg, CkptView ck, ChunkMap cm) {
+    float* __restrict__ S_T, SegView seg, CkptView ck, ChunkMap cm, int pace16) {
     static_assert(!MAP || (WIDE && !CK), "chunk lists need the wide-decay variant and outputs");
     using Sh = PrefillShape<BF16, DK, NC, CT, WIDE>;
     using T = Elem<BF16>;
@@ -1003,6 +1009,24 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
         // key channels i0 .. i0 + 3 of this wave's channel strip, so that
         // consecutive lanes load consecutive bytes of a row.
         const int pw = wave - NC;
+        // Pacing (pace16 > 0: 16 x 10-ns ticks per chunk of the longest
+        // sequence; whole sequences, sorted by length).  The launch is one
+        // round of workgroups whose makespan is the longest sequence's chain
+        // of chunks; a shorter sequence has slack.  Its producers issue the
+        // loads of chunk j no earlier than j T / n after the start (n its
+        // chunks, T the longest sequence's chunks x kPaceNs), so its memory
+        // traffic spreads over the whole launch instead of competing with
+        // the longest chains at the start.
+        int pace = 0;  // ticks x 16 per chunk of this sequence
+        uint64_t pt0 = 0;
+        if (pace16 > 0 && seg.units == nullptr && N > 1 && N <= kSortMax) {
+            int lmax = 0;
+            for (int j = 0; j < N; ++j) lmax = max(lmax, sSeq[j]);
+            const int lc = (lmax + C - 1) / C;
+            if (nchunks > 0 && nchunks * 10 < lc * 9)
+                pace = static_cast<int>(static_cast<int64_t>(lc) * pace16 / nchunks);
+            pt0 = __builtin_amdgcn_s_memrealtime();  // 100 MHz
+        }
         const int strip = pw % NPS;  // channel strip
         const int par = pw / NPS;    // parity of the chunks this wave prepares (PP == 2)
         const int rg = lane / QW;
@@ -1273,6 +1297,10 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             }
             prep12(X, P);
             ctr_publish(prodDone + pw, m + 1, lane);
+            if (pace > 0 && m + STRIDE < nchunks) {
+                const uint64_t due = pt0 + ((static_cast<uint64_t>(m + STRIDE) * pace) >> 4);
+                while (__builtin_amdgcn_s_memrealtime() < due) __builtin_amdgcn_s_sleep(1);
+            }
             load_chunk(X, m + STRIDE);
             P += PP;
             if (P >= 3) P -= 3;
@@ -1310,10 +1338,15 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, const SegView& seg, con
     const unsigned units = seg.units ? static_cast<unsigned>(seg.umax) : static_cast<unsigned>(a.N);
     const unsigned per_unit = static_cast<unsigned>(a.v_split) * (seg.units ? 2u : 1u);
     const unsigned grid = units * static_cast<unsigned>(a.H) * per_unit;
+    // pacing: the shape whose fully occupied chunk period was measured, on
+    // whole sequences (ordered in-kernel), when the launch fills the GPU
+    const bool pace = BF16 && DK == 128 && NC == 4 && CT == 2 && seg.units == nullptr && a.N > 1 &&
+                      a.N <= kSortMax && grid >= static_cast<unsigned>(a.cus);
     hipLaunchKernelGGL((prefill_kernel<BF16, DK, NC, CT, SG, WIDE, CK, MAP>), dim3(grid), dim3(Sh::NT), 0,
                        static_cast<hipStream_t>(a.stream), static_cast<const G*>(a.q),
                        static_cast<const G*>(a.k), static_cast<const G*>(a.v), a.log_alpha, a.beta,
-                       a.S0, a.cu_seqlens, a.N, a.H, a.d_v, a.v_split, static_cast<G*>(a.o), a.S_T, seg, ck, cm);
+                       a.S0, a.cu_seqlens, a.N, a.H, a.d_v, a.v_split, static_cast<G*>(a.o), a.S_T, seg, ck, cm,
+                       pace ? kPaceNs * 16 / 10 : 0);
     return hipGetLastError();
 }
 
