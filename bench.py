@@ -501,6 +501,11 @@ def main():
     esize = 2 if x.dtype == "bf16" else 4
     split = args.v_split or kda.kda_prefill_default_split(x.N, x.T_tot, x.H, x.d_k, x.d_v,
                                                           0 if x.dtype == "bf16" else 1)
+    # The decode line is timed first: its ~210 launches (about 40 ms) also
+    # bring the device out of its idle clocks, which otherwise take some 40
+    # launches of this prefill to ramp up (0.58 ms per launch at first against
+    # 0.52 ms after).
+    dres = None if args.no_decode else bench_decode(kda, torch, args.decode_steps, 10, args.decode_inputs)
     wall, kms = bench_prefill(kda, torch, x, args.steps, args.warmup, split)
     ms_per_step = wall * 1e3 / args.steps
     k_avg_ms = sum(kms) / len(kms)
@@ -542,8 +547,10 @@ def main():
                  "counter": "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs), "
                             "from the committed rocprofv3 summary; null when the kernel changed since"},
     }
+    out["order"] = ("decode line, then the headline prefill (W warmup + K timed steps), GDN, backward, "
+                    "any-decay, sub-workloads")
     if not args.no_decode:
-        d = bench_decode(kda, torch, args.decode_steps, 10, args.decode_inputs)
+        d = dres
         us = d["us"]
         mean_us = sum(us) / len(us)
         med_us = us[len(us) // 2]

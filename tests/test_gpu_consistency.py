@@ -47,6 +47,23 @@ def test_packing_does_not_change_bits(lengths):
         assert torch.equal(on, o[a:b]) and torch.equal(Sn[0], S[n]), f"sequence {n}"
 
 
+def test_paced_batch_keeps_the_bits_of_each_sequence_alone():
+    """A batch that fills the GPU (8 sequences x 32 heads, bf16, d = 128) paces
+    the loads of its shorter sequences; each sequence alone (32 workgroups,
+    unpaced) gives the same bits."""
+    import torch
+    x = _x([1000, 700, 333, 90, 64, 33, 1, 250], H=32, dk=128, dv=128, seed=17)
+    d = upload(x)
+    o, S = kda.prefill(**d)
+    for n in range(x.N):
+        a, b = int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1])
+        cu = torch.tensor([0, b - a], dtype=torch.int32, device="cuda")
+        on, Sn = kda.prefill(d["q"][a:b].contiguous(), d["k"][a:b].contiguous(), d["v"][a:b].contiguous(),
+                             d["log_alpha"][a:b].contiguous(), d["beta"][a:b].contiguous(),
+                             d["S0"][n:n + 1].contiguous(), cu)
+        assert torch.equal(on, o[a:b]) and torch.equal(Sn[0], S[n]), f"sequence {n}"
+
+
 @pytest.mark.parametrize("lengths", [[70, 0, 0, 10], [70, 0, 0, 4500]], ids=["short", "segmented"])
 def test_in_place_state_and_empty_sequences(lengths):
     import torch
