@@ -746,6 +746,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
 
         F8 sf[CT][KB];
         f32x4_t Rp[CT][NB], U[CT][NB];
+        f32x4_t accQS[CT][NB];  // Q~ S of the chunk's rows, formed beside R'
         F4 uf[CT][NB];
 
         // Checkpoints for the chunked backward pass (CK): per chunk, the
@@ -783,7 +784,8 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             lds_store4<BF16>(base + e, -rpv[0], -rpv[1], -rpv[2], -rpv[3]);
         };
 
-        // R' = beta (K~ S - V)  (= -R)
+        // R' = beta (K~ S - V)  (= -R), and beside it Q~ S for the outputs: the
+        // same S fragments, independent accumulators (off the U and S chain)
         auto chain_R = [&](int B, int ci) __attribute__((always_inline)) {
             if constexpr (WIDE) {
                 // the S operand of K~ S and Q~ S with its rows (key channels)
@@ -818,6 +820,16 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) Rp[ct][rt] = mma8<BF16>(Rp[ct][rt], a, sf[ct][kb]);
                 }
+                if constexpr (!CK) {
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) accQS[ct][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const F8 aq = tile_frag8<BF16, UK>(tQ(B), 16 * rt + ln, kb, lg);
+#pragma unroll
+                        for (int ct = 0; ct < CT; ++ct) accQS[ct][rt] = mma8<BF16>(accQS[ct][rt], aq, sf[ct][kb]);
+                    }
+                }
                 if constexpr (CK) {
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) ck_store_w0(ci, ct, rt, Rp[ct][rt]);
@@ -833,7 +845,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
         auto u_frag8 = [&](int ct, int b) __attribute__((always_inline)) {
             return F8(__builtin_shufflevector(uf[ct][b], uf[ct][b + 1], 0, 1, 2, 3, 4, 5, 6, 7));
         };
-        // U_b = (-T_bb) (R'_b + sum_{c<b} L_bc U_c);  then O^T = S^T Q~^T + U^T A_qk^T,
+        // U_b = (-T_bb) (R'_b + sum_{c<b} L_bc U_c);  then O^T = (Q~ S)^T + U^T A_qk^T,
         // written to global memory from the C layout: lane (ln, lg) holds
         // four consecutive value columns of token row 16 rt + ln.
         auto chain_UO = [&](int B, int J) __attribute__((always_inline)) {
@@ -871,13 +883,7 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             for (int rt = 0; rt < NB; ++rt) {
                 f32x4_t acc[CT];
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const F8 aq = tile_frag8<BF16, UK>(tQ(B), 16 * rt + ln, kb, lg);
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) acc[ct] = mma8<BF16>(acc[ct], aq, sf[ct][kb]);
-                }
+                for (int ct = 0; ct < CT; ++ct) acc[ct] = accQS[ct][rt];
 #pragma unroll
                 for (int sp = 0; sp + 1 <= rt; sp += 2) {
                     const F8 aa = lds_frag8<BF16>(tA(J) + 16 * rt * LDJ + 16 * sp, LDJ, lane);
