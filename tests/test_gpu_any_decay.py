@@ -224,3 +224,15 @@ def test_any_decay_full_batch_sampled_heads():
     o, ST = host(o), host(ST)
     assert_close(o[:, heads], ref_o[:, heads], "bf16", "o (sampled heads)")
     assert_close(ST[:, heads], ref_S[:, heads], "bf16", "S_T (sampled heads)")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_any_decay_all_sequences_empty(path):
+    """T_tot = 0: no flag work, every list empty; S_T equals S0 exactly."""
+    import torch
+    x = inputs.make_prefill_inputs([0, 0, 0], 2, 64, 64, "bf16", seed=5, s0_std=1.0)
+    d = upload(x)
+    o, ST = _run(d, path)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0
+    assert torch.equal(ST, d["S0"])
