@@ -959,13 +959,17 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                 const int J = i & 1;
                 const int Pn = P == 2 ? 0 : P + 1;
                 const bool has_next = i + 1 < nchunks;
+                // R' and Q~ S need only this chunk's tiles (awaited before):
+                // formed ahead of the waits, they give the producers that
+                // time to finish the next chunk's tiles, and the other
+                // consumers to store this chunk's jobs.
+                chain_R(P, i);
                 ctr_wait(nSolved, NC * (i + 1), fault);  // jobs of chunk i stored
                 if (has_next) wait_tiles(i + 1);
                 if constexpr (kJobs) {
 #pragma unroll
                     for (int t = 0; t < JPW; ++t) jobs[t] = prep3_compute(Pn, t);
                 }
-                chain_R(P, i);
                 chain_UO(P, J);
                 chain_S(P);
                 ctr_signal(nFree, lane);
