@@ -1167,15 +1167,19 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             for (int c = 0; c < 4; ++c) tot[c] = ((la[0][c] + la[1][c]) + (la[2][c] + la[3][c])) * kLog2e;
             float4* const scan = reinterpret_cast<float4*>(smem + Sh::OFF_SCAN) + 64 * pw;
             scan[lane] = make_float4(tot[0], tot[1], tot[2], tot[3]);
-            float g[4] = {0.f, 0.f, 0.f, 0.f}, sum[4] = {0.f, 0.f, 0.f, 0.f};
+            // One running sum: the groups before this one (g) are the sum
+            // after group rg - 1, and in the wide-decay variant the first
+            // half of the chunk (mid) the sum after group NRG / 2 - 1.
+            float g[4] = {0.f, 0.f, 0.f, 0.f}, sum[4] = {0.f, 0.f, 0.f, 0.f}, mid[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int r = 0; r < NRG; ++r) {
                 const float4 t4 = scan[QW * r + cq];
                 const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    g[c] = r < rg ? g[c] + tv[c] : g[c];  // groups before this one
                     sum[c] += tv[c];
+                    g[c] = r < rg ? sum[c] : g[c];
+                    if (r == NRG / 2 - 1) mid[c] = sum[c];
                 }
             }
             float Gc[4];
@@ -1188,15 +1192,6 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             // exponent is then bounded by the decay of C/2 tokens).
             float ref[4] = {0.f, 0.f, 0.f, 0.f}, GcR[4] = {Gc[0], Gc[1], Gc[2], Gc[3]};
             if constexpr (WIDE) {
-                float mid[4] = {0.f, 0.f, 0.f, 0.f};  // rows 0 .. C/2 - 1
-#pragma unroll
-                for (int r = 0; r < NRG / 2; ++r) {
-                    const float4 t4 = scan[QW * r + cq];
-                    mid[0] += t4.x;
-                    mid[1] += t4.y;
-                    mid[2] += t4.z;
-                    mid[3] += t4.w;
-                }
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     ref[c] = sum[c] < -kRefSwitchLog2 ? mid[c] : 0.f;
