@@ -440,8 +440,31 @@ __device__ __forceinline__ void ctr_wait(int* ctr, int target, int* fault) {
     asm volatile("" ::: "memory");
 }
 
-// Waits until each of n progress counters has reached target.
+// Waits until each of n progress counters has reached target.  Four
+// counters (16-byte aligned) are read with one LDS access: each 32-bit
+// counter is read whole, and they only grow, so a snapshot whose minimum
+// has reached the target means every one of them has.
 __device__ __forceinline__ void ctr_wait_each(int* ctrs, int n, int target, int* fault) {
+    if (n == 4) {
+        typedef int i32x4_t __attribute__((ext_vector_type(4)));
+        typedef const volatile __attribute__((address_space(3))) i32x4_t Lds4;
+        Lds4* const p4 = (Lds4*)(ctrs);
+        int spins = 0;
+        for (;;) {
+            const i32x4_t c = *p4;
+            // (the same value in every lane: a scalar branch)
+            if (__builtin_amdgcn_readfirstlane(min(min(c[0], c[1]), min(c[2], c[3]))) >= target) break;
+            ++spins;
+            if (spins > kSpinMax ||
+                (spins % kFaultPoll == 0 && __hip_atomic_load(fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0)) {
+                __hip_atomic_store(fault, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+        return;
+    }
     for (int w = 0; w < n; ++w) ctr_wait(ctrs + w, target, fault);
 }
 
