@@ -101,8 +101,8 @@ __device__ __forceinline__ int scalar_load(const int* p) { return *(ConstI32*)(p
 // Gamma_C, beta) rotate through three slots, so the producers can run two
 // chunks ahead of the recurrence (the consumers read chunk i+1's tiles for
 // its Gram products while they run chunk i); the consumers' job results
-// (L, A_qk, -T_bb) alternate between two buffers.  Slot s starts at
-// s * PBUF, job buffer b at OFF_JOB + b * JBUF.
+// (L, A_qk, -T_bb) alternate between two buffers.  Each tile's copies are
+// adjacent (tile-major): copy s of tile X at O_X + s * SZ_X.
 //
 // Operand tiles (the producers' tiles) are unpadded and swizzled in 16-byte
 // units (see quad_off): UK units per row of a [C][DK] tile, UT per row of a
@@ -129,23 +129,23 @@ struct Layout {
     static constexpr size_t SZ_GM = WIDE ? align16(DK * 4) : 0;  // 2^ref       [DK] (wide decay)
     static constexpr size_t SZ_L = align16(C * LDJ * ES);        // L, A_qk     [C][LDJ]
     static constexpr size_t SZ_T = align16(NB * 16 * LDT * ES);  // -T_bb       [NB][16][LDT]
-    // producer slot
+    // producer tiles, tile-major: the NSLOT copies of a tile are adjacent
+    // (slot s at O_X + s * SZ_X), so that with the slot known at compile
+    // time a tile access is a lane offset plus an immediate
     static constexpr size_t O_KB = 0;
-    static constexpr size_t O_Q = O_KB + SZ_KB;
-    static constexpr size_t O_KH = O_Q + SZ_KB;
-    static constexpr size_t O_KBT = O_KH + SZ_KB;
-    static constexpr size_t O_VT = O_KBT + SZ_KBT;
-    static constexpr size_t O_GC = O_VT + SZ_VT;
-    static constexpr size_t O_BETA = O_GC + SZ_GC;
-    static constexpr size_t O_GM = O_BETA + SZ_BETA;
-    static constexpr size_t PBUF = O_GM + SZ_GM;
-    // job buffer
-    static constexpr size_t OFF_JOB = NSLOT * PBUF;
+    static constexpr size_t O_Q = O_KB + NSLOT * SZ_KB;
+    static constexpr size_t O_KBT = O_Q + NSLOT * SZ_KB;
+    static constexpr size_t O_VT = O_KBT + NSLOT * SZ_KBT;
+    static constexpr size_t O_KH = O_VT + NSLOT * SZ_VT;
+    static constexpr size_t O_GC = O_KH + NSLOT * SZ_KB;
+    static constexpr size_t O_BETA = O_GC + NSLOT * SZ_GC;
+    static constexpr size_t O_GM = O_BETA + NSLOT * SZ_BETA;
+    // job buffers, the same way: buffer b of X at OFF_JOB + O_X + b * SZ_X
+    static constexpr size_t OFF_JOB = O_GM + NSLOT * SZ_GM;
     static constexpr size_t O_L = 0;
-    static constexpr size_t O_A = O_L + SZ_L;
-    static constexpr size_t O_T = O_A + SZ_L;
-    static constexpr size_t JBUF = O_T + SZ_T;
-    static constexpr size_t OFF_SCAN = OFF_JOB + 2 * JBUF;  // producers' scan scratch: [8][64] float4
+    static constexpr size_t O_A = O_L + 2 * SZ_L;
+    static constexpr size_t O_T = O_A + 2 * SZ_L;
+    static constexpr size_t OFF_SCAN = OFF_JOB + O_T + 2 * SZ_T;  // producers' scan scratch: [8][64] float4
     static constexpr size_t OFF_SEQ = OFF_SCAN + 8 * 64 * 16;
     static constexpr size_t OFF_CTR = OFF_SEQ + align16((kSortMax + 1) * 4);
     static constexpr size_t BYTES = OFF_CTR + 64;
@@ -500,18 +500,18 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
 #define KDA_TILE(name, type, base, stride, off) \
     auto name = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<type*>(smem + (base) + b * (stride) + (off)); }
     // producer slots 0..2
-    KDA_TILE(tKb, E, 0, Sh::PBUF, Sh::O_KB);
-    KDA_TILE(tQ, E, 0, Sh::PBUF, Sh::O_Q);
-    KDA_TILE(tKh, E, 0, Sh::PBUF, Sh::O_KH);
-    KDA_TILE(tKbT, E, 0, Sh::PBUF, Sh::O_KBT);
-    KDA_TILE(tVt, E, 0, Sh::PBUF, Sh::O_VT);
-    KDA_TILE(sGC, float, 0, Sh::PBUF, Sh::O_GC);
-    KDA_TILE(sGM, float, 0, Sh::PBUF, Sh::O_GM);
-    KDA_TILE(sBeta, float, 0, Sh::PBUF, Sh::O_BETA);
+    KDA_TILE(tKb, E, Sh::O_KB, Sh::SZ_KB, 0);
+    KDA_TILE(tQ, E, Sh::O_Q, Sh::SZ_KB, 0);
+    KDA_TILE(tKh, E, Sh::O_KH, Sh::SZ_KB, 0);
+    KDA_TILE(tKbT, E, Sh::O_KBT, Sh::SZ_KBT, 0);
+    KDA_TILE(tVt, E, Sh::O_VT, Sh::SZ_VT, 0);
+    KDA_TILE(sGC, float, Sh::O_GC, Sh::SZ_GC, 0);
+    KDA_TILE(sGM, float, Sh::O_GM, Sh::SZ_GM, 0);
+    KDA_TILE(sBeta, float, Sh::O_BETA, Sh::SZ_BETA, 0);
     // job buffers 0..1
-    KDA_TILE(tL, E, Sh::OFF_JOB, Sh::JBUF, Sh::O_L);
-    KDA_TILE(tA, E, Sh::OFF_JOB, Sh::JBUF, Sh::O_A);
-    KDA_TILE(tT, E, Sh::OFF_JOB, Sh::JBUF, Sh::O_T);
+    KDA_TILE(tL, E, Sh::OFF_JOB + Sh::O_L, Sh::SZ_L, 0);
+    KDA_TILE(tA, E, Sh::OFF_JOB + Sh::O_A, Sh::SZ_L, 0);
+    KDA_TILE(tT, E, Sh::OFF_JOB + Sh::O_T, Sh::SZ_T, 0);
 #undef KDA_TILE
     int* const sSeq = reinterpret_cast<int*>(smem + Sh::OFF_SEQ);
     // Monotonic counters, one signal per wave per chunk:
@@ -977,10 +977,11 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                 ctr_signal(nSolved, lane);
                 if constexpr (CK) ck_store_state(0);
             }
-            int P = 0;
-            for (int i = 0; i < nchunks; ++i) {
-                const int J = i & 1;
+            // Chunk i: producer slot P = i mod 3 and job buffer J = i & 1.
+            auto chunk = [&](auto PC, int i) __attribute__((always_inline)) {
+                const int P = PC;  // a compile-time constant in the unrolled loop below
                 const int Pn = P == 2 ? 0 : P + 1;
+                const int J = i & 1;
                 const bool has_next = i + 1 < nchunks;
                 // R' and Q~ S need only this chunk's tiles (awaited before):
                 // formed ahead of the waits, they give the producers that
@@ -1006,7 +1007,26 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
                     // next chunk's hand-offs are awaited
                     if constexpr (CK) ck_store_state(i + 1);
                 }
-                P = Pn;
+            };
+            // Unrolled over three chunks the slot is a constant in each copy,
+            // and with the tile-major layout a tile read is a lane offset plus
+            // an immediate.  The shapes whose registers are tighter (one state
+            // tile per wave, or the checkpointing pass) keep the rolled loop:
+            // unrolled, they spill.
+            if constexpr (CT >= 2 && !CK) {
+                for (int i = 0; i < nchunks; i += 3) {
+                    chunk(ic<0>{}, i);
+                    if (i + 1 >= nchunks) break;
+                    chunk(ic<1>{}, i + 1);
+                    if (i + 2 >= nchunks) break;
+                    chunk(ic<2>{}, i + 2);
+                }
+            } else {
+                int P = 0;
+                for (int i = 0; i < nchunks; ++i) {
+                    chunk(P, i);
+                    P = P == 2 ? 0 : P + 1;
+                }
             }
         };
         if (NC < NJOB || wave < NJOB)
