@@ -1012,8 +1012,10 @@ __global__ __launch_bounds__((PrefillShape<BF16, DK, NC, CT, WIDE>::NT)) void pr
             // and with the tile-major layout a tile read is a lane offset plus
             // an immediate.  The shapes whose registers are tighter (one state
             // tile per wave, or the checkpointing pass) keep the rolled loop:
-            // unrolled, they spill.
-            if constexpr (CT >= 2 && !CK) {
+            // unrolled, they spill; so does the wide-decay variant, which
+            // measured slower unrolled over chunk lists (0.597 against 0.559
+            // ms on the any-decay batch).
+            if constexpr (CT >= 2 && !CK && !WIDE) {
                 for (int i = 0; i < nchunks; i += 3) {
                     chunk(ic<0>{}, i);
                     if (i + 1 >= nchunks) break;
